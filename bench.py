@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-LoRA SGMV delta hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the on-device segment build
+(counting sort of the tokens by adapter, work descriptors) followed by the fused delta
+y += scale * (x A^T) B^T, both through the libsgmv C-ABI on one HIP stream. Inputs are
+synthetic and already resident in HBM when the timed region starts.
+
+Default workload: decode, 256 tokens (one per sequence), d_in = d_out = 4096, rank 16, a pool
+of 64 adapters, bf16 with fp32 accumulation. The step cycles through several independent
+copies of every buffer (pool, x, y, ids, segment arrays) whose total size is about twice the
+256 MB last-level cache, so each step reads its operands from HBM rather than from that
+cache.
+
+Timing: W untimed warm-up steps, then K steps between two device synchronisations
+(ms_per_step, value = tokens with an adapter per second). Inside the same timed region HIP
+events on the launch stream bracket every launch of the segment builder and of the delta
+kernel; their averages give the per-launch durations used for the roofline. The roofline
+figure divides the algorithmic bytes of one delta launch (x rows and y rows read and written
+for every token with an adapter, each used adapter's true-rank A and B once, 12 bytes of
+index per token) by that duration, against the 8 TB/s HBM peak.
+
+The CPU baseline is the fp64 oracle (plain per-token NumPy loop) on the same batch, repeated
+for about 10 s on this host.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LoRA-delta tokens/s + achieved HBM GB/s (% of peak), decode bs=256 d=4096 r=16"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCE = os.path.join(ROOT, "segmented_gather_gemv_amd", "csrc", "delta_bf16.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw HIP events through the runtime torch has loaded (same SONAME)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+def kernel_source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, launches_units: int):
+    """HBM bytes per delta launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(PROFILES, f"sgmv_lora_delta_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle as it stands, on the same batch, repeated for about `seconds`."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    x = w.x.float().numpy()
+    y0 = w.y0.float().numpy()
+    a = w.a.float().numpy()
+    b = w.b.float().numpy()
+    ids = w.ids.numpy()
+    rank = w.rank.numpy()
+    alpha = w.alpha.numpy()
+    n_tok = int((ids >= 0).sum())
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.lora_delta(x, y0, ids, a, b, rank, alpha)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": n_tok * reps / el, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{w.note}: the full batch ({n_tok} tokens with an adapter) through the "
+                      f"fp64 per-token oracle, {reps} times in {el:.1f} s on "
+                      f"{os.cpu_count()} visible host cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "mixed", "qkv", "tiny"])
+    ap.add_argument("--sets", type=int, default=0,
+                    help="independent buffer copies cycled by the steps (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import segmented_gather_gemv_amd as sg
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)  # default priority
+    lib = sg.library()
+    ev = HipEvents()
+
+    w = workloads.get(args.workload)
+    log(f"workload: {w.note}")
+    elem = 2 if w.dtype == torch.bfloat16 else 4
+    per_set = (w.a.numel() + w.b.numel() + w.x.numel() + w.y0.numel()) * elem
+    n_sets = args.sets or max(2, min(64, -(-2 * MALL_BYTES // per_set)))
+    log(f"buffer sets: {n_sets} x {per_set / 2**20:.1f} MiB")
+
+    sets = []
+    with torch.cuda.stream(stream):
+        a_dev, b_dev = w.a.to(dev), w.b.to(dev)
+        for i in range(n_sets):
+            pool = sg.sgmv_pool_pack(a_dev, b_dev, w.rank.tolist(), w.alpha.tolist())
+            x = w.x.to(dev)
+            y = w.y0.to(dev)
+            ids = w.ids.to(dev)
+            seg = sg.sgmv_segments_alloc(w.M, w.L, w.chunk_size, dev)
+            outs = [(y[:, n0:n0 + n], n0) for n0, n in w.slices] if len(w.slices) > 1 else [(y, 0)]
+            sl, n_sl = sg._slices(outs, pool, w.M)
+            sets.append(dict(pool=pool, x=x, y=y, ids=ids, seg=seg, sl=sl, n_sl=n_sl,
+                             outs=outs))
+        del a_dev, b_dev
+    torch.cuda.synchronize()
+
+    s_handle = ctypes.c_void_p(stream.cuda_stream)
+    build_fn, delta_fn = lib.sgmv_build_segments, lib.sgmv_lora_delta
+    calls = []
+    for st in sets:
+        bargs = (ctypes.c_void_p(st["ids"].data_ptr()), w.M, w.L, w.chunk_size, 1,
+                 ctypes.byref(st["seg"].desc), s_handle)
+        dargs = (ctypes.c_void_p(st["x"].data_ptr()), st["x"].stride(0), w.M,
+                 ctypes.byref(st["pool"].desc), ctypes.byref(st["seg"].desc), st["sl"],
+                 st["n_sl"], s_handle)
+        calls.append((bargs, dargs))
+
+    def step(i, e=None):
+        bargs, dargs = calls[i % n_sets]
+        if e is not None:
+            ev.lib.hipEventRecord(e[0], s_handle)
+        rc = build_fn(*bargs)
+        if e is not None:
+            ev.lib.hipEventRecord(e[1], s_handle)
+        rc |= delta_fn(*dargs)
+        if e is not None:
+            ev.lib.hipEventRecord(e[2], s_handle)
+        return rc
+
+    rc = 0
+    for i in range(args.warmup):
+        rc |= step(i)
+    torch.cuda.synchronize()
+    assert rc == 0, f"library call failed with status {rc}"
+    for st in sets:
+        assert int(st["seg"].info[3].item()) == sg.SGMV_OK
+
+    K = args.steps
+    evs = [ev.create(3) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        rc |= step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert rc == 0, f"library call failed with status {rc}"
+    build_ms = [ev.elapsed_ms(e[0], e[1]) for e in evs]
+    delta_ms = [ev.elapsed_ms(e[1], e[2]) for e in evs]
+    for e in evs:
+        ev.destroy(e)
+
+    wall = t1 - t0
+    ids_np = w.ids.numpy()
+    n_lora = int((ids_np >= 0).sum())
+    alg_bytes = workloads.algorithmic_bytes(ids_np, w.rank.numpy(), w.K, w.N, elem)
+    alg_flops = workloads.algorithmic_flops(ids_np, w.rank.numpy(), w.K, w.N)
+    d_avg = sum(delta_ms) / K / 1e3  # seconds
+    b_avg = sum(build_ms) / K / 1e3
+    srt = sorted(delta_ms)
+    achieved = alg_bytes / d_avg / 1e9
+    traffic = load_traffic(args.workload, 1)
+    log(f"step {wall / K * 1e6:.2f} us | delta kernel avg {d_avg * 1e6:.2f} us "
+        f"(p10 {srt[K // 10] * 1e3:.2f}, p50 {srt[K // 2] * 1e3:.2f}, p90 {srt[9 * K // 10] * 1e3:.2f}) "
+        f"| builder avg {b_avg * 1e6:.2f} us | {achieved:.0f} GB/s algorithmic "
+        f"({achieved / HBM_PEAK_GBPS * 100:.1f}% of peak) | {alg_flops / d_avg / 1e12:.2f} TFLOP/s")
+
+    result = {
+        "metric": METRIC,
+        "value": n_lora * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.note,
+            "tokens_per_step": w.M,
+            "lora_tokens_per_step": n_lora,
+            "buffer_sets": n_sets,
+            "step": "device segment build + fused delta",
+            "delta_kernel_us": d_avg * 1e6,
+            "builder_kernel_us": b_avg * 1e6,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "algorithmic_flops_per_launch": alg_flops,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    del sets
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * libsgmv — multi-LoRA segmented gather GEMV (SGMV) delta on AMD Instinct MI355X (gfx950).
+ *
+ * The library adds, for every token t that carries an adapter id l = ids[t] >= 0,
+ *
+ *     y[t, :] += (alpha_l / r_l) * B[l, :, :r_l] @ (A[l, :r_l, :] @ x[t, :])
+ *
+ * to a base output y, for a whole batch in which tokens use different adapters stored in
+ * one contiguous pool. Sources (page title and section):
+ *   - Fused-LoRA page "09. Triton Fused LoRA" (llm-algo-leetcode), Steps 1-3: pool of all
+ *     adapters as A (L, r, in) and B (L, out, r); each token routed by its own index.
+ *   - Punica page "III. Punica: Multi-Tenant LoRA Serving", SGMV section (the batched delta
+ *     next to the base product), batching-effect section (segment boundary array s), code
+ *     section (tokens reordered by adapter, optional fixed-size chunks, weight index per
+ *     segment, rows resolved through sorted token ids).
+ *   - vLLM-Ascend LoRA operator article, sections 1.1 (delta (alpha/r)(x A^T) B^T), 2.1
+ *     (per-adapter rank and alpha), 3.2 (two-stage projection: shrink then expand), 3.3
+ *     (decode SGMV with compact per-segment descriptors), 3.4 (prefill grouped GEMM),
+ *     4.1 (row-count threshold between vector and matrix units), 4.2 (adapter-major,
+ *     rank-second pool with K/N aligned to 16 or 32), 4.3 (keep the M x r intermediate on
+ *     chip), 5.3 (skip rows without adapter).
+ *
+ * Conventions for every call:
+ *   - Pointers are device memory owned by the caller unless a parameter says "host".
+ *   - Calls that take a stream are asynchronous and ordered on that stream (a hipStream_t
+ *     passed as void*; NULL is the default stream). The library allocates nothing on these
+ *     paths and keeps no mutable global state; calls on different streams that write
+ *     different outputs may run concurrently.
+ *   - Argument errors are reported synchronously by the return value before anything is
+ *     launched; SGMV_EHIP reports a failed HIP launch or copy.
+ *   - dtype: x, y, A and B share one element type (fp32 or bf16). Accumulation is fp32.
+ *     bf16 results are rounded once, to nearest even, when y is stored.
+ */
+#ifndef SGMV_H
+#define SGMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SGMV_OK = 0,
+  SGMV_EINVAL = 1,        /* null pointer, negative size, inconsistent descriptor        */
+  SGMV_EBADID = 2,        /* an adapter id outside {-1} U [0, L)                          */
+  SGMV_EUNSUPPORTED = 3,  /* valid request outside the kernels' limits (see each call)    */
+  SGMV_ECAPACITY = 4,     /* a caller-provided array is smaller than the stated bound     */
+  SGMV_EHIP = 5           /* a HIP runtime call failed                                    */
+} sgmv_status;
+
+typedef enum { SGMV_F32 = 0, SGMV_BF16 = 1 } sgmv_dtype;
+
+/* Rows per work descriptor, and the row count at or below which a descriptor is "small"
+ * (decode-like) rather than "large" (prefill-like); Ascend article 3.3 and 4.1. */
+#define SGMV_TILE_ROWS 64
+#define SGMV_SMALL_ROWS 16
+/* Largest adapter rank the kernels take (Ascend article 2.1: a maximum LoRA rank). */
+#define SGMV_MAX_RANK 64
+/* Largest pool the on-device segment builder takes (its tables live in LDS). */
+#define SGMV_DEVICE_BUILDER_MAX_L 1024
+/* Most output slices one call writes (e.g. 3 for a fused q/k/v projection). */
+#define SGMV_MAX_SLICES 4
+
+/* ------------------------------------------------------------------------------------ *
+ * Adapter pool (Fused-LoRA page Step 1; Ascend article 2.1 and 4.2).
+ *
+ * Library layout, all device memory, elements of `dtype`:
+ *   a     [L][R_pad][K_pad]        A[l][j][k]
+ *   b     [L][R_pad/8][N_pad][8]   B[l][n][j] at ((l*(R_pad/8) + j/8)*N_pad + n)*8 + j%8
+ *   rank  [L] int32                r_l in [1, R_max]
+ *   scale [L] fp32                 alpha_l / r_l
+ * Adapter-major, rank second; K and N innermost and padded to multiples of 32; R_pad is R_max
+ * rounded up to 16. B is stored in rank octets so that one 16-byte load holds 8 ranks of one
+ * output column. The first r_l ranks of an adapter are a contiguous prefix of both blocks.
+ * Padding is zero-filled by sgmv_pool_pack; kernels never read ranks at or past r_l.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  void* a;
+  void* b;
+  int32_t* rank;
+  float* scale;
+  int32_t L, R_max, R_pad, K, N, K_pad, N_pad;
+  int32_t dtype; /* sgmv_dtype */
+} sgmv_pool;
+
+/* Fill the dimensions of `pool` for L adapters of rank at most R_max, K inputs and N
+ * outputs, and report the byte sizes the caller must allocate for pool->a and pool->b
+ * (pool->rank and pool->scale take 4*L bytes each). Pointers in `pool` are cleared.
+ * Errors: EINVAL (null pool/outputs, L < 1, R_max < 1, K < 1, N < 1, bad dtype);
+ * EUNSUPPORTED (R_max > SGMV_MAX_RANK). */
+sgmv_status sgmv_pool_init(int32_t L, int32_t R_max, int32_t K, int32_t N, int32_t dtype,
+                           sgmv_pool* pool, size_t* a_bytes, size_t* b_bytes);
+
+/* Pack user-layout adapters into the pool (load time, not on the hot path).
+ *   a_user   device, [L][R_max][K] contiguous, pool dtype   (Fused-LoRA page: A (L, r, in))
+ *   b_user   device, [L][N][R_max] contiguous, pool dtype   (Fused-LoRA page: B (L, out, r))
+ *   rank     host, [L] int32, each in [1, R_max]
+ *   alpha    host, [L] fp32; scale_l = alpha_l / rank_l     (Ascend article 2.1, 3.2)
+ * Entries of a_user/b_user at ranks >= rank[l] are ignored. pool->a, b, rank, scale must
+ * point to allocations of the sizes sgmv_pool_init reported.
+ * Errors: EINVAL (null pointers, rank out of range, non-finite alpha); EHIP. */
+sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t* rank,
+                           const float* alpha, const sgmv_pool* pool, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * Segments (Punica page, batching-effect and code sections; Ascend article 3.3, 4.2).
+ *
+ * Tokens are grouped by adapter: buckets in the order in which adapters first appear among
+ * the tokens, tokens ascending inside a bucket; tokens with id -1 carry no adapter, belong
+ * to no segment and are placed last in sorted_token_ids (ascending). With chunk_size C > 0
+ * every bucket is cut into ceil(c/C) segments of C rows (the last one shorter); chunks never
+ * cross buckets. For the worked example of the Punica page, ids 2,2,2,5,5,1,1 give
+ * sorted_token_ids 0..6, seg_indptr [0,3,5,7], seg_lora_ids [2,5,1].
+ *
+ * Work descriptors ("tiles"): every segment is cut into pieces of at most SGMV_TILE_ROWS
+ * rows, in segment order. A piece of at most SGMV_SMALL_ROWS rows is small, otherwise large.
+ * tiles[i*4 .. i*4+3] = {adapter, first row in sorted order, rows, segment}; large pieces
+ * occupy slots [0, large_cap), small ones [large_cap, large_cap + small_cap).
+ * info[4] = {num_segments, num_large_tiles, num_small_tiles, status}.
+ *
+ * Capacities: seg_cap = min(M, L) without chunking, min(M, min(M, L) + M / C) with;
+ * large_cap = M / (SGMV_SMALL_ROWS + 1); small_cap = seg_cap.
+ * Array sizes: sorted_token_ids [M], seg_indptr [seg_cap + 1], seg_lora_ids [seg_cap],
+ * tiles [(large_cap + small_cap) * 4], info [4].
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t* sorted_token_ids;
+  int32_t* seg_indptr;
+  int32_t* seg_lora_ids;
+  int32_t* tiles;
+  int32_t* info;
+  int32_t M, L, chunk_size;
+  int32_t seg_cap, large_cap, small_cap;
+} sgmv_segments;
+
+/* Fill seg->M, L, chunk_size and the three capacities; pointers are left untouched.
+ * Errors: EINVAL (null seg, M < 0, L < 1, chunk_size < 0). */
+sgmv_status sgmv_segments_init(int32_t M, int32_t L, int32_t chunk_size, sgmv_segments* seg);
+
+/* Build the segment arrays and work descriptors from per-token adapter ids.
+ *   lora_indices  [M] int32 (Fused-LoRA page Step 1; -1 = no adapter, Ascend article 5.3)
+ *   on_device = 0: lora_indices and every array of `seg` are HOST memory; runs on the
+ *                  calling thread and returns SGMV_EBADID (outputs unspecified) if any id
+ *                  is outside {-1} U [0, L). `stream` is ignored.
+ *   on_device = 1: DEVICE memory; one launch on `stream`, never synchronises with the host
+ *                  (Ascend article 4.2). A bad id is treated as -1 and info[3] is set to
+ *                  SGMV_EBADID; otherwise info[3] = SGMV_OK. Requires L <=
+ *                  SGMV_DEVICE_BUILDER_MAX_L (else EUNSUPPORTED).
+ * Both paths produce identical arrays. M = 0 gives zero segments and zero tiles.
+ * Errors: EINVAL (null pointers, seg not initialised for this M/L/chunk_size); EBADID (host);
+ * EUNSUPPORTED; EHIP. */
+sgmv_status sgmv_build_segments(const int32_t* lora_indices, int32_t M, int32_t L,
+                                int32_t chunk_size, int32_t on_device, const sgmv_segments* seg,
+                                void* stream);
+
+/* One output slice: pool columns [n_begin, n_begin + n_len) land in columns [0, n_len) of
+ * y, a device array [M][ldy] of the pool dtype (e.g. q, k and v of a fused projection). */
+typedef struct {
+  void* y;
+  int64_t ldy;
+  int32_t n_begin, n_len;
+} sgmv_slice;
+
+/* Shrink (Ascend article 3.2, first stage): for every token t with an adapter l of rank r,
+ *   h[t, j] = sum_k x[t, k] * A[l, j, k]   for j < r,    h[t, j] = 0 for r <= j < R_max.
+ * Unscaled, fp32. Rows of tokens without adapter are not written.
+ *   x  [M][ldx] pool dtype, ldx >= K;   h [M][ldh] fp32, ldh >= R_max.
+ * `seg` must hold device arrays built for (M, pool->L). Rows of x are gathered through
+ * sorted_token_ids (Punica page, code section).
+ * Errors: EINVAL; EUNSUPPORTED; EHIP. */
+sgmv_status sgmv_shrink(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
+                        const sgmv_segments* seg, float* h, int64_t ldh, void* stream);
+
+/* Expand (Ascend article 3.2, second stage, and 3.3 scatter-add): for every token t with an
+ * adapter l of rank r and every output column n of every slice,
+ *   y[t, n] = round(y[t, n] + scale_l * sum_{j < r} h[t, j] * B[l, n, j]).
+ * Rows of tokens without adapter are left bit-identical. Slices must be disjoint ranges of
+ * [0, N); n_slices in [1, SGMV_MAX_SLICES]; `out` is a HOST array. y must not alias h.
+ * Errors: EINVAL; EUNSUPPORTED; EHIP. */
+sgmv_status sgmv_expand(const float* h, int64_t ldh, int32_t M, const sgmv_pool* pool,
+                        const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
+                        void* stream);
+
+/* Fused delta (Ascend article 4.3): shrink and expand in one launch; the M x r intermediate
+ * stays in registers and LDS and is never written to memory:
+ *   y[t, n] = round(y[t, n] + scale_l * sum_{j < r} B[l, n, j] * sum_k A[l, j, k] x[t, k]).
+ * Same arguments and rules as sgmv_shrink and sgmv_expand. y must not alias x or the pool.
+ * Errors: EINVAL; EUNSUPPORTED; EHIP. */
+sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
+                            const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
+                            void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* sgmv_status_string(sgmv_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t sgmv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGMV_H */

@@ -197,27 +197,6 @@ def lora_delta(x: np.ndarray, y0: np.ndarray, ids: np.ndarray, a: np.ndarray, b:
     return y
 
 
-def algorithmic_bytes(ids: np.ndarray, rank: np.ndarray, K: int, N: int, elem_bytes: int) -> int:
-    """Bytes the method itself must move for one delta over a batch: x rows of tokens with
-    an adapter (read once), their y rows (read and written), each used adapter's true-rank
-    A[l, :r, :] and B[l, :, :r] (read once), and the int32 index arrays (ids, sorted ids,
-    segment arrays: about 12 B per token). Padding, re-reads and the intermediate h are
-    excluded."""
-    ids = np.asarray(ids)
-    lora = ids[ids >= 0]
-    m = int(lora.shape[0])
-    used = np.unique(lora)
-    w = sum(int(rank[l]) * (K + N) for l in used)
-    return (m * K + 2 * m * N + w) * elem_bytes + 12 * int(ids.shape[0])
-
-
-def algorithmic_flops(ids: np.ndarray, rank: np.ndarray, K: int, N: int) -> int:
-    """2 * r * (K + N) per token with an adapter (Ascend article 3.2: about 2 d r M per
-    stage)."""
-    ids = np.asarray(ids)
-    return int(sum(2 * int(rank[l]) * (K + N) for l in ids[ids >= 0]))
-
-
 def max_segments(M: int, L: int, chunk_size: int) -> int:
     """Upper bound on the number of segments: at most one per distinct adapter, plus one
     per extra chunk when chunking."""
@@ -229,5 +208,5 @@ def max_segments(M: int, L: int, chunk_size: int) -> int:
 
 __all__ = [
     "BadAdapterId", "validate_ids", "segments", "tiles", "shrink", "expand", "lora_delta",
-    "algorithmic_bytes", "algorithmic_flops", "max_segments",
+    "max_segments",
 ]

@@ -1,0 +1,348 @@
+"""Python binding of libsgmv, the multi-LoRA SGMV delta for MI355X (gfx950).
+
+Argument marshalling only: torch tensors provide device memory and the current HIP stream,
+every step of the computation runs in the library's HIP kernels. The function names are
+those of the C-ABI in ``include/sgmv.h``:
+
+    sgmv_pool_pack(a, b, rank, alpha)                 -> Pool
+    sgmv_build_segments(ids, L, chunk_size, on_device) -> Segments
+    sgmv_shrink(x, pool, seg, h=None)                 -> h   (fp32 [M, R_max])
+    sgmv_expand(h, pool, seg, y | [slices])           -> None (y updated in place)
+    sgmv_lora_delta(x, pool, seg, y | [slices])       -> None (y updated in place)
+
+The shared library is loaded from this package directory; importing raises if it is
+missing (build it with ``python -m segmented_gather_gemv_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple, Union
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsgmv.so")
+
+SGMV_OK, SGMV_EINVAL, SGMV_EBADID, SGMV_EUNSUPPORTED, SGMV_ECAPACITY, SGMV_EHIP = range(6)
+SGMV_F32, SGMV_BF16 = 0, 1
+TILE_ROWS = 64
+SMALL_ROWS = 16
+MAX_RANK = 64
+MAX_SLICES = 4
+DEVICE_BUILDER_MAX_L = 1024
+
+EXPORTED = [
+    "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
+    "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_status_string", "sgmv_version",
+]
+
+
+class SgmvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_status_string(status)} (status {status})")
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("rank", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("L", ctypes.c_int32), ("R_max", ctypes.c_int32),
+                ("R_pad", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("K_pad", ctypes.c_int32), ("N_pad", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class _Segments(ctypes.Structure):
+    _fields_ = [("sorted_token_ids", ctypes.c_void_p), ("seg_indptr", ctypes.c_void_p),
+                ("seg_lora_ids", ctypes.c_void_p), ("tiles", ctypes.c_void_p),
+                ("info", ctypes.c_void_p), ("M", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("seg_cap", ctypes.c_int32),
+                ("large_cap", ctypes.c_int32), ("small_cap", ctypes.c_int32)]
+
+
+class _Slice(ctypes.Structure):
+    _fields_ = [("y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("n_begin", ctypes.c_int32),
+                ("n_len", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          f"'python -m segmented_gather_gemv_amd.build'")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER
+    lib.sgmv_pool_init.argtypes = [i32, i32, i32, i32, i32, P(_Pool), P(sz), P(sz)]
+    lib.sgmv_pool_pack.argtypes = [vp, vp, vp, vp, P(_Pool), vp]
+    lib.sgmv_segments_init.argtypes = [i32, i32, i32, P(_Segments)]
+    lib.sgmv_build_segments.argtypes = [vp, i32, i32, i32, i32, P(_Segments), vp]
+    lib.sgmv_shrink.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), vp, i64, vp]
+    lib.sgmv_expand.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, vp]
+    lib.sgmv_lora_delta.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, vp]
+    for f in ["sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
+              "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta"]:
+        getattr(lib, f).restype = ctypes.c_int
+    lib.sgmv_status_string.argtypes = [ctypes.c_int]
+    lib.sgmv_status_string.restype = ctypes.c_char_p
+    lib.sgmv_version.restype = ctypes.c_int32
+    return lib
+
+
+_lib = _load()
+
+
+def _status_string(s: int) -> str:
+    return _lib.sgmv_status_string(int(s)).decode()
+
+
+def _check(status: int, where: str):
+    if status != SGMV_OK:
+        raise SgmvError(status, where)
+
+
+def library():
+    """The loaded ctypes library (for tests of the raw C-ABI)."""
+    return _lib
+
+
+def _stream(device: torch.device):
+    if device.type != "cuda":
+        return None
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return SGMV_BF16
+    if dt == torch.float32:
+        return SGMV_F32
+    raise TypeError(f"libsgmv takes bfloat16 or float32, got {dt}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------------------
+# pool
+# ---------------------------------------------------------------------------------------
+@dataclass
+class Pool:
+    a: torch.Tensor        # [L, R_pad, K_pad]
+    b: torch.Tensor        # [L, R_pad/8, N_pad, 8]
+    rank: torch.Tensor     # int32 [L]
+    scale: torch.Tensor    # fp32 [L]
+    desc: _Pool
+
+    @property
+    def L(self): return self.desc.L
+
+    @property
+    def R_max(self): return self.desc.R_max
+
+    @property
+    def K(self): return self.desc.K
+
+    @property
+    def N(self): return self.desc.N
+
+    @property
+    def dtype(self): return self.a.dtype
+
+
+def sgmv_pool_init(L: int, R_max: int, K: int, N: int, dtype: torch.dtype,
+                   device: Union[str, torch.device] = "cuda") -> Pool:
+    """Allocate an empty pool (zero-filled) in the library layout."""
+    desc = _Pool()
+    ab, bb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.sgmv_pool_init(L, R_max, K, N, _dtype_code(dtype), ctypes.byref(desc),
+                               ctypes.byref(ab), ctypes.byref(bb)), "sgmv_pool_init")
+    dev = torch.device(device)
+    a = torch.zeros(L, desc.R_pad, desc.K_pad, dtype=dtype, device=dev)
+    b = torch.zeros(L, desc.R_pad // 8, desc.N_pad, 8, dtype=dtype, device=dev)
+    assert a.numel() * a.element_size() == ab.value and b.numel() * b.element_size() == bb.value
+    rank = torch.zeros(L, dtype=torch.int32, device=dev)
+    scale = torch.zeros(L, dtype=torch.float32, device=dev)
+    desc.a, desc.b = a.data_ptr(), b.data_ptr()
+    desc.rank, desc.scale = rank.data_ptr(), scale.data_ptr()
+    return Pool(a, b, rank, scale, desc)
+
+
+def sgmv_pool_pack(a: torch.Tensor, b: torch.Tensor, rank: Sequence[int],
+                   alpha: Sequence[float]) -> Pool:
+    """Pack user-layout adapters A (L, R, K) and B (L, N, R) (device tensors of the pool
+    dtype) with per-adapter rank and alpha into a new pool."""
+    if a.dim() != 3 or b.dim() != 3:
+        raise ValueError("a must be (L, R, K) and b (L, N, R)")
+    L, R, K = a.shape
+    if b.shape[0] != L or b.shape[2] != R:
+        raise ValueError(f"b shape {tuple(b.shape)} does not match a shape {tuple(a.shape)}")
+    if a.dtype != b.dtype:
+        raise TypeError("a and b must share a dtype")
+    N = b.shape[1]
+    pool = sgmv_pool_init(L, R, K, N, a.dtype, a.device)
+    a = a.contiguous()
+    b = b.contiguous()
+    rank_h = torch.as_tensor(rank, dtype=torch.int32).cpu().contiguous()
+    alpha_h = torch.as_tensor(alpha, dtype=torch.float32).cpu().contiguous()
+    if rank_h.numel() != L or alpha_h.numel() != L:
+        raise ValueError("rank and alpha need one entry per adapter")
+    _check(_lib.sgmv_pool_pack(_ptr(a), _ptr(b), _ptr(rank_h), _ptr(alpha_h),
+                               ctypes.byref(pool.desc), _stream(a.device)), "sgmv_pool_pack")
+    return pool
+
+
+# ---------------------------------------------------------------------------------------
+# segments
+# ---------------------------------------------------------------------------------------
+@dataclass
+class Segments:
+    sorted_token_ids: torch.Tensor
+    seg_indptr: torch.Tensor
+    seg_lora_ids: torch.Tensor
+    tiles: torch.Tensor          # [(large_cap + small_cap), 4]
+    info: torch.Tensor           # [4]: num_segments, n_large, n_small, status
+    desc: _Segments
+
+    @property
+    def M(self): return self.desc.M
+
+    def to(self, device) -> "Segments":
+        """Copy (e.g. host-built) segments to another device."""
+        d = _Segments()
+        ctypes.memmove(ctypes.byref(d), ctypes.byref(self.desc), ctypes.sizeof(_Segments))
+        out = Segments(*(t.to(device) for t in (self.sorted_token_ids, self.seg_indptr,
+                                                self.seg_lora_ids, self.tiles, self.info)), d)
+        out._bind()
+        return out
+
+    def _bind(self):
+        self.desc.sorted_token_ids = self.sorted_token_ids.data_ptr()
+        self.desc.seg_indptr = self.seg_indptr.data_ptr()
+        self.desc.seg_lora_ids = self.seg_lora_ids.data_ptr()
+        self.desc.tiles = self.tiles.data_ptr()
+        self.desc.info = self.info.data_ptr()
+
+    def host(self) -> dict:
+        """Synchronous host view: the trimmed arrays and the counters."""
+        info = self.info.cpu().tolist()
+        S, nl, ns, st = info
+        tiles = self.tiles.cpu()
+        return {
+            "sorted_token_ids": self.sorted_token_ids.cpu(),
+            "seg_indptr": self.seg_indptr.cpu()[:S + 1],
+            "seg_lora_ids": self.seg_lora_ids.cpu()[:S],
+            "num_segments": S,
+            "large_tiles": tiles[:nl],
+            "small_tiles": tiles[self.desc.large_cap:self.desc.large_cap + ns],
+            "status": st,
+        }
+
+
+def sgmv_segments_alloc(M: int, L: int, chunk_size: int = 0,
+                        device: Union[str, torch.device] = "cuda") -> Segments:
+    desc = _Segments()
+    _check(_lib.sgmv_segments_init(M, L, chunk_size, ctypes.byref(desc)), "sgmv_segments_init")
+    dev = torch.device(device)
+    z = lambda n: torch.zeros(max(int(n), 1), dtype=torch.int32, device=dev)
+    seg = Segments(z(M), z(desc.seg_cap + 1), z(desc.seg_cap),
+                   torch.zeros(max(desc.large_cap + desc.small_cap, 1), 4, dtype=torch.int32,
+                               device=dev), z(4), desc)
+    seg._bind()
+    return seg
+
+
+def sgmv_build_segments(ids: torch.Tensor, L: int, chunk_size: int = 0, on_device: bool = True,
+                        out: Optional[Segments] = None) -> Segments:
+    """Group tokens by adapter (id -1: no adapter). ``on_device`` runs the GPU builder on the
+    current stream without a host sync (ids must be a device tensor); otherwise the host
+    builder runs on CPU tensors and raises on a bad id."""
+    ids = ids.to(torch.int32).contiguous()
+    M = int(ids.numel())
+    dev = ids.device
+    if on_device and dev.type != "cuda":
+        raise ValueError("on_device=True needs ids on the GPU")
+    if not on_device and dev.type != "cpu":
+        raise ValueError("on_device=False needs ids on the CPU")
+    seg = out if out is not None else sgmv_segments_alloc(M, L, chunk_size, dev)
+    _check(_lib.sgmv_build_segments(_ptr(ids), M, L, chunk_size, 1 if on_device else 0,
+                                    ctypes.byref(seg.desc), _stream(dev)), "sgmv_build_segments")
+    return seg
+
+
+# ---------------------------------------------------------------------------------------
+# shrink / expand / fused delta
+# ---------------------------------------------------------------------------------------
+SliceSpec = Tuple[torch.Tensor, int]   # (y tensor [M, n_len], first pool column)
+
+
+def _slices(y_or_slices, pool: Pool, M: int):
+    if isinstance(y_or_slices, torch.Tensor):
+        specs = [(y_or_slices, 0)]
+    else:
+        specs = list(y_or_slices)
+    arr = (_Slice * len(specs))()
+    for i, (y, n0) in enumerate(specs):
+        if y.dim() != 2 or y.shape[0] != M or y.stride(1) != 1:
+            raise ValueError("each output slice must be a row-major [M, n] tensor")
+        if y.dtype != pool.dtype or y.device != pool.a.device:
+            raise TypeError("output slice dtype/device must match the pool")
+        arr[i].y = y.data_ptr()
+        arr[i].ldy = y.stride(0)
+        arr[i].n_begin = int(n0)
+        arr[i].n_len = int(y.shape[1])
+    return arr, len(specs)
+
+
+def _check_x(x: torch.Tensor, pool: Pool):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a row-major [M, K] tensor")
+    if x.dtype != pool.dtype or x.device != pool.a.device:
+        raise TypeError("x dtype/device must match the pool")
+    if x.shape[1] != pool.K:
+        raise ValueError(f"x has {x.shape[1]} columns, pool K is {pool.K}")
+
+
+def sgmv_shrink(x: torch.Tensor, pool: Pool, seg: Segments,
+                h: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """h[t, :r] = A[l, :r, :] @ x[t] for tokens with an adapter (fp32, unscaled)."""
+    _check_x(x, pool)
+    M = x.shape[0]
+    if h is None:
+        h = torch.zeros(M, pool.R_max, dtype=torch.float32, device=x.device)
+    if h.dtype != torch.float32 or h.stride(1) != 1:
+        raise TypeError("h must be a row-major fp32 tensor")
+    _check(_lib.sgmv_shrink(_ptr(x), x.stride(0), M, ctypes.byref(pool.desc),
+                            ctypes.byref(seg.desc), _ptr(h), h.stride(0), _stream(x.device)),
+           "sgmv_shrink")
+    return h
+
+
+def sgmv_expand(h: torch.Tensor, pool: Pool, seg: Segments,
+                y: Union[torch.Tensor, Sequence[SliceSpec]]) -> None:
+    """y[t] += scale_l * B[l, :, :r] @ h[t, :r] (in place; list of (y, first column) for
+    several output slices)."""
+    if h.dtype != torch.float32 or h.stride(1) != 1:
+        raise TypeError("h must be a row-major fp32 tensor")
+    M = h.shape[0]
+    arr, n = _slices(y, pool, M)
+    _check(_lib.sgmv_expand(_ptr(h), h.stride(0), M, ctypes.byref(pool.desc),
+                            ctypes.byref(seg.desc), arr, n, _stream(h.device)), "sgmv_expand")
+
+
+def sgmv_lora_delta(x: torch.Tensor, pool: Pool, seg: Segments,
+                    y: Union[torch.Tensor, Sequence[SliceSpec]]) -> None:
+    """Fused y[t] += scale_l * B[l, :, :r] @ (A[l, :r, :] @ x[t]) (in place)."""
+    _check_x(x, pool)
+    M = x.shape[0]
+    arr, n = _slices(y, pool, M)
+    _check(_lib.sgmv_lora_delta(_ptr(x), x.stride(0), M, ctypes.byref(pool.desc),
+                                ctypes.byref(seg.desc), arr, n, _stream(x.device)),
+           "sgmv_lora_delta")
+
+
+__all__ = [
+    "LIB_PATH", "EXPORTED", "SgmvError", "Pool", "Segments", "library",
+    "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_alloc", "sgmv_build_segments",
+    "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta",
+]

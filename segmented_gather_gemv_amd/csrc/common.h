@@ -1,0 +1,72 @@
+// Shared device definitions for the libsgmv HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sgmv.h"
+
+namespace sgmv {
+
+constexpr int WAVE = 64;
+
+// Eight bf16 values: one MFMA 16x16x32 operand fragment per lane.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4_t load_u32x4(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
+
+// Per-call kernel arguments shared by the delta kernels (passed by value).
+struct SliceArg {
+  void* y;
+  int64_t ldy;
+  int32_t n_begin;  // first pool column
+  int32_t v_begin;  // first column in the concatenation of all slices
+  int32_t n_len;
+};
+
+struct DeltaArgs {
+  const void* x;
+  int64_t ldx;
+  float* h;          // shrink output / expand input (unfused paths)
+  int64_t ldh;
+  const void* a;     // pool A [L][R_pad][K_pad]
+  const void* b;     // pool B [L][R_pad/8][N_pad][8]
+  const int32_t* rank;
+  const float* scale;
+  int32_t R_max, R_pad, K, K_pad, N_pad;
+  const int32_t* sorted;  // sorted_token_ids
+  const int32_t* tiles;   // work descriptors
+  const int32_t* info;    // {num_segments, n_large, n_small, status}
+  int32_t large_cap;
+  int32_t n_split_large;  // workgroups across output columns per large tile
+  int32_t n_split_small;  // ... per small tile
+  int32_t n_slices;
+  int32_t v_total;        // sum of slice widths
+  SliceArg slices[SGMV_MAX_SLICES];
+};
+
+enum Mode { MODE_FUSED = 0, MODE_SHRINK = 1, MODE_EXPAND = 2 };
+
+}  // namespace sgmv

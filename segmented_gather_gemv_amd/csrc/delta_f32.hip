@@ -1,0 +1,141 @@
+// fp32 multi-LoRA delta on the vector ALU.
+//
+// Same work descriptors, column splits and workgroup mapping as the bf16 matrix-core path,
+// with plain fp32 fused multiply-adds: the shrink gives each thread one (row, rank) pair and
+// a serial dot product over K (Ascend article 3.2, first stage); the expand gives each
+// thread one output column, streams that column's rank octets of B and updates every row of
+// the piece (second stage). Used for fp32 pools, whose products the bf16 matrix cores
+// cannot take; not tuned for speed.
+#include "common.h"
+
+namespace sgmv {
+
+constexpr int F_THREADS = 256;
+constexpr int F_HS = 65;  // LDS row stride of the h tile
+
+struct FWork {
+  int lora, start, rows, v0, v1;
+};
+
+__device__ __forceinline__ bool f32_decode_work(const DeltaArgs& A, bool split_cols, FWork& wi) {
+  const int n_large = A.info[1], n_small = A.info[2];
+  const int PL = split_cols ? A.n_split_large : 1;
+  const int PS = split_cols ? A.n_split_small : 1;
+  const int work_l = n_large * PL;
+  const int work = work_l + n_small * PS;
+  const int b = blockIdx.x;
+  const int per = (work + 7) >> 3;
+  const int slot = b >> 3;
+  if (slot >= per) return false;
+  const int u = (b & 7) * per + slot;
+  if (u >= work) return false;
+  int tile, p, P;
+  if (u < work_l) {
+    tile = u / PL;
+    p = u - tile * PL;
+    P = PL;
+  } else {
+    const int v = u - work_l;
+    tile = A.large_cap + v / PS;
+    p = v % PS;
+    P = PS;
+  }
+  const int32_t* d = A.tiles + (size_t)tile * 4;
+  wi.lora = d[0];
+  wi.start = d[1];
+  wi.rows = d[2];
+  const int width = (((A.v_total + P - 1) / P) + 63) & ~63;
+  wi.v0 = p * width;
+  wi.v1 = min(wi.v0 + width, A.v_total);
+  return !split_cols || wi.v0 < wi.v1;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
+  __shared__ int s_tok[SGMV_TILE_ROWS];
+  __shared__ float s_h[SGMV_TILE_ROWS * F_HS];
+  FWork wi;
+  if (!f32_decode_work(A, MODE != MODE_SHRINK, wi)) return;
+  const int r = A.rank[wi.lora];
+  const float scale = A.scale[wi.lora];
+  const int tid = threadIdx.x;
+  if (tid < SGMV_TILE_ROWS) s_tok[tid] = tid < wi.rows ? A.sorted[wi.start + tid] : 0;
+  __syncthreads();
+
+  if (MODE == MODE_EXPAND) {
+    for (int idx = tid; idx < SGMV_TILE_ROWS * 64; idx += F_THREADS) {
+      const int row = idx >> 6, j = idx & 63;
+      float v = 0.f;
+      if (row < wi.rows && j < r) v = A.h[(size_t)s_tok[row] * A.ldh + j] * scale;
+      s_h[row * F_HS + j] = v;
+    }
+  } else {
+    const float mult = MODE == MODE_SHRINK ? 1.f : scale;
+    const float* ab = static_cast<const float*>(A.a) + (size_t)wi.lora * A.R_pad * A.K_pad;
+    for (int idx = tid; idx < SGMV_TILE_ROWS * 64; idx += F_THREADS) {
+      const int row = idx >> 6, j = idx & 63;
+      float s = 0.f;
+      if (row < wi.rows && j < r) {
+        const float* xr = static_cast<const float*>(A.x) + (size_t)s_tok[row] * (size_t)A.ldx;
+        const float* ar = ab + (size_t)j * A.K_pad;
+        for (int k = 0; k < A.K; ++k) s = fmaf(xr[k], ar[k], s);
+      }
+      s_h[row * F_HS + j] = s * mult;
+    }
+  }
+  __syncthreads();
+
+  if (MODE == MODE_SHRINK) {
+    const int R = A.R_max;
+    for (int idx = tid; idx < wi.rows * R; idx += F_THREADS) {
+      const int row = idx / R, j = idx - row * R;
+      A.h[(size_t)s_tok[row] * A.ldh + j] = j < r ? s_h[row * F_HS + j] : 0.f;
+    }
+    return;
+  }
+
+  const float* bb = static_cast<const float*>(A.b) + (size_t)wi.lora * (A.R_pad / 8) * A.N_pad * 8;
+  for (int v = wi.v0 + tid; v < wi.v1; v += F_THREADS) {
+    float* yb = static_cast<float*>(A.slices[0].y);
+    int64_t ldy = A.slices[0].ldy;
+    int col = v, n = A.slices[0].n_begin + v;
+#pragma unroll
+    for (int i = 1; i < SGMV_MAX_SLICES; ++i) {
+      if (i < A.n_slices && v >= A.slices[i].v_begin) {
+        yb = static_cast<float*>(A.slices[i].y);
+        ldy = A.slices[i].ldy;
+        col = v - A.slices[i].v_begin;
+        n = A.slices[i].n_begin + col;
+      }
+    }
+    float acc[SGMV_TILE_ROWS];
+#pragma unroll
+    for (int row = 0; row < SGMV_TILE_ROWS; ++row) acc[row] = 0.f;
+    for (int j = 0; j < r; ++j) {
+      const float bj = bb[((size_t)(j >> 3) * A.N_pad + n) * 8 + (j & 7)];
+#pragma unroll
+      for (int row = 0; row < SGMV_TILE_ROWS; ++row) acc[row] = fmaf(s_h[row * F_HS + j], bj, acc[row]);
+    }
+#pragma unroll
+    for (int row = 0; row < SGMV_TILE_ROWS; ++row) {
+      if (row < wi.rows) {
+        float* yp = yb + (size_t)s_tok[row] * (size_t)ldy + col;
+        *yp = *yp + acc[row];
+      }
+    }
+  }
+}
+
+hipError_t launch_delta_f32(int mode, const DeltaArgs& A, int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  const dim3 g(grid), b(F_THREADS);
+  if (mode == MODE_FUSED)
+    hipLaunchKernelGGL(delta_f32_kernel<MODE_FUSED>, g, b, 0, stream, A);
+  else if (mode == MODE_SHRINK)
+    hipLaunchKernelGGL(delta_f32_kernel<MODE_SHRINK>, g, b, 0, stream, A);
+  else
+    hipLaunchKernelGGL(delta_f32_kernel<MODE_EXPAND>, g, b, 0, stream, A);
+  return hipGetLastError();
+}
+
+}  // namespace sgmv

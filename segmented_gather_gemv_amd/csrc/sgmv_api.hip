@@ -1,0 +1,274 @@
+// libsgmv C-ABI: argument validation, launch geometry and dispatch. Stateless; every call
+// runs on the caller's stream. Declarations and contracts are in include/sgmv.h.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "common.h"
+#include "segments_host.h"
+
+namespace sgmv {
+size_t build_lds_bytes(int L);
+hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_t* sorted,
+                                 int32_t* indptr, int32_t* seg_lora, int32_t* tiles,
+                                 int32_t* info, int seg_cap, int large_cap, int small_cap,
+                                 hipStream_t stream);
+hipError_t launch_pool_pack(const void* a_user, const void* b_user, const sgmv_pool& p,
+                            hipStream_t stream);
+hipError_t launch_delta_bf16(int mode, bool aligned, const DeltaArgs& A, int grid,
+                             hipStream_t stream);
+hipError_t launch_delta_f32(int mode, const DeltaArgs& A, int grid, hipStream_t stream);
+
+namespace {
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+int env_int(const char* name, int fallback) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return fallback;
+  const int v = std::atoi(s);
+  return v > 0 ? v : fallback;
+}
+
+bool pool_ok(const sgmv_pool* p) {
+  if (!p || !p->a || !p->b || !p->rank || !p->scale) return false;
+  if (p->L < 1 || p->R_max < 1 || p->K < 1 || p->N < 1) return false;
+  if (p->dtype != SGMV_F32 && p->dtype != SGMV_BF16) return false;
+  if (p->R_pad != round_up(p->R_max, 16) || p->K_pad != round_up(p->K, 32) ||
+      p->N_pad != round_up(p->N, 32))
+    return false;
+  return true;
+}
+
+bool seg_ok(const sgmv_segments* s, int32_t M, int32_t L) {
+  if (!s || !s->sorted_token_ids || !s->seg_indptr || !s->seg_lora_ids || !s->tiles || !s->info)
+    return false;
+  if (s->M != M || s->L != L || s->chunk_size < 0) return false;
+  int32_t sc, lc, smc;
+  segment_capacities(M, L, s->chunk_size, &sc, &lc, &smc);
+  return s->seg_cap == sc && s->large_cap == lc && s->small_cap == smc;
+}
+
+inline bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validates the output slices and fills the slice part of the kernel arguments.
+sgmv_status fill_slices(const sgmv_pool* p, int32_t M, const sgmv_slice* out, int32_t n_slices,
+                        DeltaArgs& A, bool& aligned) {
+  if (!out || n_slices < 1 || n_slices > SGMV_MAX_SLICES) return SGMV_EINVAL;
+  int v = 0;
+  for (int i = 0; i < n_slices; ++i) {
+    const sgmv_slice& s = out[i];
+    if (!s.y || s.n_len < 1 || s.n_begin < 0 || (int64_t)s.n_begin + s.n_len > p->N ||
+        s.ldy < s.n_len)
+      return SGMV_EINVAL;
+    for (int j = 0; j < i; ++j) {  // pool column ranges must be disjoint
+      const sgmv_slice& t = out[j];
+      if (s.n_begin < t.n_begin + t.n_len && t.n_begin < s.n_begin + s.n_len) return SGMV_EINVAL;
+    }
+    A.slices[i].y = s.y;
+    A.slices[i].ldy = s.ldy;
+    A.slices[i].n_begin = s.n_begin;
+    A.slices[i].v_begin = v;
+    A.slices[i].n_len = s.n_len;
+    if (s.n_len % 4 != 0 || s.ldy % 4 != 0 || !aligned_to(s.y, 8)) aligned = false;
+    v += s.n_len;
+  }
+  for (int i = n_slices; i < SGMV_MAX_SLICES; ++i) {
+    A.slices[i] = A.slices[0];
+    A.slices[i].v_begin = 0x7fffffff;
+  }
+  A.n_slices = n_slices;
+  A.v_total = v;
+  (void)M;
+  return SGMV_OK;
+}
+
+void fill_common(const sgmv_pool* p, const sgmv_segments* seg, DeltaArgs& A) {
+  A.a = p->a;
+  A.b = p->b;
+  A.rank = p->rank;
+  A.scale = p->scale;
+  A.R_max = p->R_max;
+  A.R_pad = p->R_pad;
+  A.K = p->K;
+  A.K_pad = p->K_pad;
+  A.N_pad = p->N_pad;
+  A.sorted = seg->sorted_token_ids;
+  A.tiles = seg->tiles;
+  A.info = seg->info;
+  A.large_cap = seg->large_cap;
+}
+
+// Column splits per work descriptor: enough workgroups to cover the chip for decode-like
+// pieces, few enough that x rows and A are not re-read too often for prefill-like ones.
+void choose_splits(int v_total, DeltaArgs& A) {
+  int ps = v_total / 1024;
+  int pl = v_total / 2048;
+  ps = ps < 1 ? 1 : (ps > 16 ? 16 : ps);
+  pl = pl < 1 ? 1 : (pl > 16 ? 16 : pl);
+  A.n_split_small = env_int("SGMV_NSPLIT_SMALL", ps);
+  A.n_split_large = env_int("SGMV_NSPLIT_LARGE", pl);
+}
+
+sgmv_status hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_EHIP; }
+
+sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, float* h_out,
+                      int64_t ldh, int32_t M, const sgmv_pool* pool, const sgmv_segments* seg,
+                      const sgmv_slice* out, int32_t n_slices, void* stream) {
+  if (M < 0 || !pool_ok(pool)) return SGMV_EINVAL;
+  if (pool->R_max > SGMV_MAX_RANK) return SGMV_EUNSUPPORTED;
+  if (!seg_ok(seg, M, pool->L)) return SGMV_EINVAL;
+  DeltaArgs A;
+  std::memset(&A, 0, sizeof(A));
+  bool aligned = true;
+  if (mode != MODE_EXPAND) {
+    if (!x || ldx < pool->K) return SGMV_EINVAL;
+    A.x = x;
+    A.ldx = ldx;
+    if (pool->K % 8 != 0 || ldx % 8 != 0 || !aligned_to(x, 16)) aligned = false;
+  }
+  if (mode == MODE_SHRINK) {
+    if (!h_out || ldh < pool->R_max) return SGMV_EINVAL;
+    A.h = h_out;
+    A.ldh = ldh;
+  }
+  if (mode == MODE_EXPAND) {
+    if (!h_in || ldh < pool->R_max) return SGMV_EINVAL;
+    A.h = const_cast<float*>(h_in);
+    A.ldh = ldh;
+  }
+  if (mode != MODE_SHRINK) {
+    const sgmv_status st = fill_slices(pool, M, out, n_slices, A, aligned);
+    if (st != SGMV_OK) return st;
+  } else {
+    A.n_slices = 0;
+    A.v_total = 0;
+  }
+  if (M == 0) return SGMV_OK;
+  fill_common(pool, seg, A);
+  int grid;
+  if (mode == MODE_SHRINK) {
+    A.n_split_large = A.n_split_small = 1;
+    grid = seg->large_cap + seg->small_cap;
+  } else {
+    choose_splits(A.v_total, A);
+    grid = seg->large_cap * A.n_split_large + seg->small_cap * A.n_split_small;
+  }
+  // the kernels place work item u on workgroup 8 * (u % per) + u / per with per =
+  // ceil(work / 8), so the grid must be a multiple of 8 covering every work item
+  grid = (int)round_up(grid, 8);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, grid, s));
+  return hip_status(launch_delta_f32(mode, A, grid, s));
+}
+
+}  // namespace
+}  // namespace sgmv
+
+using namespace sgmv;
+
+extern "C" {
+
+const char* sgmv_status_string(sgmv_status s) {
+  switch (s) {
+    case SGMV_OK: return "SGMV_OK";
+    case SGMV_EINVAL: return "SGMV_EINVAL: invalid argument";
+    case SGMV_EBADID: return "SGMV_EBADID: adapter id outside {-1} U [0, L)";
+    case SGMV_EUNSUPPORTED: return "SGMV_EUNSUPPORTED: outside the kernels' limits";
+    case SGMV_ECAPACITY: return "SGMV_ECAPACITY: output array smaller than its bound";
+    case SGMV_EHIP: return "SGMV_EHIP: HIP runtime error";
+  }
+  return "unknown sgmv_status";
+}
+
+int32_t sgmv_version(void) { return 100; }
+
+sgmv_status sgmv_pool_init(int32_t L, int32_t R_max, int32_t K, int32_t N, int32_t dtype,
+                           sgmv_pool* pool, size_t* a_bytes, size_t* b_bytes) {
+  if (!pool || !a_bytes || !b_bytes) return SGMV_EINVAL;
+  if (L < 1 || R_max < 1 || K < 1 || N < 1 || L > 65535) return SGMV_EINVAL;
+  if (dtype != SGMV_F32 && dtype != SGMV_BF16) return SGMV_EINVAL;
+  if (R_max > SGMV_MAX_RANK) return SGMV_EUNSUPPORTED;
+  std::memset(pool, 0, sizeof(*pool));
+  pool->L = L;
+  pool->R_max = R_max;
+  pool->R_pad = (int32_t)round_up(R_max, 16);
+  pool->K = K;
+  pool->N = N;
+  pool->K_pad = (int32_t)round_up(K, 32);
+  pool->N_pad = (int32_t)round_up(N, 32);
+  pool->dtype = dtype;
+  const size_t e = dtype == SGMV_BF16 ? 2 : 4;
+  *a_bytes = (size_t)L * pool->R_pad * pool->K_pad * e;
+  *b_bytes = (size_t)L * pool->R_pad * pool->N_pad * e;
+  return SGMV_OK;
+}
+
+sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t* rank,
+                           const float* alpha, const sgmv_pool* pool, void* stream) {
+  if (!a_user || !b_user || !rank || !alpha || !pool_ok(pool)) return SGMV_EINVAL;
+  const int L = pool->L;
+  float* scale = static_cast<float*>(std::malloc(sizeof(float) * (size_t)L));
+  if (!scale) return SGMV_EINVAL;
+  for (int l = 0; l < L; ++l) {
+    if (rank[l] < 1 || rank[l] > pool->R_max || !std::isfinite(alpha[l])) {
+      std::free(scale);
+      return SGMV_EINVAL;
+    }
+    scale[l] = alpha[l] / (float)rank[l];
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(pool->rank, rank, sizeof(int32_t) * L, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(pool->scale, scale, sizeof(float) * L, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // host staging buffers end here
+  std::free(scale);
+  if (e != hipSuccess) return SGMV_EHIP;
+  return hip_status(launch_pool_pack(a_user, b_user, *pool, s));
+}
+
+sgmv_status sgmv_segments_init(int32_t M, int32_t L, int32_t chunk_size, sgmv_segments* seg) {
+  if (!seg || M < 0 || L < 1 || chunk_size < 0) return SGMV_EINVAL;
+  seg->M = M;
+  seg->L = L;
+  seg->chunk_size = chunk_size;
+  segment_capacities(M, L, chunk_size, &seg->seg_cap, &seg->large_cap, &seg->small_cap);
+  return SGMV_OK;
+}
+
+sgmv_status sgmv_build_segments(const int32_t* lora_indices, int32_t M, int32_t L,
+                                int32_t chunk_size, int32_t on_device, const sgmv_segments* seg,
+                                void* stream) {
+  if (M < 0 || L < 1 || chunk_size < 0 || (M > 0 && !lora_indices)) return SGMV_EINVAL;
+  if (!seg || seg->chunk_size != chunk_size || !seg_ok(seg, M, L)) return SGMV_EINVAL;
+  if (on_device == 0) {
+    return (sgmv_status)host_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
+                                            seg->seg_indptr, seg->seg_lora_ids, seg->tiles,
+                                            seg->info, seg->seg_cap, seg->large_cap,
+                                            seg->small_cap);
+  }
+  if (L > SGMV_DEVICE_BUILDER_MAX_L) return SGMV_EUNSUPPORTED;
+  return hip_status(launch_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
+                                          seg->seg_indptr, seg->seg_lora_ids, seg->tiles,
+                                          seg->info, seg->seg_cap, seg->large_cap, seg->small_cap,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+sgmv_status sgmv_shrink(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
+                        const sgmv_segments* seg, float* h, int64_t ldh, void* stream) {
+  return run_delta(MODE_SHRINK, x, ldx, nullptr, h, ldh, M, pool, seg, nullptr, 0, stream);
+}
+
+sgmv_status sgmv_expand(const float* h, int64_t ldh, int32_t M, const sgmv_pool* pool,
+                        const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
+                        void* stream) {
+  return run_delta(MODE_EXPAND, nullptr, 0, h, nullptr, ldh, M, pool, seg, out, n_slices, stream);
+}
+
+sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
+                            const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
+                            void* stream) {
+  return run_delta(MODE_FUSED, x, ldx, nullptr, nullptr, 0, M, pool, seg, out, n_slices, stream);
+}
+
+}  // extern "C"

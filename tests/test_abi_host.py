@@ -1,0 +1,260 @@
+"""CPU tests of the C-ABI: the library loads, exports every function include/sgmv.h
+declares, the host segment builder matches the oracle bit for bit, and argument errors come
+back as the documented status codes. No GPU work is launched here."""
+import ctypes
+import itertools
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import segmented_gather_gemv_amd as sg
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgmv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgmv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary_calls():
+    names = declared_functions()
+    for n in ["sgmv_build_segments", "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta",
+              "sgmv_pool_pack"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sg.library()
+    names = declared_functions()
+    assert names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", sg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    assert set(names) <= exported
+    assert set(sg.EXPORTED) <= exported
+
+
+def test_version_and_status_strings():
+    lib = sg.library()
+    assert lib.sgmv_version() >= 100
+    for s in range(6):
+        assert lib.sgmv_status_string(s).startswith(b"SGMV_")
+
+
+def host_build(ids, L, C):
+    seg = sg.sgmv_build_segments(torch.as_tensor(np.asarray(ids, dtype=np.int32)), L, C,
+                                 on_device=False)
+    return seg.host()
+
+
+def assert_same_as_oracle(ids, L, C):
+    got = host_build(ids, L, C)
+    ref = oracle.segments(ids, L, C)
+    assert np.array_equal(got["sorted_token_ids"].numpy()[:len(ids)], ref["sorted_token_ids"])
+    assert np.array_equal(got["seg_indptr"].numpy(), ref["seg_indptr"])
+    assert np.array_equal(got["seg_lora_ids"].numpy(), ref["seg_lora_ids"])
+    assert got["num_segments"] == ref["num_segments"]
+    lg, sm = oracle.tiles(ref["seg_indptr"], ref["seg_lora_ids"], sg.TILE_ROWS, sg.SMALL_ROWS)
+    assert np.array_equal(got["large_tiles"].numpy().reshape(-1, 4), lg)
+    assert np.array_equal(got["small_tiles"].numpy().reshape(-1, 4), sm)
+    assert got["status"] == sg.SGMV_OK
+
+
+def test_host_builder_worked_example():
+    got = host_build([2, 2, 2, 5, 5, 1, 1], 6, 0)
+    assert got["seg_indptr"].tolist() == [0, 3, 5, 7]
+    assert got["seg_lora_ids"].tolist() == [2, 5, 1]
+    assert got["sorted_token_ids"].tolist() == list(range(7))
+
+
+def test_host_builder_exhaustive_small():
+    for M in range(0, 6):
+        for ids in itertools.product((-1, 0, 1, 2), repeat=M):
+            for C in (0, 1, 2, 3):
+                assert_same_as_oracle(list(ids), 3, C)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed", "qkv"])
+def test_host_builder_workloads(name):
+    w = workloads.get(name)
+    assert_same_as_oracle(w.ids.numpy(), w.L, w.chunk_size)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_host_builder_random(seed):
+    rng = np.random.default_rng(seed)
+    M = int(rng.integers(1, 5000))
+    L = int(rng.integers(1, 300))
+    C = int(rng.choice([0, 1, 7, 64, 200]))
+    ids = rng.integers(-1, L, size=M)
+    # long runs to produce many large tiles
+    ids[: M // 3] = rng.integers(0, L)
+    assert_same_as_oracle(ids, L, C)
+
+
+def test_host_builder_bad_id():
+    with pytest.raises(sg.SgmvError) as e:
+        host_build([0, 3, 1], 3, 0)
+    assert e.value.status == sg.SGMV_EBADID
+    with pytest.raises(sg.SgmvError) as e:
+        host_build([0, -2], 3, 0)
+    assert e.value.status == sg.SGMV_EBADID
+
+
+def test_host_builder_empty_and_all_negative():
+    got = host_build([], 4, 0)
+    assert got["num_segments"] == 0 and got["seg_indptr"].tolist() == [0]
+    got = host_build([-1] * 9, 4, 3)
+    assert got["num_segments"] == 0
+    assert got["sorted_token_ids"].tolist() == list(range(9))
+
+
+def test_capacities_bound_the_outputs():
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        M = int(rng.integers(0, 3000))
+        L = int(rng.integers(1, 100))
+        C = int(rng.choice([0, 1, 3, 64]))
+        seg = sg.sgmv_segments_alloc(M, L, C, "cpu")
+        d = seg.desc
+        ids = rng.integers(-1, L, size=M)
+        ref = oracle.segments(ids, L, C)
+        lg, sm = oracle.tiles(ref["seg_indptr"], ref["seg_lora_ids"])
+        assert ref["num_segments"] <= d.seg_cap
+        assert len(lg) <= d.large_cap and len(sm) <= d.small_cap
+
+
+# ---------------------------------------------------------------------------------------
+# argument errors (returned before any launch)
+# ---------------------------------------------------------------------------------------
+def test_pool_init_errors():
+    lib = sg.library()
+    p = sg._Pool()
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    ok = lib.sgmv_pool_init(4, 16, 128, 256, sg.SGMV_BF16, ctypes.byref(p), ctypes.byref(a),
+                            ctypes.byref(b))
+    assert ok == sg.SGMV_OK
+    assert (p.R_pad, p.K_pad, p.N_pad) == (16, 128, 256)
+    assert a.value == 4 * 16 * 128 * 2 and b.value == 4 * 16 * 256 * 2
+    assert lib.sgmv_pool_init(4, 65, 128, 256, 1, ctypes.byref(p), ctypes.byref(a),
+                              ctypes.byref(b)) == sg.SGMV_EUNSUPPORTED
+    for args in [(0, 16, 128, 256, 1), (4, 0, 128, 256, 1), (4, 16, 0, 256, 1),
+                 (4, 16, 128, 0, 1), (4, 16, 128, 256, 7)]:
+        assert lib.sgmv_pool_init(*args, ctypes.byref(p), ctypes.byref(a),
+                                  ctypes.byref(b)) == sg.SGMV_EINVAL
+    assert lib.sgmv_pool_init(4, 3, 100, 37, 0, ctypes.byref(p), ctypes.byref(a),
+                              ctypes.byref(b)) == sg.SGMV_OK
+    assert (p.R_pad, p.K_pad, p.N_pad) == (16, 128, 64)
+
+
+def test_segments_init_errors():
+    lib = sg.library()
+    s = sg._Segments()
+    assert lib.sgmv_segments_init(-1, 4, 0, ctypes.byref(s)) == sg.SGMV_EINVAL
+    assert lib.sgmv_segments_init(4, 0, 0, ctypes.byref(s)) == sg.SGMV_EINVAL
+    assert lib.sgmv_segments_init(4, 4, -1, ctypes.byref(s)) == sg.SGMV_EINVAL
+    assert lib.sgmv_segments_init(256, 64, 0, ctypes.byref(s)) == sg.SGMV_OK
+    assert (s.seg_cap, s.large_cap, s.small_cap) == (64, 256 // 17, 64)
+    assert lib.sgmv_segments_init(2048, 128, 64, ctypes.byref(s)) == sg.SGMV_OK
+    assert s.seg_cap == min(2048, 128 + 2048 // 64)
+
+
+def test_build_segments_errors():
+    lib = sg.library()
+    seg = sg.sgmv_segments_alloc(8, 4, 0, "cpu")
+    ids = torch.zeros(8, dtype=torch.int32)
+    # descriptor initialised for another M / chunk size
+    assert lib.sgmv_build_segments(ctypes.c_void_p(ids.data_ptr()), 7, 4, 0, 0,
+                                   ctypes.byref(seg.desc), None) == sg.SGMV_EINVAL
+    assert lib.sgmv_build_segments(ctypes.c_void_p(ids.data_ptr()), 8, 4, 2, 0,
+                                   ctypes.byref(seg.desc), None) == sg.SGMV_EINVAL
+    assert lib.sgmv_build_segments(None, 8, 4, 0, 0, ctypes.byref(seg.desc),
+                                   None) == sg.SGMV_EINVAL
+    # device builder limit on the pool size is checked before any launch
+    big = sg.sgmv_segments_alloc(8, 5000, 0, "cpu")
+    assert lib.sgmv_build_segments(ctypes.c_void_p(ids.data_ptr()), 8, 5000, 0, 1,
+                                   ctypes.byref(big.desc), None) == sg.SGMV_EUNSUPPORTED
+
+
+def _fake_pool(L=4, R=16, K=128, N=256, dtype=sg.SGMV_BF16):
+    p = sg._Pool()
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert sg.library().sgmv_pool_init(L, R, K, N, dtype, ctypes.byref(p), ctypes.byref(a),
+                                       ctypes.byref(b)) == 0
+    # non-null placeholders: validation never dereferences them
+    p.a = p.b = p.rank = p.scale = 0x1000
+    return p
+
+
+def test_delta_argument_errors():
+    lib = sg.library()
+    pool = _fake_pool()
+    seg = sg.sgmv_segments_alloc(8, 4, 0, "cpu")
+    y = sg._Slice(0x2000, 256, 0, 256)
+    x = ctypes.c_void_p(0x3000)
+    call = lambda *a: lib.sgmv_lora_delta(*a)
+    # ldx < K
+    assert call(x, 64, 8, ctypes.byref(pool), ctypes.byref(seg.desc), ctypes.byref(y), 1,
+                None) == sg.SGMV_EINVAL
+    # M does not match the segments
+    assert call(x, 128, 9, ctypes.byref(pool), ctypes.byref(seg.desc), ctypes.byref(y), 1,
+                None) == sg.SGMV_EINVAL
+    # slice past N, zero slices, too many slices, overlapping slices
+    bad = sg._Slice(0x2000, 256, 200, 100)
+    assert call(x, 128, 8, ctypes.byref(pool), ctypes.byref(seg.desc), ctypes.byref(bad), 1,
+                None) == sg.SGMV_EINVAL
+    assert call(x, 128, 8, ctypes.byref(pool), ctypes.byref(seg.desc), ctypes.byref(y), 0,
+                None) == sg.SGMV_EINVAL
+    arr = (sg._Slice * 5)(*[sg._Slice(0x2000, 256, 0, 8)] * 5)
+    assert call(x, 128, 8, ctypes.byref(pool), ctypes.byref(seg.desc), arr, 5,
+                None) == sg.SGMV_EINVAL
+    ov = (sg._Slice * 2)(sg._Slice(0x2000, 256, 0, 100), sg._Slice(0x4000, 256, 50, 100))
+    assert call(x, 128, 8, ctypes.byref(pool), ctypes.byref(seg.desc), ov, 2,
+                None) == sg.SGMV_EINVAL
+    # null x, null pool pointer fields
+    assert call(None, 128, 8, ctypes.byref(pool), ctypes.byref(seg.desc), ctypes.byref(y), 1,
+                None) == sg.SGMV_EINVAL
+    p2 = _fake_pool()
+    p2.a = 0
+    assert call(x, 128, 8, ctypes.byref(p2), ctypes.byref(seg.desc), ctypes.byref(y), 1,
+                None) == sg.SGMV_EINVAL
+    # shrink: ldh < R_max
+    assert lib.sgmv_shrink(x, 128, 8, ctypes.byref(pool), ctypes.byref(seg.desc),
+                           ctypes.c_void_p(0x5000), 8, None) == sg.SGMV_EINVAL
+    # expand: null h
+    assert lib.sgmv_expand(None, 16, 8, ctypes.byref(pool), ctypes.byref(seg.desc),
+                           ctypes.byref(y), 1, None) == sg.SGMV_EINVAL
+
+
+def test_empty_batch_is_a_noop():
+    lib = sg.library()
+    pool = _fake_pool()
+    seg = sg.sgmv_segments_alloc(0, 4, 0, "cpu")
+    y = sg._Slice(0x2000, 256, 0, 256)
+    assert lib.sgmv_lora_delta(ctypes.c_void_p(0x3000), 128, 0, ctypes.byref(pool),
+                               ctypes.byref(seg.desc), ctypes.byref(y), 1, None) == sg.SGMV_OK
+
+
+def test_pool_pack_rejects_bad_rank_before_launch():
+    lib = sg.library()
+    pool = _fake_pool(L=2, R=8)
+    rank = torch.tensor([8, 9], dtype=torch.int32)
+    alpha = torch.tensor([1.0, 1.0])
+    assert lib.sgmv_pool_pack(ctypes.c_void_p(0x10), ctypes.c_void_p(0x10),
+                              ctypes.c_void_p(rank.data_ptr()), ctypes.c_void_p(alpha.data_ptr()),
+                              ctypes.byref(pool), None) == sg.SGMV_EINVAL
+    rank = torch.tensor([0, 3], dtype=torch.int32)
+    assert lib.sgmv_pool_pack(ctypes.c_void_p(0x10), ctypes.c_void_p(0x10),
+                              ctypes.c_void_p(rank.data_ptr()), ctypes.c_void_p(alpha.data_ptr()),
+                              ctypes.byref(pool), None) == sg.SGMV_EINVAL

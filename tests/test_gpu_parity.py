@@ -1,0 +1,384 @@
+"""GPU parity: the HIP path through the C-ABI against the fp64 oracle on the same seeded
+inputs.
+
+Bars: segment and index arrays bit-exact (device builder vs host builder vs oracle); y for
+bf16 within relative L2 5e-3 and max-abs 1e-2 * max|ref|, for fp32 within relative L2 1e-4
+(plus the Fused-LoRA page's own max-abs < 1e-3 on its test recipe); every check repeated on
+a zero-base twin (y0 = 0) so the delta itself is held to the bar; rows of tokens without an
+adapter bit-identical to y0; h of the unfused shrink within relative L2 1e-4.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+BF16_REL_L2 = 5e-3
+BF16_MAX_FRAC = 1e-2
+F32_REL_L2 = 1e-4
+
+
+@pytest.fixture(scope="module")
+def sg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import segmented_gather_gemv_amd as m
+    return m
+
+
+DEV = "cuda"
+
+
+def np32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def upload(w, sg, y0_zero=False):
+    pool = sg.sgmv_pool_pack(w.a.to(DEV), w.b.to(DEV), w.rank.tolist(), w.alpha.tolist())
+    x = w.x.to(DEV)
+    y = torch.zeros_like(w.y0).to(DEV) if y0_zero else w.y0.to(DEV)
+    ids = w.ids.to(DEV)
+    return pool, x, y, ids
+
+
+def slice_views(w, y):
+    """Output slices as separate tensors holding the matching columns of y."""
+    return [(y[:, n0:n0 + n].contiguous(), n0) for n0, n in w.slices]
+
+
+def compare(got, ref, dtype, rows=None, what=""):
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
+    diff = got.astype(np.float64) - ref
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(diff) / max(nref, 1e-30)
+    mx = np.max(np.abs(diff)) if diff.size else 0.0
+    if dtype == torch.bfloat16:
+        assert rel <= BF16_REL_L2, f"{what} rel-L2 {rel:.3e}"
+        assert mx <= BF16_MAX_FRAC * np.max(np.abs(ref)), f"{what} max-abs {mx:.3e}"
+    else:
+        assert rel <= F32_REL_L2, f"{what} rel-L2 {rel:.3e}"
+    return rel, mx
+
+
+def oracle_y(w, y0, rows=None):
+    return oracle.lora_delta(np32(w.x), y0, w.ids.numpy(), np32(w.a), np32(w.b),
+                             w.rank.numpy(), w.alpha.numpy(), rows=rows)
+
+
+def run_fused(w, sg, y0_zero=False, chunk=None, on_device=True):
+    pool, x, y, ids = upload(w, sg, y0_zero)
+    C = w.chunk_size if chunk is None else chunk
+    if on_device:
+        seg = sg.sgmv_build_segments(ids, w.L, C, on_device=True)
+    else:
+        seg = sg.sgmv_build_segments(w.ids, w.L, C, on_device=False).to(DEV)
+    outs = slice_views(w, y)
+    sg.sgmv_lora_delta(x, pool, seg, outs if len(outs) > 1 else outs[0][0])
+    torch.cuda.synchronize()
+    yy = y.clone()
+    for t, n0 in outs:
+        n = t.shape[1]
+        yy[:, n0:n0 + n] = t
+    return yy, seg
+
+
+def check_no_adapter_rows(w, y_gpu, y0):
+    neg = (w.ids == -1).numpy()
+    if neg.any():
+        assert torch.equal(y_gpu[torch.from_numpy(neg)].cpu(), y0[torch.from_numpy(neg)].cpu())
+
+
+def sample_rows(w, n, seed=0):
+    """Tokens to check one by one: random ones plus the first and last token of every
+    segment, so the edges of pieces and segments are covered."""
+    seg = oracle.segments(w.ids.numpy(), w.L, w.chunk_size)
+    st, ip = seg["sorted_token_ids"], seg["seg_indptr"]
+    edge = set()
+    for s in range(seg["num_segments"]):
+        edge.add(int(st[ip[s]]))
+        edge.add(int(st[ip[s + 1] - 1]))
+    rng = np.random.default_rng(seed)
+    rnd = set(rng.choice(w.M, size=min(n, w.M), replace=False).tolist())
+    return sorted(edge | rnd)
+
+
+# ---------------------------------------------------------------------------------------
+# segment builder: device == host == oracle, bit for bit
+# ---------------------------------------------------------------------------------------
+def builder_cases():
+    rng = np.random.default_rng(0)
+    cases = [
+        ("example", np.array([2, 2, 2, 5, 5, 1, 1]), 6, 0),
+        ("empty", np.zeros(0, dtype=np.int64), 4, 0),
+        ("all_neg", np.full(3000, -1), 7, 64),
+        ("one", np.array([0]), 1, 0),
+        ("uniform_dec", rng.integers(0, 64, 256), 64, 0),
+        ("distinct_each_lane", np.arange(2048) % 1024, 1024, 0),
+        ("runs", np.repeat(rng.integers(0, 50, 40), rng.integers(1, 300, 40)), 50, 0),
+        ("runs_chunk", np.repeat(rng.integers(0, 50, 40), rng.integers(1, 300, 40)), 50, 7),
+        ("neg_mix_c1", rng.integers(-1, 5, 1500), 5, 1),
+        ("ragged", rng.integers(-1, 300, 5001), 300, 64),
+        ("big_L", rng.integers(-1, 1024, 9000), 1024, 0),
+    ]
+    for name in ("decode", "prefill", "mixed", "qkv"):
+        w = workloads.get(name)
+        cases.append((name, w.ids.numpy(), w.L, w.chunk_size))
+    return cases
+
+
+@pytest.mark.parametrize("case", builder_cases(), ids=lambda c: c[0])
+def test_device_builder_bit_exact(sg, case):
+    name, ids, L, C = case
+    ids_t = torch.as_tensor(np.asarray(ids, dtype=np.int32))
+    dev = sg.sgmv_build_segments(ids_t.to(DEV), L, C, on_device=True).host()
+    host = sg.sgmv_build_segments(ids_t, L, C, on_device=False).host()
+    ref = oracle.segments(ids_t.numpy(), L, C)
+    M = ids_t.numel()
+    assert dev["status"] == sg.SGMV_OK
+    assert np.array_equal(dev["sorted_token_ids"].numpy()[:M], ref["sorted_token_ids"])
+    for k in ("sorted_token_ids", "seg_indptr", "seg_lora_ids", "large_tiles", "small_tiles"):
+        assert torch.equal(dev[k][:M] if k == "sorted_token_ids" else dev[k],
+                           host[k][:M] if k == "sorted_token_ids" else host[k]), k
+    assert dev["num_segments"] == host["num_segments"] == ref["num_segments"]
+
+
+def test_device_builder_bad_ids_flagged(sg):
+    ids = torch.tensor([0, 5, 1, -3, 0, 2], dtype=torch.int32)
+    dev = sg.sgmv_build_segments(ids.to(DEV), 3, 0, on_device=True).host()
+    assert dev["status"] == sg.SGMV_EBADID
+    clean = torch.tensor([0, -1, 1, -1, 0, 2], dtype=torch.int32)
+    ref = oracle.segments(clean.numpy(), 3, 0)
+    assert np.array_equal(dev["sorted_token_ids"].numpy(), ref["sorted_token_ids"])
+    assert np.array_equal(dev["seg_indptr"].numpy(), ref["seg_indptr"])
+
+
+def test_device_builder_reuse_of_buffers(sg):
+    """Building twice into the same arrays (the per-step pattern) gives the same result."""
+    w = workloads.get("decode")
+    ids = w.ids.to(DEV)
+    seg = sg.sgmv_build_segments(ids, w.L, 0, on_device=True)
+    first = seg.host()
+    sg.sgmv_build_segments(ids, w.L, 0, on_device=True, out=seg)
+    again = seg.host()
+    for k in ("sorted_token_ids", "seg_indptr", "seg_lora_ids", "large_tiles", "small_tiles"):
+        assert torch.equal(first[k], again[k])
+
+
+# ---------------------------------------------------------------------------------------
+# the Fused-LoRA page's test recipe (fp32)
+# ---------------------------------------------------------------------------------------
+def test_tiny_recipe_fp32(sg):
+    rec = json.load(open(os.path.join(GOLDEN, "fused_lora_test_recipe.json")))
+    w = workloads.tiny()
+    assert w.ids.tolist() == rec["lora_indices"] and w.M == rec["batch_size"]
+    assert (w.K, w.N, w.L, w.R) == (rec["in_dim"], rec["out_dim"], rec["num_loras"], rec["r"])
+    y_gpu, _ = run_fused(w, sg, y0_zero=True)
+    ref = oracle_y(w, np.zeros((w.M, w.N)))
+    got = np32(y_gpu)
+    assert np.max(np.abs(got - ref)) < rec["max_abs_tol"]
+    compare(got, ref, torch.float32, what="tiny")
+
+
+# ---------------------------------------------------------------------------------------
+# parity on small shapes spanning several pieces and ragged tails
+# ---------------------------------------------------------------------------------------
+SMALL_CASES = {
+    # name: custom() kwargs
+    "bf16_ragged": dict(M=300, K=512, N=640, L=8, R=16, no_lora_frac=0.1),
+    "bf16_mixed_rank": dict(M=333, K=384, N=320, L=12, R=64, ranks=[3, 8, 16, 24, 33, 64],
+                            no_lora_frac=0.15),
+    "bf16_prefill_like": dict(M=700, K=256, N=512, L=6, R=32,
+                              seq_lens=[200, 17, 1, 64, 130, 288]),
+    "bf16_odd_shape": dict(M=77, K=100, N=37, L=5, R=3),
+    "bf16_odd_shape_rank": dict(M=150, K=136, N=200, L=4, R=40, ranks=[1, 9, 17, 40]),
+    "bf16_chunked": dict(M=500, K=256, N=256, L=3, R=16, chunk=13, no_lora_frac=0.05),
+    "f32_ragged": dict(M=130, K=200, N=96, L=5, R=16, dtype=torch.float32, w_std=0.1,
+                       no_lora_frac=0.1),
+    "f32_odd": dict(M=40, K=100, N=37, L=3, R=3, dtype=torch.float32, w_std=0.1),
+    "f32_mixed_rank": dict(M=90, K=64, N=70, L=6, R=64, ranks=[1, 5, 16, 64],
+                           dtype=torch.float32, w_std=0.1, seq_lens=[70, 20]),
+}
+
+
+def small_workload(name, y0_zero=False):
+    kw = dict(SMALL_CASES[name])
+    return workloads.custom(name=name, y0_zero=y0_zero, seed=7, **kw)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_CASES))
+@pytest.mark.parametrize("zero_base", [False, True])
+def test_fused_small(sg, name, zero_base):
+    w = small_workload(name, y0_zero=zero_base)
+    y_gpu, _ = run_fused(w, sg)
+    ref = oracle_y(w, np32(w.y0))
+    compare(np32(y_gpu), ref, w.dtype, what=name)
+    check_no_adapter_rows(w, y_gpu, w.y0)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_CASES))
+def test_unfused_small(sg, name):
+    w = small_workload(name)
+    pool, x, y, ids = upload(w, sg)
+    seg = sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True)
+    h = sg.sgmv_shrink(x, pool, seg)
+    torch.cuda.synchronize()
+    h_ref = oracle.shrink(np32(w.x), w.ids.numpy(), np32(w.a), w.rank.numpy())
+    lora = w.ids.numpy() >= 0
+    hg = h.cpu().numpy()[lora]
+    hr = h_ref[lora]
+    assert np.linalg.norm(hg - hr) / max(np.linalg.norm(hr), 1e-30) <= 1e-4
+    # expand from the GPU h
+    sg.sgmv_expand(h, pool, seg, y)
+    torch.cuda.synchronize()
+    ref = oracle.expand(h_ref, np32(w.y0), w.ids.numpy(), np32(w.b), w.rank.numpy(),
+                        w.alpha.numpy())
+    compare(np32(y), ref, w.dtype, what=name + " unfused")
+    check_no_adapter_rows(w, y, w.y0)
+
+
+def test_rank_padding_never_read(sg):
+    """Poison every pool entry at ranks >= r_l with NaN: y must not change at all."""
+    w = small_workload("bf16_mixed_rank")
+    pool, x, y, ids = upload(w, sg)
+    seg = sg.sgmv_build_segments(ids, w.L, 0, on_device=True)
+    y_clean = y.clone()
+    sg.sgmv_lora_delta(x, pool, seg, y_clean)
+    torch.cuda.synchronize()
+    nan = float("nan")
+    for l, r in enumerate(w.rank.tolist()):
+        pool.a[l, r:, :] = nan
+        # rank octets: ranks j >= r live at b[l, j // 8, :, j % 8]
+        for j in range(r, pool.b.shape[1] * 8):
+            pool.b[l, j // 8, :, j % 8] = nan
+    y_nan = y.clone()
+    sg.sgmv_lora_delta(x, pool, seg, y_nan)
+    torch.cuda.synchronize()
+    assert torch.equal(y_clean, y_nan)
+
+
+def test_guard_bands_and_strides(sg):
+    """x and y as strided views inside larger buffers: nothing outside the views changes."""
+    w = small_workload("bf16_ragged")
+    pool = sg.sgmv_pool_pack(w.a.to(DEV), w.b.to(DEV), w.rank.tolist(), w.alpha.tolist())
+    xb = torch.randn(w.M + 6, w.K + 40, generator=torch.Generator().manual_seed(3)).to(
+        torch.bfloat16).to(DEV)
+    xb[3:3 + w.M, 8:8 + w.K] = w.x.to(DEV)
+    x = xb[3:3 + w.M, 8:8 + w.K]
+    yb = torch.full((w.M + 4, w.N + 24), 7.0, dtype=torch.bfloat16, device=DEV)
+    yb[2:2 + w.M, 8:8 + w.N] = w.y0.to(DEV)
+    y = yb[2:2 + w.M, 8:8 + w.N]
+    before = yb.clone()
+    seg = sg.sgmv_build_segments(w.ids.to(DEV), w.L, 0, on_device=True)
+    sg.sgmv_lora_delta(x, pool, seg, y)
+    torch.cuda.synchronize()
+    mask = torch.ones_like(yb, dtype=torch.bool)
+    mask[2:2 + w.M, 8:8 + w.N] = False
+    assert torch.equal(yb[mask], before[mask])
+    compare(np32(y), oracle_y(w, np32(w.y0)), w.dtype, what="strided")
+
+
+def test_chunk_size_and_host_segments_agree(sg):
+    w = small_workload("bf16_ragged")
+    ref = oracle_y(w, np32(w.y0))
+    for C in (0, 1, 5, 64):
+        for on_dev in (True, False):
+            y_gpu, _ = run_fused(w, sg, chunk=C, on_device=on_dev)
+            compare(np32(y_gpu), ref, w.dtype, what=f"chunk {C} dev {on_dev}")
+
+
+def test_token_permutation(sg):
+    w = small_workload("bf16_ragged", y0_zero=True)
+    y_a, _ = run_fused(w, sg)
+    perm = torch.from_numpy(np.random.default_rng(4).permutation(w.M))
+    wp = workloads.Workload(w.name, w.dtype, w.ids[perm], w.x[perm], w.a, w.b, w.y0[perm],
+                            w.rank, w.alpha)
+    y_b, _ = run_fused(wp, sg)
+    compare(np32(y_b), np32(y_a)[perm.numpy()].astype(np.float64), w.dtype, what="perm")
+
+
+def test_all_no_adapter_and_empty(sg):
+    w = small_workload("bf16_ragged")
+    w.ids[:] = -1
+    y_gpu, _ = run_fused(w, sg)
+    assert torch.equal(y_gpu.cpu(), w.y0)
+    e = workloads.custom(M=0, K=64, N=64, L=2, R=16)
+    y_gpu, _ = run_fused(e, sg)
+    assert y_gpu.numel() == 0
+
+
+def test_bad_ids_on_device_are_skipped(sg):
+    w = small_workload("bf16_ragged")
+    bad = w.ids.clone()
+    bad[5] = 99
+    bad[17] = -4
+    pool, x, y, _ = upload(w, sg)
+    seg = sg.sgmv_build_segments(bad.to(DEV), w.L, 0, on_device=True)
+    sg.sgmv_lora_delta(x, pool, seg, y)
+    torch.cuda.synchronize()
+    assert int(seg.info[3].item()) == sg.SGMV_EBADID
+    clean = bad.clone()
+    clean[5] = -1
+    clean[17] = -1
+    ref = oracle.lora_delta(np32(w.x), np32(w.y0), clean.numpy(), np32(w.a), np32(w.b),
+                            w.rank.numpy(), w.alpha.numpy())
+    compare(np32(y), ref, w.dtype, what="bad ids")
+    assert torch.equal(y[5].cpu(), w.y0[5]) and torch.equal(y[17].cpu(), w.y0[17])
+
+
+def test_slices_in_any_order(sg):
+    """Three output slices listed out of pool order, each its own tensor."""
+    w = workloads.custom(M=120, K=256, N=320, L=5, R=32, seed=3, no_lora_frac=0.1,
+                         slices=[(0, 192), (192, 64), (256, 64)])
+    pool, x, y, ids = upload(w, sg)
+    seg = sg.sgmv_build_segments(ids, w.L, 0, on_device=True)
+    q = y[:, 0:192].contiguous()
+    k = y[:, 192:256].contiguous()
+    v = y[:, 256:320].contiguous()
+    sg.sgmv_lora_delta(x, pool, seg, [(v, 256), (q, 0), (k, 192)])
+    torch.cuda.synchronize()
+    got = torch.cat([q, k, v], dim=1)
+    compare(np32(got), oracle_y(w, np32(w.y0)), w.dtype, what="slices")
+
+
+# ---------------------------------------------------------------------------------------
+# full-size workloads, checked on sampled tokens
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed", "qkv"])
+@pytest.mark.parametrize("zero_base", [False, True])
+def test_fused_full_size(sg, name, zero_base):
+    w = workloads.get(name)
+    if zero_base:
+        w.y0 = torch.zeros_like(w.y0)
+    y_gpu, seg = run_fused(w, sg)
+    assert int(seg.info[3].item()) == sg.SGMV_OK
+    rows = sample_rows(w, 128)
+    ref = oracle_y(w, np32(w.y0), rows=rows)
+    compare(np32(y_gpu), ref, w.dtype, rows=rows, what=name)
+    check_no_adapter_rows(w, y_gpu, w.y0)
+
+
+@pytest.mark.parametrize("name", ["decode", "mixed"])
+def test_unfused_full_size(sg, name):
+    w = workloads.get(name)
+    pool, x, y, ids = upload(w, sg)
+    seg = sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True)
+    h = sg.sgmv_shrink(x, pool, seg)
+    sg.sgmv_expand(h, pool, seg, y)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 96)
+    h_ref = oracle.shrink(np32(w.x), w.ids.numpy(), np32(w.a), w.rank.numpy(), rows=rows)
+    hr = h_ref[rows]
+    hg = h.cpu().numpy()[rows]
+    lora = w.ids.numpy()[rows] >= 0
+    assert np.linalg.norm(hg[lora] - hr[lora]) / np.linalg.norm(hr[lora]) <= 1e-4
+    ref = oracle_y(w, np32(w.y0), rows=rows)
+    compare(np32(y), ref, w.dtype, rows=rows, what=name + " unfused")

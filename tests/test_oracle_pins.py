@@ -342,12 +342,13 @@ def test_rows_subset_matches_full():
 
 
 def test_algorithmic_counts():
+    import workloads
     ids = np.asarray([0, 0, 1, -1])
     rank = np.asarray([4, 2])
     # x: 3 rows * K, y: 3 rows * N read+write, weights (4+2)*(K+N), 12 B index per token
     K, N = 10, 6
-    assert oracle.algorithmic_bytes(ids, rank, K, N, 2) == (3 * K + 2 * 3 * N + 6 * (K + N)) * 2 + 48
-    assert oracle.algorithmic_flops(ids, rank, K, N) == 2 * (K + N) * (4 + 4 + 2)
+    assert workloads.algorithmic_bytes(ids, rank, K, N, 2) == (3 * K + 2 * 3 * N + 6 * (K + N)) * 2 + 48
+    assert workloads.algorithmic_flops(ids, rank, K, N) == 2 * (K + N) * (4 + 4 + 2)
 
 
 # ---------------------------------------------------------------------------------------

@@ -23,6 +23,7 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence, Tuple
 
+import numpy as _np
 import torch
 
 SEED = 42
@@ -244,6 +245,31 @@ def custom(M: int, K: int, N: int, L: int, R: int, dtype: torch.dtype = torch.bf
     return Workload(name, dtype, ids, x, a, b, y0, rank, al, chunk_size=chunk,
                     slices=list(slices) if slices else [],
                     note=f"custom M={M} K={K} N={N} L={L} R={R} {dtype}")
+
+
+# ---------------------------------------------------------------------------------------
+# accounting (counts only; used for roofline figures)
+# ---------------------------------------------------------------------------------------
+def algorithmic_bytes(ids, rank, K: int, N: int, elem_bytes: int) -> int:
+    """Bytes the method itself must move for one delta over a batch: x rows of tokens with
+    an adapter (read once), their y rows (read and written), each used adapter's true-rank
+    A[l, :r, :] and B[l, :, :r] (read once), and the int32 index arrays (ids, sorted ids,
+    segment arrays: about 12 B per token). Padding, re-reads and the intermediate h are
+    excluded."""
+    ids = _np.asarray(ids)
+    lora = ids[ids >= 0]
+    m = int(lora.shape[0])
+    used = _np.unique(lora)
+    w = sum(int(rank[l]) * (K + N) for l in used)
+    return (m * K + 2 * m * N + w) * elem_bytes + 12 * int(ids.shape[0])
+
+
+def algorithmic_flops(ids, rank, K: int, N: int) -> int:
+    """2 * r * (K + N) per token with an adapter (Ascend article 3.2: about 2 d r M per
+    stage)."""
+    ids = _np.asarray(ids)
+    return int(sum(2 * int(rank[l]) * (K + N) for l in ids[ids >= 0]))
+
 
 
 BY_NAME = {"tiny": tiny, "decode": decode, "prefill": prefill, "mixed": mixed, "qkv": qkv}
