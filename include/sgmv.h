@@ -21,6 +21,7 @@
  *     chip), 5.3 (skip rows without adapter).
  *
  * Conventions for every call:
+ *   - M = 0 is a no-op that returns SGMV_OK; data pointers may then be NULL.
  *   - Pointers are device memory owned by the caller unless a parameter says "host".
  *   - Calls that take a stream are asynchronous and ordered on that stream (a hipStream_t
  *     passed as void*; NULL is the default stream). The library allocates nothing on these
@@ -56,6 +57,8 @@ typedef enum { SGMV_F32 = 0, SGMV_BF16 = 1 } sgmv_dtype;
  * (decode-like) rather than "large" (prefill-like); Ascend article 3.3 and 4.1. */
 #define SGMV_TILE_ROWS 64
 #define SGMV_SMALL_ROWS 16
+/* int32 entries per work descriptor record (one 128-byte line). */
+#define SGMV_TILE_INTS 32
 /* Largest adapter rank the kernels take (Ascend article 2.1: a maximum LoRA rank). */
 #define SGMV_MAX_RANK 64
 /* Largest pool the on-device segment builder takes (its tables live in LDS). */
@@ -116,14 +119,17 @@ sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t
  *
  * Work descriptors ("tiles"): every segment is cut into pieces of at most SGMV_TILE_ROWS
  * rows, in segment order. A piece of at most SGMV_SMALL_ROWS rows is small, otherwise large.
- * tiles[i*4 .. i*4+3] = {adapter, first row in sorted order, rows, segment}; large pieces
- * occupy slots [0, large_cap), small ones [large_cap, large_cap + small_cap).
+ * Each descriptor is a record of SGMV_TILE_INTS int32 at tiles + i * SGMV_TILE_INTS:
+ *   [0] adapter, [1] first row in sorted order, [2] rows, [3] segment, [4..15] 0,
+ *   [16..31] for a small piece its token ids (sorted_token_ids[first .. first + rows)), then
+ *            -1; for a large piece all -1.
+ * Large pieces occupy records [0, large_cap), small ones [large_cap, large_cap + small_cap).
  * info[4] = {num_segments, num_large_tiles, num_small_tiles, status}.
  *
  * Capacities: seg_cap = min(M, L) without chunking, min(M, min(M, L) + M / C) with;
  * large_cap = M / (SGMV_SMALL_ROWS + 1); small_cap = seg_cap.
  * Array sizes: sorted_token_ids [M], seg_indptr [seg_cap + 1], seg_lora_ids [seg_cap],
- * tiles [(large_cap + small_cap) * 4], info [4].
+ * tiles [(large_cap + small_cap) * SGMV_TILE_INTS], info [4].
  * ------------------------------------------------------------------------------------ */
 typedef struct {
   int32_t* sorted_token_ids;

@@ -29,6 +29,7 @@ SGMV_OK, SGMV_EINVAL, SGMV_EBADID, SGMV_EUNSUPPORTED, SGMV_ECAPACITY, SGMV_EHIP 
 SGMV_F32, SGMV_BF16 = 0, 1
 TILE_ROWS = 64
 SMALL_ROWS = 16
+TILE_INTS = 32
 MAX_RANK = 64
 MAX_SLICES = 4
 DEVICE_BUILDER_MAX_L = 1024
@@ -200,7 +201,7 @@ class Segments:
     sorted_token_ids: torch.Tensor
     seg_indptr: torch.Tensor
     seg_lora_ids: torch.Tensor
-    tiles: torch.Tensor          # [(large_cap + small_cap), 4]
+    tiles: torch.Tensor          # [(large_cap + small_cap), TILE_INTS] descriptor records
     info: torch.Tensor           # [4]: num_segments, n_large, n_small, status
     desc: _Segments
 
@@ -246,8 +247,8 @@ def sgmv_segments_alloc(M: int, L: int, chunk_size: int = 0,
     dev = torch.device(device)
     z = lambda n: torch.zeros(max(int(n), 1), dtype=torch.int32, device=dev)
     seg = Segments(z(M), z(desc.seg_cap + 1), z(desc.seg_cap),
-                   torch.zeros(max(desc.large_cap + desc.small_cap, 1), 4, dtype=torch.int32,
-                               device=dev), z(4), desc)
+                   torch.zeros(max(desc.large_cap + desc.small_cap, 1), TILE_INTS,
+                               dtype=torch.int32, device=dev), z(4), desc)
     seg._bind()
     return seg
 

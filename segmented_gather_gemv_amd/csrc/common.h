@@ -56,17 +56,39 @@ struct DeltaArgs {
   const int32_t* rank;
   const float* scale;
   int32_t R_max, R_pad, K, K_pad, N_pad;
+  int32_t L;
   const int32_t* sorted;  // sorted_token_ids
-  const int32_t* tiles;   // work descriptors
+  const int32_t* tiles;   // work descriptor records (SGMV_TILE_INTS ints each)
   const int32_t* info;    // {num_segments, n_large, n_small, status}
-  int32_t large_cap;
-  int32_t n_split_large;  // workgroups across output columns per large tile
-  int32_t n_split_small;  // ... per small tile
+  int32_t large_cap, small_cap;
+  int32_t n_split_large;  // workgroups across output columns per large piece
+  int32_t n_split_small;  // ... per small piece
+  int32_t grid_large;     // workgroups [0, grid_large) take large pieces, the rest small ones
   int32_t n_slices;
   int32_t v_total;        // sum of slice widths
   SliceArg slices[SGMV_MAX_SLICES];
 };
 
 enum Mode { MODE_FUSED = 0, MODE_SHRINK = 1, MODE_EXPAND = 2 };
+
+// Piece and column split of this workgroup, from its index alone. Workgroups
+// [0, grid_large) take large pieces, the rest small ones; within a class, piece i runs on
+// XCD i % 8 (workgroup b runs on XCD b % 8) and its P column splits on consecutive slots of
+// that XCD. Returns false for a workgroup past the class capacity.
+__device__ __forceinline__ bool locate_piece(const DeltaArgs& A, bool split, bool& small,
+                                             int& tile, int& p, int& P) {
+  int b = blockIdx.x;
+  small = b >= A.grid_large;
+  if (small) b -= A.grid_large;
+  P = split ? (small ? A.n_split_small : A.n_split_large) : 1;
+  const int slot = b >> 3;
+  const int q = slot / P;
+  tile = q * 8 + (b & 7);
+  p = slot - q * P;
+  return tile < (small ? A.small_cap : A.large_cap);
+}
+
+// Workgroups for one class of pieces: 8 XCDs x P splits x ceil(cap / 8) pieces per XCD.
+inline int class_grid(int cap, int P) { return 8 * P * ((cap + 7) / 8); }
 
 }  // namespace sgmv

@@ -13,49 +13,25 @@ namespace sgmv {
 constexpr int F_THREADS = 256;
 constexpr int F_HS = 65;  // LDS row stride of the h tile
 
-struct FWork {
-  int lora, start, rows, v0, v1;
-};
-
-__device__ __forceinline__ bool f32_decode_work(const DeltaArgs& A, bool split_cols, FWork& wi) {
-  const int n_large = A.info[1], n_small = A.info[2];
-  const int PL = split_cols ? A.n_split_large : 1;
-  const int PS = split_cols ? A.n_split_small : 1;
-  const int work_l = n_large * PL;
-  const int work = work_l + n_small * PS;
-  const int b = blockIdx.x;
-  const int per = (work + 7) >> 3;
-  const int slot = b >> 3;
-  if (slot >= per) return false;
-  const int u = (b & 7) * per + slot;
-  if (u >= work) return false;
-  int tile, p, P;
-  if (u < work_l) {
-    tile = u / PL;
-    p = u - tile * PL;
-    P = PL;
-  } else {
-    const int v = u - work_l;
-    tile = A.large_cap + v / PS;
-    p = v % PS;
-    P = PS;
-  }
-  const int32_t* d = A.tiles + (size_t)tile * 4;
-  wi.lora = d[0];
-  wi.start = d[1];
-  wi.rows = d[2];
-  const int width = (((A.v_total + P - 1) / P) + 63) & ~63;
-  wi.v0 = p * width;
-  wi.v1 = min(wi.v0 + width, A.v_total);
-  return !split_cols || wi.v0 < wi.v1;
-}
-
 template <int MODE>
 __global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
   __shared__ int s_tok[SGMV_TILE_ROWS];
   __shared__ float s_h[SGMV_TILE_ROWS * F_HS];
-  FWork wi;
-  if (!f32_decode_work(A, MODE != MODE_SHRINK, wi)) return;
+  bool small;
+  int tile, p, P;
+  if (!locate_piece(A, MODE != MODE_SHRINK, small, tile, p, P)) return;
+  const int32_t* rec = A.tiles + (size_t)(small ? A.large_cap + tile : tile) * SGMV_TILE_INTS;
+  if (tile >= A.info[small ? 2 : 1]) return;
+  struct {
+    int lora, start, rows, v0, v1;
+  } wi;
+  wi.lora = rec[0];
+  wi.start = rec[1];
+  wi.rows = rec[2];
+  const int width = (((A.v_total + P - 1) / P) + 63) & ~63;
+  wi.v0 = p * width;
+  wi.v1 = min(wi.v0 + width, A.v_total);
+  if (MODE != MODE_SHRINK && wi.v0 >= wi.v1) return;
   const int r = A.rank[wi.lora];
   const float scale = A.scale[wi.lora];
   const int tid = threadIdx.x;
@@ -126,7 +102,10 @@ __global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
   }
 }
 
-hipError_t launch_delta_f32(int mode, const DeltaArgs& A, int grid, hipStream_t stream) {
+hipError_t launch_delta_f32(int mode, DeltaArgs A, hipStream_t stream) {
+  const bool split = mode != MODE_SHRINK;
+  A.grid_large = class_grid(A.large_cap, split ? A.n_split_large : 1);
+  const int grid = A.grid_large + class_grid(A.small_cap, split ? A.n_split_small : 1);
   if (grid <= 0) return hipSuccess;
   const dim3 g(grid), b(F_THREADS);
   if (mode == MODE_FUSED)

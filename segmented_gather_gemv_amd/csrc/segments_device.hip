@@ -2,15 +2,19 @@
 // workgroup, with no host synchronisation (Ascend article 4.2: a per-step sort that syncs
 // host and device sits on the critical path).
 //
-// One workgroup of 16 waves walks the tokens in rounds of 1024 (one 64-token chunk per
-// wave). Inside a chunk, lanes holding the same key are grouped with ballots: the lowest
-// lane leads, its group's size goes into a per-(key, wave) byte table in LDS, and each lane
-// learns its rank among the equal keys of lower lanes. Across the waves of a round, the
-// table gives each lane the count of equal keys in lower waves. A per-key running counter
-// carries the count over rounds. Pass 1 counts keys and records where each adapter first
-// appears; the bucket order (by first appearance), bucket starts, segment arrays and work
-// descriptors follow from scans; pass 2 repeats the rounds and scatters every token to
-// base[key] + (equal keys before it), which keeps tokens ascending inside a bucket.
+// Shared definitions: keys are adapter ids, with key L standing for "no adapter" (-1, or a
+// bad id, which also raises the status flag). Buckets follow the order in which adapters
+// first appear; tokens ascend inside a bucket (Punica page, code section; worked example in
+// the batching-effect section). A token lands at bucket start + (equal keys before it).
+//
+// Two kernels:
+//  * small batches (M <= 1024, one token per thread): each wave ranks its 64 keys in
+//    registers (readlane loop), a per-(key, wave) byte table in LDS adds the counts of lower
+//    waves, and one workgroup scan over the tokens of (first-appearance flag, bucket size,
+//    segments, large and small descriptors) places every bucket;
+//  * larger batches: the same in rounds of 1024 tokens with a running count per key, lanes
+//    of equal keys grouped by ballots.
+// Every global write index is checked against its array bound.
 #include <climits>
 
 #include "common.h"
@@ -22,38 +26,220 @@ constexpr int BUILD_WAVES = BUILD_THREADS / WAVE;
 
 __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
 
-// Dynamic LDS bytes for a pool of L adapters.
-size_t build_lds_bytes(int L) {
-  const size_t nk = (size_t)L + 1;
-  return align16(nk * BUILD_WAVES) + 6 * align16((nk + 1) * sizeof(int));
+// Inclusive scan across the 64 lanes of a wave with DPP row shifts and row broadcasts.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
-// Exclusive scan of one int per thread across the workgroup. s_w holds BUILD_WAVES + 1
-// ints; on return *total is the sum. Contains barriers: call from all threads.
-__device__ int block_exclusive_scan(int v, int* s_w, int* total) {
+// Exclusive scan of NV ints per thread across the workgroup. s_w holds NV * BUILD_WAVES
+// ints. Contains barriers: call from all threads.
+template <int NV>
+__device__ void block_scan(const int (&v)[NV], int (&ex)[NV], int (&tot)[NV], int* s_w) {
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  int x = v;
+  int x[NV];
 #pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) {
-    const int y = __shfl_up(x, off, WAVE);
-    if (lane >= off) x += y;
+  for (int i = 0; i < NV; ++i) {
+    x[i] = wave_incl_scan(v[i]);
+    if (lane == WAVE - 1) s_w[i * BUILD_WAVES + w] = x[i];
   }
-  if (lane == WAVE - 1) s_w[w] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < BUILD_WAVES; ++i) {
-      const int t = s_w[i];
-      s_w[i] = acc;
-      acc += t;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int4* q = reinterpret_cast<const int4*>(s_w + i * BUILD_WAVES);
+    int before = 0, all = 0;
+#pragma unroll
+    for (int j = 0; j < BUILD_WAVES / 4; ++j) {
+      const int4 s = q[j];
+      const int vals[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        all += vals[e];
+        before += (4 * j + e < w) ? vals[e] : 0;
+      }
     }
-    s_w[BUILD_WAVES] = acc;
+    ex[i] = before + x[i] - v[i];
+    tot[i] = all;
   }
   __syncthreads();
-  const int res = s_w[w] + x - v;
-  *total = s_w[BUILD_WAVES];
+}
+
+// Counts of equal keys in lower waves (pre), in this wave (cw) and in higher waves (post),
+// from the per-(key, wave) byte table.
+__device__ __forceinline__ void wave_counts(const uint8_t* rc, int key, int& pre, int& cw,
+                                            int& post) {
+  const int w = threadIdx.x / WAVE;
+  const u32x4_t q = *reinterpret_cast<const u32x4_t*>(rc + key * BUILD_WAVES);
+  pre = cw = post = 0;
+#pragma unroll
+  for (int i = 0; i < BUILD_WAVES; ++i) {
+    const int v = (q[i >> 2] >> (8 * (i & 3))) & 0xff;
+    if (i < w) pre += v;
+    else if (i == w) cw = v;
+    else post += v;
+  }
+}
+
+// Descriptor counts of one segment of `len` rows.
+__device__ __forceinline__ void piece_tiles(int len, int& nl, int& ns) {
+  const int rem = len % SGMV_TILE_ROWS;
+  nl = len / SGMV_TILE_ROWS + (rem > SGMV_SMALL_ROWS ? 1 : 0);
+  ns = (rem > 0 && rem <= SGMV_SMALL_ROWS) ? 1 : 0;
+}
+
+// Writes the descriptors of one bucket (adapter `lora`, `cnt` rows from sorted row `start`,
+// chunk size C) and its segments. Token slots of small descriptors are left to the tokens'
+// own threads (token_slot); every other token slot gets -1.
+__device__ void write_bucket(int lora, int cnt, int C, int start, int seg0, int lt, int st,
+                             int32_t* indptr, int32_t* seg_lora, int32_t* tiles, int seg_cap,
+                             int large_cap, int small_cap) {
+  const int np = C > 0 ? (cnt + C - 1) / C : 1;
+  for (int i = 0; i < np; ++i) {
+    const int seg = seg0 + i;
+    const int s0 = start + (C > 0 ? i * C : 0);
+    const int len = C > 0 ? min(C, cnt - i * C) : cnt;
+    if (seg < seg_cap) {
+      indptr[seg] = s0;
+      seg_lora[seg] = lora;
+    }
+    for (int r0 = 0; r0 < len; r0 += SGMV_TILE_ROWS) {
+      const int rows = min(SGMV_TILE_ROWS, len - r0);
+      const bool small = rows <= SGMV_SMALL_ROWS;
+      const int idx = small ? st++ : lt++;
+      if (small ? idx >= small_cap : idx >= large_cap) continue;
+      int32_t* d = tiles + (size_t)(small ? large_cap + idx : idx) * SGMV_TILE_INTS;
+      d[0] = lora;
+      d[1] = s0 + r0;
+      d[2] = rows;
+      d[3] = seg;
+#pragma unroll
+      for (int e = 4; e < 16; ++e) d[e] = 0;
+      for (int e = small ? rows : 0; e < 16; ++e) d[16 + e] = -1;
+    }
+  }
+}
+
+// The token with in-bucket rank `rank` of a bucket of `cnt` rows whose first small
+// descriptor is `sbase`: if it lands in a small descriptor, store its id in that record.
+__device__ __forceinline__ void token_slot(int t, int rank, int cnt, int C, int sbase,
+                                           int32_t* tiles, int large_cap, int small_cap) {
+  const int i = C > 0 ? rank / C : 0;                  // segment (chunk) inside the bucket
+  const int in_seg = C > 0 ? rank - i * C : rank;
+  const int len = C > 0 ? min(C, cnt - i * C) : cnt;
+  const int piece = in_seg / SGMV_TILE_ROWS;
+  const int rows = min(SGMV_TILE_ROWS, len - piece * SGMV_TILE_ROWS);
+  if (rows > SGMV_SMALL_ROWS) return;
+  int nl_full, ns_full;
+  piece_tiles(C > 0 ? C : cnt, nl_full, ns_full);
+  const int sidx = sbase + (C > 0 ? i * ns_full : 0);  // one small piece at most per segment
+  const int slot = in_seg - piece * SGMV_TILE_ROWS;
+  if (sidx < small_cap && slot < SGMV_SMALL_ROWS)
+    tiles[(size_t)(large_cap + sidx) * SGMV_TILE_INTS + 16 + slot] = t;
+}
+
+// ---------------------------------------------------------------------------------------
+// small batches: M <= 1024
+// ---------------------------------------------------------------------------------------
+size_t build_small_lds_bytes(int L) {
+  const size_t nk = (size_t)L + 1;
+  return align16(nk * BUILD_WAVES) + 2 * align16(nk * sizeof(int));
+}
+
+__global__ __launch_bounds__(BUILD_THREADS) void build_segments_small_kernel(
+    const int32_t* __restrict__ ids, int M, int L, int C, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ indptr, int32_t* __restrict__ seg_lora, int32_t* __restrict__ tiles,
+    int32_t* __restrict__ info, int seg_cap, int large_cap, int small_cap) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NK = L + 1;
+  uint8_t* rc = smem;                                                              // [NK][16]
+  int* s_base = reinterpret_cast<int*>(smem + align16((size_t)NK * BUILD_WAVES));  // [NK]
+  int* s_sbase = s_base + align16((size_t)NK * sizeof(int)) / sizeof(int);        // [NK]
+  __shared__ __align__(16) int s_w[5 * BUILD_WAVES];
+  __shared__ int s_bad;
+
+  const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+  const bool valid = t < M;
+  for (int i = t; i < NK * (BUILD_WAVES / 4); i += BUILD_THREADS)
+    reinterpret_cast<uint32_t*>(rc)[i] = 0;
+  if (t == 0) s_bad = 0;
+  int key = -2;  // never equal to a real key (0..L)
+  if (valid) {
+    int id = ids[t];
+    if (id < -1 || id >= L) {
+      s_bad = 1;
+      id = -1;
+    }
+    key = id < 0 ? L : id;
+  }
+  // rank among equal keys of lower lanes, and the count in this wave, in registers
+  const int n_in_wave = min(WAVE, max(0, M - w * WAVE));
+  int rk = 0, cw = 0;
+  for (int j = 0; j < n_in_wave; ++j) {
+    const int kj = __builtin_amdgcn_readlane(key, j);
+    const int eq = kj == key ? 1 : 0;
+    cw += eq;
+    rk += j < lane ? eq : 0;
+  }
   __syncthreads();
-  return res;
+  if (valid && rk == 0) rc[key * BUILD_WAVES + w] = (uint8_t)cw;
+  __syncthreads();
+  int pre = 0, cwt = 0, post = 0;
+  if (valid) wave_counts(rc, key, pre, cwt, post);
+  const int rank = pre + rk;
+  const int cnt = pre + cwt + post;
+  const bool first = valid && key < L && rank == 0;
+  int v[5] = {0, 0, 0, 0, 0};
+  if (first) {
+    const int np = C > 0 ? (cnt + C - 1) / C : 1;
+    const int last = C > 0 ? cnt - C * (np - 1) : cnt;
+    int nl, ns, nl1, ns1;
+    piece_tiles(C > 0 ? C : cnt, nl, ns);
+    piece_tiles(last, nl1, ns1);
+    v[0] = 1;
+    v[1] = cnt;
+    v[2] = np;
+    v[3] = (np - 1) * nl + nl1;
+    v[4] = (np - 1) * ns + ns1;
+  }
+  int ex[5], tot[5];
+  block_scan<5>(v, ex, tot, s_w);
+  const int n_lora = tot[1], n_seg = tot[2], n_large = tot[3], n_small = tot[4];
+  const bool overflow = n_seg > seg_cap || n_large > large_cap || n_small > small_cap;
+  if (first) {
+    s_base[key] = ex[1];
+    s_sbase[key] = ex[4];
+    if (!overflow)
+      write_bucket(key, cnt, C, ex[1], ex[2], ex[3], ex[4], indptr, seg_lora, tiles, seg_cap,
+                   large_cap, small_cap);
+  }
+  if (t == 0) {
+    if (!overflow) indptr[n_seg] = n_lora;
+    info[0] = overflow ? 0 : n_seg;
+    info[1] = overflow ? 0 : n_large;
+    info[2] = overflow ? 0 : n_small;
+    info[3] = overflow ? SGMV_ECAPACITY : (s_bad ? SGMV_EBADID : SGMV_OK);
+    s_base[L] = n_lora;
+  }
+  __syncthreads();
+  if (valid) {
+    const int pos = s_base[key] + rank;
+    if (pos < M) sorted[pos] = t;
+    if (key < L && !overflow)
+      token_slot(t, rank, cnt, C, s_sbase[key], tiles, large_cap, small_cap);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// larger batches: rounds of 1024 tokens
+// ---------------------------------------------------------------------------------------
+size_t build_lds_bytes(int L) {
+  const size_t nk = (size_t)L + 1;
+  return align16(nk * BUILD_WAVES) + 7 * align16((nk + 1) * sizeof(int));
 }
 
 // Group lanes of this wave holding equal keys. Returns the lane's rank among lanes with the
@@ -77,20 +263,6 @@ __device__ int match_rank(bool valid, int key, int t, uint8_t* rc, int* first, i
   return myrank;
 }
 
-// Counts of equal keys in lower waves (pre), in this wave (cw) and in higher waves (post).
-__device__ inline void wave_counts(const uint8_t* rc, int key, int& pre, int& cw, int& post) {
-  const int w = threadIdx.x / WAVE;
-  const u32x4_t q = *reinterpret_cast<const u32x4_t*>(rc + key * BUILD_WAVES);
-  pre = cw = post = 0;
-#pragma unroll
-  for (int i = 0; i < BUILD_WAVES; ++i) {
-    const int v = (q[i >> 2] >> (8 * (i & 3))) & 0xff;
-    if (i < w) pre += v;
-    else if (i == w) cw = v;
-    else post += v;
-  }
-}
-
 __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
     const int32_t* __restrict__ ids, int M, int L, int C, int32_t* __restrict__ sorted,
     int32_t* __restrict__ indptr, int32_t* __restrict__ seg_lora, int32_t* __restrict__ tiles,
@@ -100,12 +272,13 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
   uint8_t* rc = smem;
   int* run = reinterpret_cast<int*>(smem + align16((size_t)NK * BUILD_WAVES));
   const size_t stride = align16((size_t)(NK + 1) * sizeof(int)) / sizeof(int);
-  int* first = run + stride;
-  int* bidx = first + stride;
-  int* ord = bidx + stride;
-  int* bstart = ord + stride;
-  int* pstart = bstart + stride;
-  __shared__ int s_w[BUILD_WAVES + 1];
+  int* first = run + stride;      // first token of each adapter, then its first large piece
+  int* bidx = first + stride;     // bucket of each adapter
+  int* ord = bidx + stride;       // adapter of each bucket
+  int* bstart = ord + stride;     // first sorted row of each bucket
+  int* pstart = bstart + stride;  // first segment of each bucket
+  int* sbase = pstart + stride;   // first small descriptor of each bucket
+  __shared__ __align__(16) int s_w[4 * BUILD_WAVES];
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
@@ -154,112 +327,71 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
       const int id = ids[t];
       key = (id < 0 || id >= L) ? L : id;
     }
-    const int flag = (t < M && key < L && first[key] == t) ? 1 : 0;
-    int tot;
-    const int ex = block_exclusive_scan(flag, s_w, &tot);
-    if (flag) {
-      bidx[key] = n_buckets + ex;
-      ord[n_buckets + ex] = key;
+    const int v[1] = {(t < M && key < L && first[key] == t) ? 1 : 0};
+    int ex[1], tot[1];
+    block_scan<1>(v, ex, tot, s_w);
+    if (v[0]) {
+      bidx[key] = n_buckets + ex[0];
+      ord[n_buckets + ex[0]] = key;
     }
-    n_buckets += tot;
+    n_buckets += tot[0];
   }
   __syncthreads();
 
-  // ---- bucket starts and chunk counts ----
-  int n_lora = 0, n_seg = 0;
+  // ---- bucket starts, first segment and first descriptors of each bucket ----
+  int n_lora = 0, n_seg = 0, n_large = 0, n_small = 0;
   for (int b0 = 0; b0 < n_buckets; b0 += BUILD_THREADS) {
     const int b = b0 + tid;
-    const int sz = b < n_buckets ? run[ord[b]] : 0;
-    const int np = b < n_buckets ? (C > 0 ? (sz + C - 1) / C : 1) : 0;
-    int tot1, tot2;
-    const int e1 = block_exclusive_scan(sz, s_w, &tot1);
-    const int e2 = block_exclusive_scan(np, s_w, &tot2);
+    int v[4] = {0, 0, 0, 0};
     if (b < n_buckets) {
-      bstart[b] = n_lora + e1;
-      pstart[b] = n_seg + e2;
+      const int cnt = run[ord[b]];
+      const int np = C > 0 ? (cnt + C - 1) / C : 1;
+      const int last = C > 0 ? cnt - C * (np - 1) : cnt;
+      int nl, ns, nl1, ns1;
+      piece_tiles(C > 0 ? C : cnt, nl, ns);
+      piece_tiles(last, nl1, ns1);
+      v[0] = cnt;
+      v[1] = np;
+      v[2] = (np - 1) * nl + nl1;
+      v[3] = (np - 1) * ns + ns1;
     }
-    n_lora += tot1;
-    n_seg += tot2;
+    int ex[4], tot[4];
+    block_scan<4>(v, ex, tot, s_w);
+    if (b < n_buckets) {
+      bstart[b] = n_lora + ex[0];
+      pstart[b] = n_seg + ex[1];
+      first[ord[b]] = n_large + ex[2];  // first[] is free after the bucket order
+      sbase[b] = n_small + ex[3];
+    }
+    n_lora += tot[0];
+    n_seg += tot[1];
+    n_large += tot[2];
+    n_small += tot[3];
   }
   if (tid == 0) {
     bstart[n_buckets] = n_lora;
     pstart[n_buckets] = n_seg;
   }
-  const bool seg_overflow = n_seg > seg_cap;  // cannot happen with the stated capacities
-  if (seg_overflow) n_seg = 0;
+  const bool overflow = n_seg > seg_cap || n_large > large_cap || n_small > small_cap;
   __syncthreads();
-
-  // ---- segment arrays ----
-  for (int p = tid; p < n_seg; p += BUILD_THREADS) {
-    int lo = 0, hi = n_buckets - 1;  // last bucket b with pstart[b] <= p
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pstart[mid] <= p) lo = mid;
-      else hi = mid - 1;
+  if (!overflow) {
+    for (int b = tid; b < n_buckets; b += BUILD_THREADS) {
+      const int lora = ord[b];
+      write_bucket(lora, bstart[b + 1] - bstart[b], C, bstart[b], pstart[b], first[lora],
+                   sbase[b], indptr, seg_lora, tiles, seg_cap, large_cap, small_cap);
     }
-    const int i = p - pstart[lo];
-    indptr[p] = bstart[lo] + (C > 0 ? i * C : 0);
-    seg_lora[p] = ord[lo];
-  }
-  if (tid == 0) indptr[n_seg] = seg_overflow ? 0 : n_lora;
-
-  // ---- work descriptors ----
-  int n_large = 0, n_small = 0;
-  bool tile_overflow = false;
-  for (int p0 = 0; p0 < n_seg; p0 += BUILD_THREADS) {
-    const int p = p0 + tid;
-    int nl = 0, ns = 0, start = 0, len = 0, lora = 0;
-    if (p < n_seg) {
-      int lo = 0, hi = n_buckets - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pstart[mid] <= p) lo = mid;
-        else hi = mid - 1;
-      }
-      const int i = p - pstart[lo];
-      const int size = bstart[lo + 1] - bstart[lo];
-      start = bstart[lo] + (C > 0 ? i * C : 0);
-      len = C > 0 ? min(C, size - i * C) : size;
-      lora = ord[lo];
-      const int rem = len % SGMV_TILE_ROWS;
-      nl = len / SGMV_TILE_ROWS + (rem > SGMV_SMALL_ROWS ? 1 : 0);
-      ns = (rem > 0 && rem <= SGMV_SMALL_ROWS) ? 1 : 0;
-    }
-    int totl, tots;
-    const int el = block_exclusive_scan(nl, s_w, &totl);
-    const int es = block_exclusive_scan(ns, s_w, &tots);
-    if (n_large + totl > large_cap || n_small + tots > small_cap) {
-      tile_overflow = true;  // cannot happen with the stated capacities
-      break;
-    }
-    for (int i = 0; i < nl; ++i) {
-      int32_t* d = tiles + (size_t)(n_large + el + i) * 4;
-      d[0] = lora;
-      d[1] = start + i * SGMV_TILE_ROWS;
-      d[2] = min(SGMV_TILE_ROWS, len - i * SGMV_TILE_ROWS);
-      d[3] = p;
-    }
-    if (ns) {
-      int32_t* d = tiles + (size_t)(large_cap + n_small + es) * 4;
-      const int q = len / SGMV_TILE_ROWS;
-      d[0] = lora;
-      d[1] = start + q * SGMV_TILE_ROWS;
-      d[2] = len - q * SGMV_TILE_ROWS;
-      d[3] = p;
-    }
-    n_large += totl;
-    n_small += tots;
   }
   if (tid == 0) {
-    info[0] = n_seg;
-    info[1] = tile_overflow ? 0 : n_large;
-    info[2] = tile_overflow ? 0 : n_small;
-    info[3] = (seg_overflow || tile_overflow) ? SGMV_ECAPACITY : (s_bad ? SGMV_EBADID : SGMV_OK);
+    if (!overflow) indptr[n_seg] = n_lora;
+    info[0] = overflow ? 0 : n_seg;
+    info[1] = overflow ? 0 : n_large;
+    info[2] = overflow ? 0 : n_small;
+    info[3] = overflow ? SGMV_ECAPACITY : (s_bad ? SGMV_EBADID : SGMV_OK);
   }
 
   // ---- pass 2: stable scatter ----
-  for (int u = tid; u < L; u += BUILD_THREADS)
-    if (first[u] != INT_MAX) run[u] = bstart[bidx[u]];
+  __syncthreads();
+  for (int b = tid; b < n_buckets; b += BUILD_THREADS) run[ord[b]] = bstart[b];
   if (tid == 0) run[L] = n_lora;
   __syncthreads();
   for (int rd = 0; rd < rounds; ++rd) {
@@ -275,7 +407,13 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
     int pre = 0, cw = 0, post = 0;
     if (valid) {
       wave_counts(rc, key, pre, cw, post);
-      sorted[run[key] + pre + myrank] = t;
+      const int pos = run[key] + pre + myrank;
+      if (pos < M) sorted[pos] = t;
+      if (key < L && !overflow) {
+        const int b = bidx[key];
+        token_slot(t, pos - bstart[b], bstart[b + 1] - bstart[b], C, sbase[b], tiles, large_cap,
+                   small_cap);
+      }
     }
     __syncthreads();
     if (valid) {
@@ -289,9 +427,15 @@ hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_
                                  int32_t* indptr, int32_t* seg_lora, int32_t* tiles,
                                  int32_t* info, int seg_cap, int large_cap, int small_cap,
                                  hipStream_t stream) {
-  const size_t lds = build_lds_bytes(L);
-  hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(BUILD_THREADS), lds, stream, ids, M, L,
-                     C, sorted, indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap);
+  if (M <= BUILD_THREADS) {
+    hipLaunchKernelGGL(build_segments_small_kernel, dim3(1), dim3(BUILD_THREADS),
+                       build_small_lds_bytes(L), stream, ids, M, L, C, sorted, indptr, seg_lora,
+                       tiles, info, seg_cap, large_cap, small_cap);
+  } else {
+    hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(BUILD_THREADS), build_lds_bytes(L),
+                       stream, ids, M, L, C, sorted, indptr, seg_lora, tiles, info, seg_cap,
+                       large_cap, small_cap);
+  }
   return hipGetLastError();
 }
 

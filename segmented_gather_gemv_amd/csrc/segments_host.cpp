@@ -6,7 +6,9 @@
 // descriptors (start row, row count, adapter index) prepared once per step on the host.
 //
 // Buckets follow the order in which adapters first appear among the tokens; tokens ascend
-// inside a bucket; id -1 tokens form the tail. This is plain C++ with no HIP dependency.
+// inside a bucket; id -1 tokens form the tail. Work descriptors are the pieces of at most
+// SGMV_TILE_ROWS rows of each segment (compact descriptors: adapter, start row, row count),
+// small pieces carrying their token ids. This is plain C++ with no HIP dependency.
 #include "segments_host.h"
 
 #include <vector>
@@ -61,17 +63,20 @@ int host_build_segments(const int32_t* ids, int32_t M, int32_t L, int32_t C, int
     for (int32_t start = indptr[s]; start < end; start += SGMV_TILE_ROWS) {
       const int32_t rows = end - start < SGMV_TILE_ROWS ? end - start : SGMV_TILE_ROWS;
       int32_t* d;
-      if (rows <= SGMV_SMALL_ROWS) {
+      const bool small = rows <= SGMV_SMALL_ROWS;
+      if (small) {
         if (ns >= small_cap) return SGMV_ECAPACITY;
-        d = tiles + (size_t)(large_cap + ns++) * 4;
+        d = tiles + (size_t)(large_cap + ns++) * SGMV_TILE_INTS;
       } else {
         if (nl >= large_cap) return SGMV_ECAPACITY;
-        d = tiles + (size_t)(nl++) * 4;
+        d = tiles + (size_t)(nl++) * SGMV_TILE_INTS;
       }
       d[0] = seg_lora[s];
       d[1] = start;
       d[2] = rows;
       d[3] = s;
+      for (int i = 4; i < 16; ++i) d[i] = 0;
+      for (int i = 0; i < 16; ++i) d[16 + i] = (small && i < rows) ? sorted[start + i] : -1;
     }
   }
   info[0] = S;

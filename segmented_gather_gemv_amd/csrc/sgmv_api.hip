@@ -15,9 +15,8 @@ hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_
                                  hipStream_t stream);
 hipError_t launch_pool_pack(const void* a_user, const void* b_user, const sgmv_pool& p,
                             hipStream_t stream);
-hipError_t launch_delta_bf16(int mode, bool aligned, const DeltaArgs& A, int grid,
-                             hipStream_t stream);
-hipError_t launch_delta_f32(int mode, const DeltaArgs& A, int grid, hipStream_t stream);
+hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, hipStream_t stream);
+hipError_t launch_delta_f32(int mode, DeltaArgs A, hipStream_t stream);
 
 namespace {
 
@@ -93,10 +92,12 @@ void fill_common(const sgmv_pool* p, const sgmv_segments* seg, DeltaArgs& A) {
   A.K = p->K;
   A.K_pad = p->K_pad;
   A.N_pad = p->N_pad;
+  A.L = p->L;
   A.sorted = seg->sorted_token_ids;
   A.tiles = seg->tiles;
   A.info = seg->info;
   A.large_cap = seg->large_cap;
+  A.small_cap = seg->small_cap;
 }
 
 // Column splits per work descriptor: enough workgroups to cover the chip for decode-like
@@ -118,6 +119,11 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
   if (M < 0 || !pool_ok(pool)) return SGMV_EINVAL;
   if (pool->R_max > SGMV_MAX_RANK) return SGMV_EUNSUPPORTED;
   if (!seg_ok(seg, M, pool->L)) return SGMV_EINVAL;
+  if (M == 0) {  // no-op; empty buffers may have null addresses
+    if (mode != MODE_SHRINK && (!out || n_slices < 1 || n_slices > SGMV_MAX_SLICES))
+      return SGMV_EINVAL;
+    return SGMV_OK;
+  }
   DeltaArgs A;
   std::memset(&A, 0, sizeof(A));
   bool aligned = true;
@@ -144,22 +150,15 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
     A.n_slices = 0;
     A.v_total = 0;
   }
-  if (M == 0) return SGMV_OK;
   fill_common(pool, seg, A);
-  int grid;
   if (mode == MODE_SHRINK) {
     A.n_split_large = A.n_split_small = 1;
-    grid = seg->large_cap + seg->small_cap;
   } else {
     choose_splits(A.v_total, A);
-    grid = seg->large_cap * A.n_split_large + seg->small_cap * A.n_split_small;
   }
-  // the kernels place work item u on workgroup 8 * (u % per) + u / per with per =
-  // ceil(work / 8), so the grid must be a multiple of 8 covering every work item
-  grid = (int)round_up(grid, 8);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, grid, s));
-  return hip_status(launch_delta_f32(mode, A, grid, s));
+  if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, s));
+  return hip_status(launch_delta_f32(mode, A, s));
 }
 
 }  // namespace

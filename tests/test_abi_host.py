@@ -65,10 +65,25 @@ def assert_same_as_oracle(ids, L, C):
     assert np.array_equal(got["seg_indptr"].numpy(), ref["seg_indptr"])
     assert np.array_equal(got["seg_lora_ids"].numpy(), ref["seg_lora_ids"])
     assert got["num_segments"] == ref["num_segments"]
-    lg, sm = oracle.tiles(ref["seg_indptr"], ref["seg_lora_ids"], sg.TILE_ROWS, sg.SMALL_ROWS)
-    assert np.array_equal(got["large_tiles"].numpy().reshape(-1, 4), lg)
-    assert np.array_equal(got["small_tiles"].numpy().reshape(-1, 4), sm)
+    check_records(got, ref)
     assert got["status"] == sg.SGMV_OK
+
+
+def check_records(got, ref):
+    """Descriptor records: header fields equal the oracle's pieces, [4..16) zero, token slots
+    of a small piece hold its sorted token ids then -1, those of a large piece all -1."""
+    lg, sm = oracle.tiles(ref["seg_indptr"], ref["seg_lora_ids"], sg.TILE_ROWS, sg.SMALL_ROWS)
+    st = np.asarray(ref["sorted_token_ids"])
+    for recs, want, small in ((got["large_tiles"], lg, False), (got["small_tiles"], sm, True)):
+        recs = recs.numpy().reshape(-1, sg.TILE_INTS)
+        assert np.array_equal(recs[:, :4], want)
+        assert np.all(recs[:, 4:16] == 0)
+        for rec in recs:
+            start, rows = int(rec[1]), int(rec[2])
+            toks = np.full(16, -1)
+            if small:
+                toks[:rows] = st[start:start + rows]
+            assert np.array_equal(rec[16:], toks)
 
 
 def test_host_builder_worked_example():

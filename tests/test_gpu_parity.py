@@ -128,6 +128,14 @@ def builder_cases():
         ("neg_mix_c1", rng.integers(-1, 5, 1500), 5, 1),
         ("ragged", rng.integers(-1, 300, 5001), 300, 64),
         ("big_L", rng.integers(-1, 1024, 9000), 1024, 0),
+        # one-round fast path (M <= 1024)
+        ("fast_full_one_key", np.full(1024, 3), 4, 0),
+        ("fast_full_c1", rng.integers(-1, 7, 1024), 7, 1),
+        ("fast_1000_c16", rng.integers(-1, 40, 1000), 40, 16),
+        ("fast_1025", rng.integers(-1, 40, 1025), 40, 0),
+        ("fast_all_distinct", rng.permutation(1024), 1024, 0),
+        ("fast_runs_c64", np.repeat(rng.integers(0, 9, 12), rng.integers(1, 90, 12)), 9, 64),
+        ("fast_pool_1024", rng.integers(-1, 1024, 700), 1024, 5),
     ]
     for name in ("decode", "prefill", "mixed", "qkv"):
         w = workloads.get(name)
@@ -149,6 +157,8 @@ def test_device_builder_bit_exact(sg, case):
         assert torch.equal(dev[k][:M] if k == "sorted_token_ids" else dev[k],
                            host[k][:M] if k == "sorted_token_ids" else host[k]), k
     assert dev["num_segments"] == host["num_segments"] == ref["num_segments"]
+    from test_abi_host import check_records
+    check_records(dev, ref)
 
 
 def test_device_builder_bad_ids_flagged(sg):
