@@ -13,9 +13,10 @@ copies of every buffer (pool, x, y, ids, segment arrays) whose total size is abo
 cache.
 
 Timing: W untimed warm-up steps, then K steps between two device synchronisations
-(ms_per_step, value = tokens with an adapter per second). Inside the same timed region HIP
-events on the launch stream bracket every launch of the segment builder and of the delta
-kernel; their averages give the per-launch durations used for the roofline. The roofline
+(ms_per_step, value = tokens with an adapter per second). Inside the same timed region every
+launch of the segment builder and of the delta kernel records a pair of HIP events as part
+of its own dispatch on the launch stream (start and end of the kernel, no extra stream
+packets); their averages give the per-launch durations used for the roofline. The roofline
 figure divides the algorithmic bytes of one delta launch (x rows and y rows read and written
 for every token with an adapter, each used adapter's true-rank A and B once, 12 bytes of
 index per token) by that duration, against the 8 TB/s HBM peak.
@@ -143,6 +144,10 @@ def main():
                     help="independent buffer copies cycled by the steps (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-small", type=int, default=0,
+                    help="column splits per small piece (0: library choice)")
+    ap.add_argument("--split-large", type=int, default=0,
+                    help="column splits per large piece (0: library choice)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -186,26 +191,27 @@ def main():
     torch.cuda.synchronize()
 
     s_handle = ctypes.c_void_p(stream.cuda_stream)
-    build_fn, delta_fn = lib.sgmv_build_segments, lib.sgmv_lora_delta
+    build_fn, delta_fn = lib.sgmv_build_segments_ex, lib.sgmv_lora_delta_ex
+    K = args.steps
+    # per timed step: events the kernels' own dispatches record (start, end) -- no extra
+    # packets in the stream
+    evs = [ev.create(4) for _ in range(K)]
+    plain = sg.LaunchOpts(n_split_small=args.split_small, n_split_large=args.split_large)
+    opts_b = [sg.LaunchOpts(e[0], e[1]) for e in evs]
+    opts_d = [sg.LaunchOpts(e[2], e[3], args.split_small, args.split_large) for e in evs]
     calls = []
     for st in sets:
         bargs = (ctypes.c_void_p(st["ids"].data_ptr()), w.M, w.L, w.chunk_size, 1,
-                 ctypes.byref(st["seg"].desc), s_handle)
+                 ctypes.byref(st["seg"].desc))
         dargs = (ctypes.c_void_p(st["x"].data_ptr()), st["x"].stride(0), w.M,
                  ctypes.byref(st["pool"].desc), ctypes.byref(st["seg"].desc), st["sl"],
-                 st["n_sl"], s_handle)
+                 st["n_sl"])
         calls.append((bargs, dargs))
 
-    def step(i, e=None):
+    def step(i, timed=False):
         bargs, dargs = calls[i % n_sets]
-        if e is not None:
-            ev.lib.hipEventRecord(e[0], s_handle)
-        rc = build_fn(*bargs)
-        if e is not None:
-            ev.lib.hipEventRecord(e[1], s_handle)
-        rc |= delta_fn(*dargs)
-        if e is not None:
-            ev.lib.hipEventRecord(e[2], s_handle)
+        rc = build_fn(*bargs, opts_b[i].ref() if timed else None, s_handle)
+        rc |= delta_fn(*dargs, opts_d[i].ref() if timed else plain.ref(), s_handle)
         return rc
 
     rc = 0
@@ -216,17 +222,15 @@ def main():
     for st in sets:
         assert int(st["seg"].info[3].item()) == sg.SGMV_OK
 
-    K = args.steps
-    evs = [ev.create(3) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        rc |= step(i, evs[i])
+        rc |= step(i, timed=True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     assert rc == 0, f"library call failed with status {rc}"
     build_ms = [ev.elapsed_ms(e[0], e[1]) for e in evs]
-    delta_ms = [ev.elapsed_ms(e[1], e[2]) for e in evs]
+    delta_ms = [ev.elapsed_ms(e[2], e[3]) for e in evs]
     for e in evs:
         ev.destroy(e)
 

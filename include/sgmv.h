@@ -198,6 +198,38 @@ sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_po
                             const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
                             void* stream);
 
+/* ------------------------------------------------------------------------------------ *
+ * Launch options (optional; NULL means library defaults). Shared by the _ex variants below,
+ * which behave exactly like the calls without the suffix otherwise.
+ *   start_event, stop_event: hipEvent_t (as void*) or NULL. When given, the kernel's own
+ *     dispatch records them as it starts and as it ends (no extra stream packets), so
+ *     hipEventElapsedTime(start, stop) is the kernel's execution time. The caller creates,
+ *     owns and destroys them.
+ *   n_split_small, n_split_large: workgroups across the output columns for each small /
+ *     large work descriptor in expand and fused calls; 0 = the library's choice, else 1..64.
+ * Errors: EINVAL (a split outside 0..64).
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  void* start_event;
+  void* stop_event;
+  int32_t n_split_small;
+  int32_t n_split_large;
+} sgmv_launch_opts;
+
+sgmv_status sgmv_build_segments_ex(const int32_t* lora_indices, int32_t M, int32_t L,
+                                   int32_t chunk_size, int32_t on_device,
+                                   const sgmv_segments* seg, const sgmv_launch_opts* opts,
+                                   void* stream);
+sgmv_status sgmv_shrink_ex(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
+                           const sgmv_segments* seg, float* h, int64_t ldh,
+                           const sgmv_launch_opts* opts, void* stream);
+sgmv_status sgmv_expand_ex(const float* h, int64_t ldh, int32_t M, const sgmv_pool* pool,
+                           const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
+                           const sgmv_launch_opts* opts, void* stream);
+sgmv_status sgmv_lora_delta_ex(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
+                               const sgmv_segments* seg, const sgmv_slice* out,
+                               int32_t n_slices, const sgmv_launch_opts* opts, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* sgmv_status_string(sgmv_status s);
 

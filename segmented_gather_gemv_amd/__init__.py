@@ -36,7 +36,9 @@ DEVICE_BUILDER_MAX_L = 1024
 
 EXPORTED = [
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
-    "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_status_string", "sgmv_version",
+    "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
+    "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_status_string",
+    "sgmv_version",
 ]
 
 
@@ -61,6 +63,27 @@ class _Segments(ctypes.Structure):
                 ("large_cap", ctypes.c_int32), ("small_cap", ctypes.c_int32)]
 
 
+class _LaunchOpts(ctypes.Structure):
+    _fields_ = [("start_event", ctypes.c_void_p), ("stop_event", ctypes.c_void_p),
+                ("n_split_small", ctypes.c_int32), ("n_split_large", ctypes.c_int32)]
+
+
+class LaunchOpts:
+    """Optional launch settings: HIP events (raw hipEvent_t handles) that the kernel's own
+    dispatch records at its start and end, and column-split overrides (0 = library's
+    choice)."""
+
+    def __init__(self, start_event=None, stop_event=None, n_split_small=0, n_split_large=0):
+        self.c = _LaunchOpts(start_event, stop_event, int(n_split_small), int(n_split_large))
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _opts(opts):
+    return None if opts is None else opts.ref()
+
+
 class _Slice(ctypes.Structure):
     _fields_ = [("y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("n_begin", ctypes.c_int32),
                 ("n_len", ctypes.c_int32)]
@@ -80,8 +103,15 @@ def _load():
     lib.sgmv_shrink.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), vp, i64, vp]
     lib.sgmv_expand.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, vp]
     lib.sgmv_lora_delta.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, vp]
+    O = P(_LaunchOpts)
+    lib.sgmv_build_segments_ex.argtypes = [vp, i32, i32, i32, i32, P(_Segments), O, vp]
+    lib.sgmv_shrink_ex.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), vp, i64, O, vp]
+    lib.sgmv_expand_ex.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, O, vp]
+    lib.sgmv_lora_delta_ex.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, O,
+                                       vp]
     for f in ["sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
-              "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta"]:
+              "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
+              "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.sgmv_status_string.argtypes = [ctypes.c_int]
     lib.sgmv_status_string.restype = ctypes.c_char_p
@@ -254,7 +284,8 @@ def sgmv_segments_alloc(M: int, L: int, chunk_size: int = 0,
 
 
 def sgmv_build_segments(ids: torch.Tensor, L: int, chunk_size: int = 0, on_device: bool = True,
-                        out: Optional[Segments] = None) -> Segments:
+                        out: Optional[Segments] = None,
+                        opts: Optional[LaunchOpts] = None) -> Segments:
     """Group tokens by adapter (id -1: no adapter). ``on_device`` runs the GPU builder on the
     current stream without a host sync (ids must be a device tensor); otherwise the host
     builder runs on CPU tensors and raises on a bad id."""
@@ -266,8 +297,9 @@ def sgmv_build_segments(ids: torch.Tensor, L: int, chunk_size: int = 0, on_devic
     if not on_device and dev.type != "cpu":
         raise ValueError("on_device=False needs ids on the CPU")
     seg = out if out is not None else sgmv_segments_alloc(M, L, chunk_size, dev)
-    _check(_lib.sgmv_build_segments(_ptr(ids), M, L, chunk_size, 1 if on_device else 0,
-                                    ctypes.byref(seg.desc), _stream(dev)), "sgmv_build_segments")
+    _check(_lib.sgmv_build_segments_ex(_ptr(ids), M, L, chunk_size, 1 if on_device else 0,
+                                       ctypes.byref(seg.desc), _opts(opts), _stream(dev)),
+           "sgmv_build_segments")
     return seg
 
 
@@ -305,7 +337,8 @@ def _check_x(x: torch.Tensor, pool: Pool):
 
 
 def sgmv_shrink(x: torch.Tensor, pool: Pool, seg: Segments,
-                h: Optional[torch.Tensor] = None) -> torch.Tensor:
+                h: Optional[torch.Tensor] = None,
+                opts: Optional[LaunchOpts] = None) -> torch.Tensor:
     """h[t, :r] = A[l, :r, :] @ x[t] for tokens with an adapter (fp32, unscaled)."""
     _check_x(x, pool)
     M = x.shape[0]
@@ -313,37 +346,40 @@ def sgmv_shrink(x: torch.Tensor, pool: Pool, seg: Segments,
         h = torch.zeros(M, pool.R_max, dtype=torch.float32, device=x.device)
     if h.dtype != torch.float32 or h.stride(1) != 1:
         raise TypeError("h must be a row-major fp32 tensor")
-    _check(_lib.sgmv_shrink(_ptr(x), x.stride(0), M, ctypes.byref(pool.desc),
-                            ctypes.byref(seg.desc), _ptr(h), h.stride(0), _stream(x.device)),
-           "sgmv_shrink")
+    _check(_lib.sgmv_shrink_ex(_ptr(x), x.stride(0), M, ctypes.byref(pool.desc),
+                               ctypes.byref(seg.desc), _ptr(h), h.stride(0), _opts(opts),
+                               _stream(x.device)), "sgmv_shrink")
     return h
 
 
 def sgmv_expand(h: torch.Tensor, pool: Pool, seg: Segments,
-                y: Union[torch.Tensor, Sequence[SliceSpec]]) -> None:
+                y: Union[torch.Tensor, Sequence[SliceSpec]],
+                opts: Optional[LaunchOpts] = None) -> None:
     """y[t] += scale_l * B[l, :, :r] @ h[t, :r] (in place; list of (y, first column) for
     several output slices)."""
     if h.dtype != torch.float32 or h.stride(1) != 1:
         raise TypeError("h must be a row-major fp32 tensor")
     M = h.shape[0]
     arr, n = _slices(y, pool, M)
-    _check(_lib.sgmv_expand(_ptr(h), h.stride(0), M, ctypes.byref(pool.desc),
-                            ctypes.byref(seg.desc), arr, n, _stream(h.device)), "sgmv_expand")
+    _check(_lib.sgmv_expand_ex(_ptr(h), h.stride(0), M, ctypes.byref(pool.desc),
+                               ctypes.byref(seg.desc), arr, n, _opts(opts), _stream(h.device)),
+           "sgmv_expand")
 
 
 def sgmv_lora_delta(x: torch.Tensor, pool: Pool, seg: Segments,
-                    y: Union[torch.Tensor, Sequence[SliceSpec]]) -> None:
+                    y: Union[torch.Tensor, Sequence[SliceSpec]],
+                    opts: Optional[LaunchOpts] = None) -> None:
     """Fused y[t] += scale_l * B[l, :, :r] @ (A[l, :r, :] @ x[t]) (in place)."""
     _check_x(x, pool)
     M = x.shape[0]
     arr, n = _slices(y, pool, M)
-    _check(_lib.sgmv_lora_delta(_ptr(x), x.stride(0), M, ctypes.byref(pool.desc),
-                                ctypes.byref(seg.desc), arr, n, _stream(x.device)),
-           "sgmv_lora_delta")
+    _check(_lib.sgmv_lora_delta_ex(_ptr(x), x.stride(0), M, ctypes.byref(pool.desc),
+                                   ctypes.byref(seg.desc), arr, n, _opts(opts),
+                                   _stream(x.device)), "sgmv_lora_delta")
 
 
 __all__ = [
-    "LIB_PATH", "EXPORTED", "SgmvError", "Pool", "Segments", "library",
+    "LIB_PATH", "EXPORTED", "SgmvError", "Pool", "Segments", "LaunchOpts", "library",
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_alloc", "sgmv_build_segments",
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta",
 ]

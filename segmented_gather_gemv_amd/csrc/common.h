@@ -1,6 +1,7 @@
 // Shared device definitions for the libsgmv HIP kernels (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,6 +71,11 @@ struct DeltaArgs {
 };
 
 enum Mode { MODE_FUSED = 0, MODE_SHRINK = 1, MODE_EXPAND = 2 };
+
+// Optional events recorded by a kernel's own dispatch (start and end of execution).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
 
 // Piece and column split of this workgroup, from its index alone. Workgroups
 // [0, grid_large) take large pieces, the rest small ones; within a class, piece i runs on

@@ -518,7 +518,8 @@ __global__ __launch_bounds__(DT_THREADS) void delta_bf16_kernel(DeltaArgs A) {
   }
 }
 
-hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, hipStream_t stream) {
+hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, LaunchEvents ev,
+                             hipStream_t stream) {
   const bool split = mode != MODE_SHRINK;
   A.grid_large = class_grid(A.large_cap, split ? A.n_split_large : 1);
   const int grid = A.grid_large + class_grid(A.small_cap, split ? A.n_split_small : 1);
@@ -526,7 +527,8 @@ hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, hipStream_t st
   const dim3 g(grid), b(DT_THREADS);
   // partial tiles of every wave; at least 16 KB, which also holds the h fragments
   const size_t lds = (size_t)DT_WAVES * (A.R_pad / 16) * 256 * sizeof(float);
-#define SGMV_LAUNCH(M_, AL_) hipLaunchKernelGGL((delta_bf16_kernel<M_, AL_>), g, b, lds, stream, A)
+#define SGMV_LAUNCH(M_, AL_) \
+  hipExtLaunchKernelGGL((delta_bf16_kernel<M_, AL_>), g, b, lds, stream, ev.start, ev.stop, 0, A)
   if (mode == MODE_FUSED) {
     if (aligned) SGMV_LAUNCH(MODE_FUSED, true); else SGMV_LAUNCH(MODE_FUSED, false);
   } else if (mode == MODE_SHRINK) {

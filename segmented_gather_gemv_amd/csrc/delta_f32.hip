@@ -102,18 +102,18 @@ __global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
   }
 }
 
-hipError_t launch_delta_f32(int mode, DeltaArgs A, hipStream_t stream) {
+hipError_t launch_delta_f32(int mode, DeltaArgs A, LaunchEvents ev, hipStream_t stream) {
   const bool split = mode != MODE_SHRINK;
   A.grid_large = class_grid(A.large_cap, split ? A.n_split_large : 1);
   const int grid = A.grid_large + class_grid(A.small_cap, split ? A.n_split_small : 1);
   if (grid <= 0) return hipSuccess;
   const dim3 g(grid), b(F_THREADS);
   if (mode == MODE_FUSED)
-    hipLaunchKernelGGL(delta_f32_kernel<MODE_FUSED>, g, b, 0, stream, A);
+    hipExtLaunchKernelGGL(delta_f32_kernel<MODE_FUSED>, g, b, 0, stream, ev.start, ev.stop, 0, A);
   else if (mode == MODE_SHRINK)
-    hipLaunchKernelGGL(delta_f32_kernel<MODE_SHRINK>, g, b, 0, stream, A);
+    hipExtLaunchKernelGGL(delta_f32_kernel<MODE_SHRINK>, g, b, 0, stream, ev.start, ev.stop, 0, A);
   else
-    hipLaunchKernelGGL(delta_f32_kernel<MODE_EXPAND>, g, b, 0, stream, A);
+    hipExtLaunchKernelGGL(delta_f32_kernel<MODE_EXPAND>, g, b, 0, stream, ev.start, ev.stop, 0, A);
   return hipGetLastError();
 }
 

@@ -426,15 +426,15 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
 hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_t* sorted,
                                  int32_t* indptr, int32_t* seg_lora, int32_t* tiles,
                                  int32_t* info, int seg_cap, int large_cap, int small_cap,
-                                 hipStream_t stream) {
+                                 LaunchEvents ev, hipStream_t stream) {
   if (M <= BUILD_THREADS) {
-    hipLaunchKernelGGL(build_segments_small_kernel, dim3(1), dim3(BUILD_THREADS),
-                       build_small_lds_bytes(L), stream, ids, M, L, C, sorted, indptr, seg_lora,
-                       tiles, info, seg_cap, large_cap, small_cap);
+    hipExtLaunchKernelGGL(build_segments_small_kernel, dim3(1), dim3(BUILD_THREADS),
+                          build_small_lds_bytes(L), stream, ev.start, ev.stop, 0, ids, M, L, C,
+                          sorted, indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap);
   } else {
-    hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(BUILD_THREADS), build_lds_bytes(L),
-                       stream, ids, M, L, C, sorted, indptr, seg_lora, tiles, info, seg_cap,
-                       large_cap, small_cap);
+    hipExtLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(BUILD_THREADS),
+                          build_lds_bytes(L), stream, ev.start, ev.stop, 0, ids, M, L, C, sorted,
+                          indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap);
   }
   return hipGetLastError();
 }

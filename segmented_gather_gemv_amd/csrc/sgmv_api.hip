@@ -1,7 +1,6 @@
 // libsgmv C-ABI: argument validation, launch geometry and dispatch. Stateless; every call
 // runs on the caller's stream. Declarations and contracts are in include/sgmv.h.
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
 
 #include "common.h"
@@ -12,22 +11,16 @@ size_t build_lds_bytes(int L);
 hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_t* sorted,
                                  int32_t* indptr, int32_t* seg_lora, int32_t* tiles,
                                  int32_t* info, int seg_cap, int large_cap, int small_cap,
-                                 hipStream_t stream);
+                                 LaunchEvents ev, hipStream_t stream);
 hipError_t launch_pool_pack(const void* a_user, const void* b_user, const sgmv_pool& p,
                             hipStream_t stream);
-hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, hipStream_t stream);
-hipError_t launch_delta_f32(int mode, DeltaArgs A, hipStream_t stream);
+hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, LaunchEvents ev,
+                             hipStream_t stream);
+hipError_t launch_delta_f32(int mode, DeltaArgs A, LaunchEvents ev, hipStream_t stream);
 
 namespace {
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
-
-int env_int(const char* name, int fallback) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return fallback;
-  const int v = std::atoi(s);
-  return v > 0 ? v : fallback;
-}
 
 bool pool_ok(const sgmv_pool* p) {
   if (!p || !p->a || !p->b || !p->rank || !p->scale) return false;
@@ -101,22 +94,38 @@ void fill_common(const sgmv_pool* p, const sgmv_segments* seg, DeltaArgs& A) {
 }
 
 // Column splits per work descriptor: enough workgroups to cover the chip for decode-like
-// pieces, few enough that x rows and A are not re-read too often for prefill-like ones.
-void choose_splits(int v_total, DeltaArgs& A) {
+// pieces, few enough that x rows and A are not re-read too often for prefill-like ones
+// (every split of a piece recomputes its shrink). Caller overrides win.
+void choose_splits(int v_total, const sgmv_launch_opts* opts, DeltaArgs& A) {
   int ps = v_total / 1024;
   int pl = v_total / 2048;
   ps = ps < 1 ? 1 : (ps > 16 ? 16 : ps);
   pl = pl < 1 ? 1 : (pl > 16 ? 16 : pl);
-  A.n_split_small = env_int("SGMV_NSPLIT_SMALL", ps);
-  A.n_split_large = env_int("SGMV_NSPLIT_LARGE", pl);
+  A.n_split_small = (opts && opts->n_split_small > 0) ? opts->n_split_small : ps;
+  A.n_split_large = (opts && opts->n_split_large > 0) ? opts->n_split_large : pl;
+}
+
+bool opts_ok(const sgmv_launch_opts* o) {
+  return !o || (o->n_split_small >= 0 && o->n_split_small <= 64 && o->n_split_large >= 0 &&
+                o->n_split_large <= 64);
+}
+
+LaunchEvents events_of(const sgmv_launch_opts* o) {
+  LaunchEvents e;
+  if (o) {
+    e.start = static_cast<hipEvent_t>(o->start_event);
+    e.stop = static_cast<hipEvent_t>(o->stop_event);
+  }
+  return e;
 }
 
 sgmv_status hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_EHIP; }
 
 sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, float* h_out,
                       int64_t ldh, int32_t M, const sgmv_pool* pool, const sgmv_segments* seg,
-                      const sgmv_slice* out, int32_t n_slices, void* stream) {
-  if (M < 0 || !pool_ok(pool)) return SGMV_EINVAL;
+                      const sgmv_slice* out, int32_t n_slices, const sgmv_launch_opts* opts,
+                      void* stream) {
+  if (M < 0 || !pool_ok(pool) || !opts_ok(opts)) return SGMV_EINVAL;
   if (pool->R_max > SGMV_MAX_RANK) return SGMV_EUNSUPPORTED;
   if (!seg_ok(seg, M, pool->L)) return SGMV_EINVAL;
   if (M == 0) {  // no-op; empty buffers may have null addresses
@@ -154,11 +163,12 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
   if (mode == MODE_SHRINK) {
     A.n_split_large = A.n_split_small = 1;
   } else {
-    choose_splits(A.v_total, A);
+    choose_splits(A.v_total, opts, A);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, s));
-  return hip_status(launch_delta_f32(mode, A, s));
+  const LaunchEvents ev = events_of(opts);
+  if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, ev, s));
+  return hip_status(launch_delta_f32(mode, A, ev, s));
 }
 
 }  // namespace
@@ -235,11 +245,13 @@ sgmv_status sgmv_segments_init(int32_t M, int32_t L, int32_t chunk_size, sgmv_se
   return SGMV_OK;
 }
 
-sgmv_status sgmv_build_segments(const int32_t* lora_indices, int32_t M, int32_t L,
-                                int32_t chunk_size, int32_t on_device, const sgmv_segments* seg,
-                                void* stream) {
+sgmv_status sgmv_build_segments_ex(const int32_t* lora_indices, int32_t M, int32_t L,
+                                   int32_t chunk_size, int32_t on_device,
+                                   const sgmv_segments* seg, const sgmv_launch_opts* opts,
+                                   void* stream) {
   if (M < 0 || L < 1 || chunk_size < 0 || (M > 0 && !lora_indices)) return SGMV_EINVAL;
   if (!seg || seg->chunk_size != chunk_size || !seg_ok(seg, M, L)) return SGMV_EINVAL;
+  if (!opts_ok(opts)) return SGMV_EINVAL;
   if (on_device == 0) {
     return (sgmv_status)host_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
                                             seg->seg_indptr, seg->seg_lora_ids, seg->tiles,
@@ -250,24 +262,50 @@ sgmv_status sgmv_build_segments(const int32_t* lora_indices, int32_t M, int32_t 
   return hip_status(launch_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
                                           seg->seg_indptr, seg->seg_lora_ids, seg->tiles,
                                           seg->info, seg->seg_cap, seg->large_cap, seg->small_cap,
-                                          static_cast<hipStream_t>(stream)));
+                                          events_of(opts), static_cast<hipStream_t>(stream)));
+}
+
+sgmv_status sgmv_build_segments(const int32_t* lora_indices, int32_t M, int32_t L,
+                                int32_t chunk_size, int32_t on_device, const sgmv_segments* seg,
+                                void* stream) {
+  return sgmv_build_segments_ex(lora_indices, M, L, chunk_size, on_device, seg, nullptr, stream);
+}
+
+sgmv_status sgmv_shrink_ex(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
+                           const sgmv_segments* seg, float* h, int64_t ldh,
+                           const sgmv_launch_opts* opts, void* stream) {
+  return run_delta(MODE_SHRINK, x, ldx, nullptr, h, ldh, M, pool, seg, nullptr, 0, opts, stream);
 }
 
 sgmv_status sgmv_shrink(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
                         const sgmv_segments* seg, float* h, int64_t ldh, void* stream) {
-  return run_delta(MODE_SHRINK, x, ldx, nullptr, h, ldh, M, pool, seg, nullptr, 0, stream);
+  return sgmv_shrink_ex(x, ldx, M, pool, seg, h, ldh, nullptr, stream);
+}
+
+sgmv_status sgmv_expand_ex(const float* h, int64_t ldh, int32_t M, const sgmv_pool* pool,
+                           const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
+                           const sgmv_launch_opts* opts, void* stream) {
+  return run_delta(MODE_EXPAND, nullptr, 0, h, nullptr, ldh, M, pool, seg, out, n_slices, opts,
+                   stream);
 }
 
 sgmv_status sgmv_expand(const float* h, int64_t ldh, int32_t M, const sgmv_pool* pool,
                         const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
                         void* stream) {
-  return run_delta(MODE_EXPAND, nullptr, 0, h, nullptr, ldh, M, pool, seg, out, n_slices, stream);
+  return sgmv_expand_ex(h, ldh, M, pool, seg, out, n_slices, nullptr, stream);
+}
+
+sgmv_status sgmv_lora_delta_ex(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
+                               const sgmv_segments* seg, const sgmv_slice* out,
+                               int32_t n_slices, const sgmv_launch_opts* opts, void* stream) {
+  return run_delta(MODE_FUSED, x, ldx, nullptr, nullptr, 0, M, pool, seg, out, n_slices, opts,
+                   stream);
 }
 
 sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
                             const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
                             void* stream) {
-  return run_delta(MODE_FUSED, x, ldx, nullptr, nullptr, 0, M, pool, seg, out, n_slices, stream);
+  return sgmv_lora_delta_ex(x, ldx, M, pool, seg, out, n_slices, nullptr, stream);
 }
 
 }  // extern "C"
