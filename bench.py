@@ -14,9 +14,10 @@ cache.
 
 Timing: W untimed warm-up steps, then K steps between two device synchronisations
 (ms_per_step, value = tokens with an adapter per second). Inside the same timed region every
-launch of the segment builder and of the delta kernel records a pair of HIP events as part
-of its own dispatch on the launch stream (start and end of the kernel, no extra stream
-packets); their averages give the per-launch durations used for the roofline. The roofline
+eighth step's launches of the segment builder and of the delta kernel record a pair of HIP
+events as part of their own dispatch on the launch stream (start and end of the kernel, no
+extra stream packets); their averages give the per-launch durations used for the roofline.
+Events on every launch would slow the host's launch path and lengthen the step. The roofline
 figure divides the algorithmic bytes of one delta launch (x rows and y rows read and written
 for every token with an adapter, each used adapter's true-rank A and B once, 12 bytes of
 index per token) by that duration, against the 8 TB/s HBM peak.
@@ -100,6 +101,62 @@ def load_traffic(workload: str, launches_units: int):
     return d.get("hbm_bytes_per_launch")
 
 
+def _counter_per_dispatch(csv_path: str, counter: str, name_part: str):
+    """Mean of a rocprofv3 --pmc counter over the dispatches of one kernel: among kernel names
+    containing name_part, the one dispatched most often (counter_collection.csv has one row
+    per dispatch and counter)."""
+    import csv
+    by_name = {}
+    for row in csv.DictReader(open(csv_path)):
+        if row.get("Counter_Name") == counter and name_part in row.get("Kernel_Name", ""):
+            by_name.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    if not by_name:
+        raise SystemExit(f"no {counter} rows for kernels matching '{name_part}' in {csv_path}")
+    vals = max(by_name.values(), key=len)
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(args):
+    """Turn four rocprofv3 counter CSVs (delta FETCH_SIZE, delta WRITE_SIZE, copy FETCH_SIZE,
+    copy WRITE_SIZE) into profiles/sgmv_lora_delta_<workload>_traffic.json. The counters read
+    KiB per dispatch; each is scaled by bytes-moved / counter-reading of a plain device copy
+    of known size measured the same way."""
+    d_fetch, d_wr, c_fetch, c_wr = args.write_traffic
+    copy_bytes = args.copy_mib * 2 ** 20
+    f_kib, n1 = _counter_per_dispatch(d_fetch, "FETCH_SIZE", "delta_bf16_kernel")
+    w_kib, n2 = _counter_per_dispatch(d_wr, "WRITE_SIZE", "delta_bf16_kernel")
+    cf_kib, _ = _counter_per_dispatch(c_fetch, "FETCH_SIZE", "elementwise")
+    cw_kib, _ = _counter_per_dispatch(c_wr, "WRITE_SIZE", "elementwise")
+    f_scale = copy_bytes / cf_kib
+    w_scale = copy_bytes / cw_kib
+    out = {
+        "workload": args.workload,
+        "kernel": "delta_bf16_kernel<fused, aligned>",
+        "kernel_sha": kernel_source_sha(),
+        "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+        "dispatches": [n1, n2],
+        "copy_bytes": copy_bytes, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+        "fetch_bytes_per_kib": f_scale, "write_bytes_per_kib": w_scale,
+        "hbm_bytes_per_launch": f_kib * f_scale + w_kib * w_scale,
+    }
+    path = os.path.join(PROFILES, f"sgmv_lora_delta_{args.workload}_traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out))
+
+
+def calibration_copy(args):
+    """A plain device copy of known size (the scale reference for the byte counters)."""
+    import torch
+    n = args.copy_mib * 2 ** 20 // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(8):  # elementwise kernel: reads a, writes b, copy_mib MiB each way
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    log(f"elementwise copy of {args.copy_mib} MiB, 8 times")
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle as it stands, on the same batch, repeated for about `seconds`."""
     import numpy as np
@@ -144,11 +201,24 @@ def main():
                     help="independent buffer copies cycled by the steps (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="timed steps between launches that carry timing events")
     ap.add_argument("--split-small", type=int, default=0,
                     help="column splits per small piece (0: library choice)")
     ap.add_argument("--split-large", type=int, default=0,
                     help="column splits per large piece (0: library choice)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="only run a plain device copy of --copy-mib MiB (counter scale)")
+    ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
+                    help="delta FETCH, delta WRITE, copy FETCH, copy WRITE counter CSVs")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args)
+        return
+    if args.calibration_copy:
+        calibration_copy(args)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -195,10 +265,13 @@ def main():
     K = args.steps
     # per timed step: events the kernels' own dispatches record (start, end) -- no extra
     # packets in the stream
-    evs = [ev.create(4) for _ in range(K)]
+    every = max(1, args.event_every)
+    sampled = list(range(0, K, every))
+    evs = {i: ev.create(4) for i in sampled}
     plain = sg.LaunchOpts(n_split_small=args.split_small, n_split_large=args.split_large)
-    opts_b = [sg.LaunchOpts(e[0], e[1]) for e in evs]
-    opts_d = [sg.LaunchOpts(e[2], e[3], args.split_small, args.split_large) for e in evs]
+    opts_b = {i: sg.LaunchOpts(e[0], e[1]) for i, e in evs.items()}
+    opts_d = {i: sg.LaunchOpts(e[2], e[3], args.split_small, args.split_large)
+              for i, e in evs.items()}
     calls = []
     for st in sets:
         bargs = (ctypes.c_void_p(st["ids"].data_ptr()), w.M, w.L, w.chunk_size, 1,
@@ -210,8 +283,9 @@ def main():
 
     def step(i, timed=False):
         bargs, dargs = calls[i % n_sets]
-        rc = build_fn(*bargs, opts_b[i].ref() if timed else None, s_handle)
-        rc |= delta_fn(*dargs, opts_d[i].ref() if timed else plain.ref(), s_handle)
+        sample = timed and i in evs
+        rc = build_fn(*bargs, opts_b[i].ref() if sample else None, s_handle)
+        rc |= delta_fn(*dargs, opts_d[i].ref() if sample else plain.ref(), s_handle)
         return rc
 
     rc = 0
@@ -229,23 +303,25 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     assert rc == 0, f"library call failed with status {rc}"
-    build_ms = [ev.elapsed_ms(e[0], e[1]) for e in evs]
-    delta_ms = [ev.elapsed_ms(e[2], e[3]) for e in evs]
-    for e in evs:
+    build_ms = [ev.elapsed_ms(e[0], e[1]) for e in evs.values()]
+    delta_ms = [ev.elapsed_ms(e[2], e[3]) for e in evs.values()]
+    for e in evs.values():
         ev.destroy(e)
+    n_ev = len(delta_ms)
 
     wall = t1 - t0
     ids_np = w.ids.numpy()
     n_lora = int((ids_np >= 0).sum())
     alg_bytes = workloads.algorithmic_bytes(ids_np, w.rank.numpy(), w.K, w.N, elem)
     alg_flops = workloads.algorithmic_flops(ids_np, w.rank.numpy(), w.K, w.N)
-    d_avg = sum(delta_ms) / K / 1e3  # seconds
-    b_avg = sum(build_ms) / K / 1e3
+    d_avg = sum(delta_ms) / n_ev / 1e3  # seconds
+    b_avg = sum(build_ms) / n_ev / 1e3
     srt = sorted(delta_ms)
     achieved = alg_bytes / d_avg / 1e9
     traffic = load_traffic(args.workload, 1)
     log(f"step {wall / K * 1e6:.2f} us | delta kernel avg {d_avg * 1e6:.2f} us "
-        f"(p10 {srt[K // 10] * 1e3:.2f}, p50 {srt[K // 2] * 1e3:.2f}, p90 {srt[9 * K // 10] * 1e3:.2f}) "
+        f"(p10 {srt[n_ev // 10] * 1e3:.2f}, p50 {srt[n_ev // 2] * 1e3:.2f}, "
+        f"p90 {srt[9 * n_ev // 10] * 1e3:.2f}, {n_ev} sampled launches) "
         f"| builder avg {b_avg * 1e6:.2f} us | {achieved:.0f} GB/s algorithmic "
         f"({achieved / HBM_PEAK_GBPS * 100:.1f}% of peak) | {alg_flops / d_avg / 1e12:.2f} TFLOP/s")
 
@@ -268,6 +344,7 @@ def main():
             "lora_tokens_per_step": n_lora,
             "buffer_sets": n_sets,
             "step": "device segment build + fused delta",
+            "timed_launches_sampled": n_ev,
             "delta_kernel_us": d_avg * 1e6,
             "builder_kernel_us": b_avg * 1e6,
             "algorithmic_bytes_per_launch": alg_bytes,
