@@ -45,7 +45,9 @@ METRIC = "LoRA-delta tokens/s + achieved HBM GB/s (% of peak), decode bs=256 d=4
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCE = os.path.join(ROOT, "segmented_gather_gemv_amd", "csrc", "delta_bf16.hip")
+# sources of the fused delta kernel: byte-counter results are kept only while these match
+KERNEL_SOURCES = [os.path.join(ROOT, "segmented_gather_gemv_amd", "csrc", f)
+                  for f in ("delta_bf16.h", "delta_bf16_fused.hip", "common.h", "workspace.h")]
 
 
 def log(*a):
@@ -83,7 +85,10 @@ class HipEvents:
 
 
 def kernel_source_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str, launches_units: int):
@@ -207,6 +212,8 @@ def main():
                     help="column splits per small piece (0: library choice)")
     ap.add_argument("--split-large", type=int, default=0,
                     help="column splits per large piece (0: library choice)")
+    ap.add_argument("--exchange", type=int, default=0, choices=[-1, 0, 1],
+                    help="K-split exchange of small pieces: 0 library choice, 1 on, -1 off")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain device copy of --copy-mib MiB (counter scale)")
     ap.add_argument("--copy-mib", type=int, default=256)
@@ -268,9 +275,10 @@ def main():
     every = max(1, args.event_every)
     sampled = list(range(0, K, every))
     evs = {i: ev.create(4) for i in sampled}
-    plain = sg.LaunchOpts(n_split_small=args.split_small, n_split_large=args.split_large)
+    plain = sg.LaunchOpts(n_split_small=args.split_small, n_split_large=args.split_large,
+                          exchange=args.exchange)
     opts_b = {i: sg.LaunchOpts(e[0], e[1]) for i, e in evs.items()}
-    opts_d = {i: sg.LaunchOpts(e[2], e[3], args.split_small, args.split_large)
+    opts_d = {i: sg.LaunchOpts(e[2], e[3], args.split_small, args.split_large, args.exchange)
               for i, e in evs.items()}
     calls = []
     for st in sets:

@@ -130,7 +130,23 @@ sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t
  * large_cap = M / (SGMV_SMALL_ROWS + 1); small_cap = seg_cap.
  * Array sizes: sorted_token_ids [M], seg_indptr [seg_cap + 1], seg_lora_ids [seg_cap],
  * tiles [(large_cap + small_cap) * SGMV_TILE_INTS], info [4].
+ *
+ * exchange (optional, may be NULL): device workspace of exchange_bytes for the fused call.
+ * With it, a small piece whose output columns are split over P workgroups (2 <= P <=
+ * SGMV_EXCHANGE_MAX_SPLITS) also splits its shrink over K among them: each workgroup sums
+ * its K range, publishes that fp32 partial M x r tile here, and adds all P partials in split
+ * order, so A and x are read once per piece instead of once per workgroup (Ascend article
+ * 3.3: the decode kernel's weight traffic; the full intermediate still never leaves the
+ * chip, only K-range partial sums pass through this buffer). Results do not depend on
+ * timing: a workgroup that waits too long for its partners computes their partials itself,
+ * bit-identically. Layout: [small_cap][16] int32 control words (word 0: the piece's arrival
+ * counter, which every call advances by exactly 64; the rest reserved), padded to 256 bytes,
+ * then [small_cap][SGMV_EXCHANGE_MAX_SPLITS][16][64] fp32 partials. Zero-fill it when it is
+ * allocated; the device builder clears the control words on every build. Fused calls that
+ * share one segments object with an exchange workspace must be ordered on one stream.
  * ------------------------------------------------------------------------------------ */
+#define SGMV_EXCHANGE_MAX_SPLITS 8
+
 typedef struct {
   int32_t* sorted_token_ids;
   int32_t* seg_indptr;
@@ -139,9 +155,12 @@ typedef struct {
   int32_t* info;
   int32_t M, L, chunk_size;
   int32_t seg_cap, large_cap, small_cap;
+  void* exchange;
+  int64_t exchange_bytes;
 } sgmv_segments;
 
-/* Fill seg->M, L, chunk_size and the three capacities; pointers are left untouched.
+/* Fill seg->M, L, chunk_size, the three capacities and exchange_bytes; pointers (including
+ * exchange) are left untouched.
  * Errors: EINVAL (null seg, M < 0, L < 1, chunk_size < 0). */
 sgmv_status sgmv_segments_init(int32_t M, int32_t L, int32_t chunk_size, sgmv_segments* seg);
 
@@ -190,7 +209,8 @@ sgmv_status sgmv_expand(const float* h, int64_t ldh, int32_t M, const sgmv_pool*
                         void* stream);
 
 /* Fused delta (Ascend article 4.3): shrink and expand in one launch; the M x r intermediate
- * stays in registers and LDS and is never written to memory:
+ * stays in registers and LDS and is never written to memory (with an exchange workspace in
+ * `seg`, K-range partial sums of it pass through that workspace; see sgmv_segments):
  *   y[t, n] = round(y[t, n] + scale_l * sum_{j < r} B[l, n, j] * sum_k A[l, j, k] x[t, k]).
  * Same arguments and rules as sgmv_shrink and sgmv_expand. y must not alias x or the pool.
  * Errors: EINVAL; EUNSUPPORTED; EHIP. */
@@ -207,13 +227,20 @@ sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_po
  *     owns and destroys them.
  *   n_split_small, n_split_large: workgroups across the output columns for each small /
  *     large work descriptor in expand and fused calls; 0 = the library's choice, else 1..64.
- * Errors: EINVAL (a split outside 0..64).
+ *   exchange: fused calls only; 0 = the library's choice, 1 = split small pieces' shrink
+ *     over K whenever seg->exchange is set and 2 <= n_split_small <= 8, -1 = never.
+ *   exchange_wait: bound on a workgroup's wait for its partners' partial sums, in units of
+ *     10 ns; 0 = default (20 us), -1 = no wait (every partial not yet published is computed
+ *     locally; same results, for testing that path).
+ * Errors: EINVAL (a split outside 0..64, exchange outside -1..1, exchange_wait < -1).
  * ------------------------------------------------------------------------------------ */
 typedef struct {
   void* start_event;
   void* stop_event;
   int32_t n_split_small;
   int32_t n_split_large;
+  int32_t exchange;
+  int32_t exchange_wait;
 } sgmv_launch_opts;
 
 sgmv_status sgmv_build_segments_ex(const int32_t* lora_indices, int32_t M, int32_t L,

@@ -60,21 +60,26 @@ class _Segments(ctypes.Structure):
                 ("seg_lora_ids", ctypes.c_void_p), ("tiles", ctypes.c_void_p),
                 ("info", ctypes.c_void_p), ("M", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("seg_cap", ctypes.c_int32),
-                ("large_cap", ctypes.c_int32), ("small_cap", ctypes.c_int32)]
+                ("large_cap", ctypes.c_int32), ("small_cap", ctypes.c_int32),
+                ("exchange", ctypes.c_void_p), ("exchange_bytes", ctypes.c_int64)]
 
 
 class _LaunchOpts(ctypes.Structure):
     _fields_ = [("start_event", ctypes.c_void_p), ("stop_event", ctypes.c_void_p),
-                ("n_split_small", ctypes.c_int32), ("n_split_large", ctypes.c_int32)]
+                ("n_split_small", ctypes.c_int32), ("n_split_large", ctypes.c_int32),
+                ("exchange", ctypes.c_int32), ("exchange_wait", ctypes.c_int32)]
 
 
 class LaunchOpts:
     """Optional launch settings: HIP events (raw hipEvent_t handles) that the kernel's own
-    dispatch records at its start and end, and column-split overrides (0 = library's
-    choice)."""
+    dispatch records at its start and end, column-split overrides (0 = library's choice),
+    the K-split exchange of small pieces (0 = library's choice, 1 = on where possible,
+    -1 = off) and its wait bound (10 ns units; 0 = default, -1 = no wait)."""
 
-    def __init__(self, start_event=None, stop_event=None, n_split_small=0, n_split_large=0):
-        self.c = _LaunchOpts(start_event, stop_event, int(n_split_small), int(n_split_large))
+    def __init__(self, start_event=None, stop_event=None, n_split_small=0, n_split_large=0,
+                 exchange=0, exchange_wait=0):
+        self.c = _LaunchOpts(start_event, stop_event, int(n_split_small), int(n_split_large),
+                             int(exchange), int(exchange_wait))
 
     def ref(self):
         return ctypes.byref(self.c)
@@ -234,16 +239,20 @@ class Segments:
     tiles: torch.Tensor          # [(large_cap + small_cap), TILE_INTS] descriptor records
     info: torch.Tensor           # [4]: num_segments, n_large, n_small, status
     desc: _Segments
+    exchange: Optional[torch.Tensor] = None  # fused-call workspace (device, zero-filled)
 
     @property
     def M(self): return self.desc.M
 
     def to(self, device) -> "Segments":
-        """Copy (e.g. host-built) segments to another device."""
+        """Copy (e.g. host-built) segments to another device; a GPU copy gets a fresh
+        exchange workspace."""
         d = _Segments()
         ctypes.memmove(ctypes.byref(d), ctypes.byref(self.desc), ctypes.sizeof(_Segments))
-        out = Segments(*(t.to(device) for t in (self.sorted_token_ids, self.seg_indptr,
-                                                self.seg_lora_ids, self.tiles, self.info)), d)
+        dev = torch.device(device)
+        out = Segments(*(t.to(dev) for t in (self.sorted_token_ids, self.seg_indptr,
+                                             self.seg_lora_ids, self.tiles, self.info)), d,
+                       _exchange_buffer(d, dev))
         out._bind()
         return out
 
@@ -253,6 +262,7 @@ class Segments:
         self.desc.seg_lora_ids = self.seg_lora_ids.data_ptr()
         self.desc.tiles = self.tiles.data_ptr()
         self.desc.info = self.info.data_ptr()
+        self.desc.exchange = None if self.exchange is None else self.exchange.data_ptr()
 
     def host(self) -> dict:
         """Synchronous host view: the trimmed arrays and the counters."""
@@ -270,15 +280,27 @@ class Segments:
         }
 
 
+def _exchange_buffer(desc: _Segments, dev: torch.device) -> Optional[torch.Tensor]:
+    if dev.type != "cuda" or desc.exchange_bytes <= 0:
+        return None
+    buf = torch.zeros(int(desc.exchange_bytes) + 256, dtype=torch.uint8, device=dev)
+    off = (-buf.data_ptr()) % 256  # the library wants 256-byte alignment
+    return buf[off:off + int(desc.exchange_bytes)]
+
+
 def sgmv_segments_alloc(M: int, L: int, chunk_size: int = 0,
-                        device: Union[str, torch.device] = "cuda") -> Segments:
+                        device: Union[str, torch.device] = "cuda",
+                        exchange: bool = True) -> Segments:
+    """Allocate segment arrays for M tokens and L adapters; on a GPU, also the zero-filled
+    exchange workspace of the fused call unless ``exchange`` is False."""
     desc = _Segments()
     _check(_lib.sgmv_segments_init(M, L, chunk_size, ctypes.byref(desc)), "sgmv_segments_init")
     dev = torch.device(device)
     z = lambda n: torch.zeros(max(int(n), 1), dtype=torch.int32, device=dev)
     seg = Segments(z(M), z(desc.seg_cap + 1), z(desc.seg_cap),
                    torch.zeros(max(desc.large_cap + desc.small_cap, 1), TILE_INTS,
-                               dtype=torch.int32, device=dev), z(4), desc)
+                               dtype=torch.int32, device=dev), z(4), desc,
+                   _exchange_buffer(desc, dev) if exchange else None)
     seg._bind()
     return seg
 

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "sgmv.h"
+#include "workspace.h"
 
 namespace sgmv {
 
@@ -16,14 +17,17 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
 
-// Round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats as packed bf16, the first in the low half: one gfx950 conversion instruction,
+// rounding to nearest even (NaN stays NaN; checked bit for bit against the integer
+// round-to-nearest-even on 16.8M fp32 patterns, denormals and ties included).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -67,6 +71,12 @@ struct DeltaArgs {
   int32_t grid_large;     // workgroups [0, grid_large) take large pieces, the rest small ones
   int32_t n_slices;
   int32_t v_total;        // sum of slice widths
+  // K-split exchange of small pieces (fused calls): control words [small_cap][16] (arrival
+  // counter, tag of each split) and partial tiles [small_cap][SGMV_EXCHANGE_MAX_SPLITS][16][64]
+  int32_t* xctl;
+  float* xpart;
+  int32_t exchange;       // nonzero: small pieces split their shrink over K
+  int32_t xwait;          // wait bound in 10 ns ticks; < 0: no wait
   SliceArg slices[SGMV_MAX_SLICES];
 };
 

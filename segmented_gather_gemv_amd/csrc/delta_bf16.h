@@ -1,4 +1,5 @@
-// bf16 multi-LoRA delta on gfx950 matrix cores.
+// bf16 multi-LoRA delta on gfx950 matrix cores (device code; instantiated by
+// delta_bf16_fused.hip and delta_bf16_unfused.hip).
 //
 // One workgroup (8 waves) takes one work descriptor -- a piece of at most 64 rows of one
 // segment, i.e. of one adapter (Ascend article 3.3: start row, row count, adapter) -- and
@@ -32,6 +33,8 @@
 // parts of h go through two MFMAs on that fragment. MFMA q of a 64-column group covers
 // column 4 c + q for lane column c, so a lane's four accumulators are four adjacent columns
 // of one output row and y moves 8 bytes per lane access.
+#pragma once
+
 #include "common.h"
 
 namespace sgmv {
@@ -45,7 +48,8 @@ constexpr int RANK_TABLE_MAX = 2048;  // pools up to this size get rank/scale st
 struct Piece {
   int lora, start, rows, r;
   float scale;
-  int v0, v1;  // column range, in the concatenation of the output slices
+  int v0, v1;         // column range, in the concatenation of the output slices
+  int tile, split, nsplit;  // descriptor index in its class, column split and split count
 };
 
 // Where concatenated output column v lives: its slice's y, row stride, y column, pool column.
@@ -170,15 +174,15 @@ __device__ __forceinline__ void store_y(const int* s_tok, int rows, int rt, int 
       const float d1 = bf16_bits_to_f32(v.x >> 16) + yacc[1][e];
       const float d2 = bf16_bits_to_f32(v.y & 0xffffu) + yacc[2][e];
       const float d3 = bf16_bits_to_f32(v.y >> 16) + yacc[3][e];
-      v.x = f32_to_bf16_bits(d0) | (f32_to_bf16_bits(d1) << 16);
-      v.y = f32_to_bf16_bits(d2) | (f32_to_bf16_bits(d3) << 16);
+      v.x = pack_bf16x2(d0, d1);
+      v.y = pack_bf16x2(d2, d3);
       *reinterpret_cast<uint2*>(yp) = v;
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (vl + q >= v1) continue;
         uint16_t* yp = cm[q].y + tok * (size_t)cm[q].ldy + cm[q].col;
-        *yp = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(*yp) + yacc[q][e]);
+        *yp = (uint16_t)pack_bf16x2(bf16_bits_to_f32(*yp) + yacc[q][e], 0.f);
       }
     }
   }
@@ -200,6 +204,20 @@ __device__ void reduce_partials(int nrt, int ntp, int ks, int r, float mult, con
   }
 }
 
+// hi and lo bf16 parts of 8 consecutive h values (16-byte aligned in LDS): hi = rne(h),
+// lo = rne(h - hi), so hi + lo keeps about 16 significant bits of h.
+__device__ __forceinline__ void split_hi_lo(const float* hp, u32x4_t& hi, u32x4_t& lo) {
+  const float4 a = *reinterpret_cast<const float4*>(hp);
+  const float4 b = *reinterpret_cast<const float4*>(hp + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const uint32_t h2 = pack_bf16x2(v[e], v[e + 1]);
+    hi[e >> 1] = h2;
+    lo[e >> 1] = pack_bf16x2(v[e] - bf16_bits_to_f32(h2 & 0xffffu), v[e + 1] - bf16_bits_to_f32(h2 >> 16));
+  }
+}
+
 // hi and lo bf16 operand fragments of the h tile into s_pf ([row tile][rank tile of 32][hi,
 // lo][lane], 16 B each). Lane (c, g) of fragment (rt, re) holds row rt*16 + c, ranks
 // re*32 + 8g + 0..7; the lo part is h - hi, rounded, so hi + lo keeps about 16 bits of h.
@@ -209,20 +227,8 @@ __device__ void build_fragments(int nrt, const float* s_h, u32x4_t* s_pf) {
   const int c = lane & 15, g = lane >> 4;
   for (int f = w; f < nrt * NE; f += DT_WAVES) {
     const int rt = f / NE, re = f - rt * NE;
-    const float* hp = s_h + (rt * 16 + c) * HS + re * 32 + 8 * g;
     u32x4_t hi, lo;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      uint32_t hb[2], lb[2];
-#pragma unroll
-      for (int z = 0; z < 2; ++z) {
-        const float v = hp[e + z];
-        hb[z] = f32_to_bf16_bits(v);
-        lb[z] = f32_to_bf16_bits(v - bf16_bits_to_f32(hb[z]));
-      }
-      hi[e >> 1] = hb[0] | (hb[1] << 16);
-      lo[e >> 1] = lb[0] | (lb[1] << 16);
-    }
+    split_hi_lo(s_h + (rt * 16 + c) * HS + re * 32 + 8 * g, hi, lo);
     s_pf[(2 * f) * WAVE + lane] = hi;
     s_pf[(2 * f + 1) * WAVE + lane] = lo;
   }
@@ -235,6 +241,20 @@ __device__ __forceinline__ void read_fragments(const u32x4_t* s_pf, int rt, int 
   for (int re = 0; re < NE; ++re) {
     P[re][0] = as_bf16x8(s_pf[(2 * (rt * NE + re)) * WAVE + lane]);
     P[re][1] = as_bf16x8(s_pf[(2 * (rt * NE + re) + 1) * WAVE + lane]);
+  }
+}
+
+// The same hi and lo fragments straight from the h tile, for a wave that needs them once.
+template <int NE>
+__device__ __forceinline__ void h_fragments(const float* s_h, int rt, int lane,
+                                            bf16x8_t (&P)[NE][2]) {
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int re = 0; re < NE; ++re) {
+    u32x4_t hi, lo;
+    split_hi_lo(s_h + (rt * 16 + c) * HS + re * 32 + 8 * g, hi, lo);
+    P[re][0] = as_bf16x8(hi);
+    P[re][1] = as_bf16x8(lo);
   }
 }
 
@@ -292,16 +312,188 @@ struct ExpandPrefetch {
 };
 
 // ---------------------------------------------------------------------------------------
+// K-split exchange between the column-split workgroups of one small piece
+// ---------------------------------------------------------------------------------------
+// Workgroup p of the P that share a small piece reduces K steps [p*nch/P, (p+1)*nch/P) of the
+// shrink, publishes that fp32 partial tile (16 rows x 64 ranks) to the workspace and adds its
+// share to the piece's arrival counter: 1 for every split but the last, which adds 64 - (P-1),
+// so that every call advances the counter by exactly 64 and a workgroup knows that all P
+// partials are in once the counter has moved 64 past the multiple of 64 it found (no reset is
+// needed between calls; the counter wraps safely). It then adds the P partials in split order,
+// so the sum does not depend on which workgroup finished first. If the counter has not moved
+// 64 within a bounded wait, the workgroup computes every other split's partial itself, by the
+// same steps in the same order as its owner (bit-identical), and uses those instead.
+//
+// Memory ordering. Partial tiles are written and read only with agent-scope atomic stores and
+// loads, which bypass the non-coherent caches (the stores write through to the device's
+// coherence point); a workgroup waits for its own stores to complete before it adds to the
+// counter, and reads partials only after it has seen the counter complete. This orders data
+// and counter without agent-scope fences, whose L2 write-back and invalidate would stall every
+// workgroup of the XCD. The partners of a piece run on one XCD and their counter atomics meet
+// in its L2; if they are not seen in time, the local fallback keeps the results unchanged.
+
+// Waits until every vector memory operation of this wave has completed (vmcnt = 0).
+__device__ __forceinline__ void wait_stores() {
+  // s_waitcnt encoding on gfx9: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+}
+
+// Wave partials of one (row, rank), summed in wave order (zero for j >= r).
+template <int NRK>
+__device__ __forceinline__ float wave_sum(const float* s_part, int row, int j, int r) {
+  const int rk = j >> 4, cc = j & 15;
+  float s = 0.f;
+  if (j < r) {
+#pragma unroll
+    for (int q = 0; q < DT_WAVES; ++q) s += s_part[((q * NRK + rk) * 16 + row) * 16 + cc];
+  }
+  return s;
+}
+
+template <int NRK>
+__device__ __forceinline__ void store_wave_partial(float* s_part, int w, int c, int g,
+                                                   const f32x4_t (&acc)[NRK]) {
+  // D layout: lane (c, g) holds rows 4g..4g+3 of column c
+#pragma unroll
+  for (int rk = 0; rk < NRK; ++rk)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_part[((w * NRK + rk) * 16 + 4 * g + e) * 16 + c] = acc[rk][e];
+}
+
+// Entries of a partial tile per thread: 16 rows x NCOL ranks (whole 32-rank expand tiles);
+// thread t holds entries t and t + DT_THREADS.
+template <int NRK>
+struct XchShape {
+  static constexpr int NCOL = (NRK + 1) / 2 * 32;
+  static constexpr int PER = (16 * NCOL + DT_THREADS - 1) / DT_THREADS;
+};
+
+// Wave w's part of the shrink over K steps [k0, k1) of a split, one step at a time (the
+// order of the MFMAs is the same as with several steps per load round).
+template <int NRK, bool ALIGNED>
+__device__ void shrink_split(const DeltaArgs& A, const Piece& pc, const int* s_tok, int k0,
+                             int k1, float* s_part) {
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x & (WAVE - 1);
+  const int c = lane & 15, g = lane >> 4;
+  const bool vx = c < pc.rows;
+  const uint16_t* xr =
+      static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[c] : 0) * (size_t)A.ldx;
+  const uint16_t* ab = static_cast<const uint16_t*>(A.a) + (size_t)pc.lora * A.R_pad * A.K_pad;
+  const int n = k1 - k0;
+  const int c0 = k0 + w * n / DT_WAVES, c1 = k0 + (w + 1) * n / DT_WAVES;
+  f32x4_t acc[NRK];
+#pragma unroll
+  for (int i = 0; i < NRK; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int ch = c0; ch < c1; ++ch) {
+    ShrinkSteps<NRK, 1, ALIGNED> S;
+    S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
+    S.mfma(acc);
+  }
+  store_wave_partial<NRK>(s_part, w, c, g, acc);
+}
+
+// Called by all threads once the wave partials of this workgroup's K range are in s_part.
+// Leaves the scaled full h tile in s_h (16 rows x NCOL ranks).
+template <int NRK, bool ALIGNED>
+__device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const int* s_tok, int nch,
+                           float* s_part, float* s_h, int* s_flag) {
+  using S = XchShape<NRK>;
+  const int tid = threadIdx.x, P = pc.nsplit, p = pc.split;
+  uint32_t* counter = reinterpret_cast<uint32_t*>(A.xctl) + (size_t)pc.tile * XCH_CTL_INTS;
+  float* part = A.xpart + (size_t)pc.tile * SGMV_EXCHANGE_MAX_SPLITS * XCH_TILE_FLOATS;
+
+  // own partial: kept, and published
+  float own[S::PER];
+#pragma unroll
+  for (int e = 0; e < S::PER; ++e) {
+    const int idx = tid + e * DT_THREADS;
+    const int row = idx / S::NCOL, j = idx - row * S::NCOL;
+    own[e] = 0.f;
+    if (idx < 16 * S::NCOL) {
+      own[e] = wave_sum<NRK>(s_part, row, j, pc.r);
+      __hip_atomic_store(part + (p * 16 + row) * 64 + j, own[e], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t inc = p == P - 1 ? 64u - (uint32_t)(P - 1) : 1u;
+    const uint32_t old =
+        __hip_atomic_fetch_add(counter, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t base = old & ~63u;
+    uint32_t cur = old + inc;
+    if (cur - base < 64u && A.xwait >= 0) {
+      const uint64_t t0 = wall_clock64();
+      do {
+        __builtin_amdgcn_s_sleep(2);
+        cur = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } while (cur - base < 64u && wall_clock64() - t0 < (uint64_t)A.xwait);
+    }
+    *s_flag = cur - base >= 64u ? 1 : 0;
+  }
+  __syncthreads();
+
+  float h[S::PER];
+#pragma unroll
+  for (int e = 0; e < S::PER; ++e) h[e] = 0.f;
+  if (*s_flag) {  // uniform: every partial is in
+    float pv[SGMV_EXCHANGE_MAX_SPLITS][S::PER];
+#pragma unroll
+    for (int q = 0; q < SGMV_EXCHANGE_MAX_SPLITS; ++q)
+#pragma unroll
+      for (int e = 0; e < S::PER; ++e) {
+        const int idx = tid + e * DT_THREADS;
+        const int row = idx / S::NCOL, j = idx - row * S::NCOL;
+        pv[q][e] = (q < P && q != p && idx < 16 * S::NCOL)
+                       ? __hip_atomic_load(part + (q * 16 + row) * 64 + j, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : own[e];
+      }
+#pragma unroll
+    for (int q = 0; q < SGMV_EXCHANGE_MAX_SPLITS; ++q)
+#pragma unroll
+      for (int e = 0; e < S::PER; ++e)
+        if (q < P) h[e] += pv[q][e];
+  } else {  // a partner is late: every other partial is computed here, in split order
+    for (int q = 0; q < P; ++q) {
+      if (q != p) {
+        __syncthreads();
+        shrink_split<NRK, ALIGNED>(A, pc, s_tok, q * nch / P, (q + 1) * nch / P, s_part);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int e = 0; e < S::PER; ++e) {
+        const int idx = tid + e * DT_THREADS;
+        const int row = idx / S::NCOL, j = idx - row * S::NCOL;
+        h[e] += q == p ? own[e] : (idx < 16 * S::NCOL ? wave_sum<NRK>(s_part, row, j, pc.r) : 0.f);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < S::PER; ++e) {
+    const int idx = tid + e * DT_THREADS;
+    if (idx < 16 * S::NCOL) {
+      const int row = idx / S::NCOL, j = idx - row * S::NCOL;
+      s_h[row * HS + j] = h[e] * pc.scale;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // small pieces (<= 16 rows): K split across the 8 waves, expand operands prefetched
 // ---------------------------------------------------------------------------------------
-template <int MODE, int NRK, bool ALIGNED>
-__device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc, const int* s_tok, float* s_part,
-                            float* s_h) {
+template <int MODE, int NRK, bool ALIGNED, bool XCH>
+__device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc, const int* s_tok,
+                                            float* s_part, float* s_h, int* s_mask) {
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
+  constexpr bool xch = XCH && MODE == MODE_FUSED;
   // K steps whose loads are issued together, and column groups per wave whose B and y are
-  // prefetched, sized so that everything in flight fits in registers
-  constexpr int NSTEP = NRK == 1 ? 4 : (NRK == 2 ? 2 : 1);
+  // prefetched, sized so that everything in flight fits in registers. With the exchange a
+  // workgroup covers a fraction of K, one step per load round suffices, and the smaller
+  // register footprint lets two workgroups share a CU.
+  constexpr int NSTEP = xch ? 1 : (NRK == 1 ? 4 : (NRK == 2 ? 2 : 1));
   constexpr int PF = NRK == 1 ? 2 : 1;
   constexpr int NE = (NRK + 1) / 2;  // expand rank tiles of 32
   const uint16_t* bb =
@@ -309,6 +501,7 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc,
 
   ExpandPrefetch<NE, PF, ALIGNED> pf;
   bool fetched = false;
+  const int nch = (A.K + KSTEP - 1) / KSTEP;
 
   if (MODE != MODE_EXPAND) {
     f32x4_t acc[NRK];
@@ -318,8 +511,10 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc,
     const uint16_t* xr =
         static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[c] : 0) * (size_t)A.ldx;
     const uint16_t* ab = static_cast<const uint16_t*>(A.a) + (size_t)pc.lora * A.R_pad * A.K_pad;
-    const int nch = (A.K + KSTEP - 1) / KSTEP;
-    const int c0 = w * nch / DT_WAVES, c1 = (w + 1) * nch / DT_WAVES;
+    // K steps of this workgroup (all of K, or its split's range), then of this wave
+    const int k0 = xch ? pc.split * nch / pc.nsplit : 0;
+    const int k1 = xch ? (pc.split + 1) * nch / pc.nsplit : nch;
+    const int c0 = k0 + w * (k1 - k0) / DT_WAVES, c1 = k0 + (w + 1) * (k1 - k0) / DT_WAVES;
     for (int ch = c0; ch < c1; ch += NSTEP) {
       ShrinkSteps<NRK, NSTEP, ALIGNED> S;
       S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
@@ -329,24 +524,19 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc,
       }
       S.mfma(acc);
     }
-    // D layout: lane (c, g) holds rows 4g..4g+3 of column c
-#pragma unroll
-    for (int rk = 0; rk < NRK; ++rk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_part[((w * NRK + rk) * 16 + 4 * g + e) * 16 + c] = acc[rk][e];
+    store_wave_partial<NRK>(s_part, w, c, g, acc);
   }
   if (MODE != MODE_SHRINK && !fetched) pf.load(A, bb, pc, s_tok, w, c, g);
   __syncthreads();
-  if (MODE != MODE_EXPAND)
+  if constexpr (xch)
+    exchange_h<NRK, ALIGNED>(A, pc, s_tok, nch, s_part, s_h, s_mask);
+  else if (MODE != MODE_EXPAND)
     reduce_partials<NRK>(1, 1, DT_WAVES, pc.r, MODE == MODE_SHRINK ? 1.f : pc.scale, s_part, s_h);
   __syncthreads();
   if (MODE == MODE_SHRINK) return;
 
-  u32x4_t* s_pf = reinterpret_cast<u32x4_t*>(s_part);  // free once the partials are summed
-  build_fragments<NE>(1, s_h, s_pf);
-  __syncthreads();
   bf16x8_t P[NE][2];
-  read_fragments<NE>(s_pf, 0, lane, P);
+  h_fragments<NE>(s_h, 0, lane, P);
 
   // prefetched groups
 #pragma unroll
@@ -380,8 +570,8 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc,
 // large pieces (17..64 rows): waves cover (row tile, K slice) pairs and stream K
 // ---------------------------------------------------------------------------------------
 template <int MODE, int NRK, bool ALIGNED>
-__device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc, const int* s_tok, float* s_part,
-                            float* s_h) {
+__device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc, const int* s_tok,
+                                            float* s_part, float* s_h, int*) {
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
   const int nrt = (pc.rows + 15) >> 4;  // 2..4
@@ -444,12 +634,45 @@ __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc,
   }
 }
 
-template <int MODE, bool ALIGNED>
+// Dispatch on the piece's rank tiles (1..NRKM) and class.
+template <int MODE, bool ALIGNED, int NRK, bool XCH>
+__device__ __forceinline__ void piece_of(const DeltaArgs& A, const Piece& pc, bool small,
+                                         const int* s_tok, float* s_part, float* s_h,
+                                         int* s_mask) {
+  if (small)
+    small_piece<MODE, NRK, ALIGNED, XCH>(A, pc, s_tok, s_part, s_h, s_mask);
+  else
+    large_piece<MODE, NRK, ALIGNED>(A, pc, s_tok, s_part, s_h, s_mask);
+}
+
+template <int MODE, bool ALIGNED, int NRKM, bool XCH>
+__device__ __forceinline__ void run_piece(const DeltaArgs& A, const Piece& pc, bool small,
+                                          int nrk, const int* s_tok, float* s_part, float* s_h,
+                                          int* s_mask) {
+  if constexpr (NRKM == 1) {
+    piece_of<MODE, ALIGNED, 1, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask);
+  } else if constexpr (NRKM == 2) {
+    if (nrk <= 1) piece_of<MODE, ALIGNED, 1, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask);
+    else piece_of<MODE, ALIGNED, 2, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask);
+  } else {
+    switch (nrk) {
+      case 1: piece_of<MODE, ALIGNED, 1, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
+      case 2: piece_of<MODE, ALIGNED, 2, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
+      case 3: piece_of<MODE, ALIGNED, 3, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
+      default: piece_of<MODE, ALIGNED, 4, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
+    }
+  }
+}
+
+// Pieces of rank tiles up to NRKM (ranks up to 16 NRKM); XCH: small pieces of fused calls
+// split their shrink over K with the other column splits of the piece.
+template <int MODE, bool ALIGNED, int NRKM, bool XCH>
 __global__ __launch_bounds__(DT_THREADS) void delta_bf16_kernel(DeltaArgs A) {
   __shared__ int s_tok[SGMV_TILE_ROWS];
   __shared__ __align__(16) float s_h[SGMV_TILE_ROWS * HS];
   __shared__ int s_rank[RANK_TABLE_MAX];
   __shared__ float s_scale[RANK_TABLE_MAX];
+  __shared__ int s_mask;  // K-split exchange: 1 when every partner's partial is in
   // partial shrink tiles, [wave][rank tile][16][16] fp32 (R_pad/16 rank tiles); reused for
   // the expand's h fragments afterwards
   extern __shared__ __align__(16) float s_part[];
@@ -484,7 +707,11 @@ __global__ __launch_bounds__(DT_THREADS) void delta_bf16_kernel(DeltaArgs A) {
   const int width = (((A.v_total + P - 1) / P) + 63) & ~63;
   pc.v0 = p * width;
   pc.v1 = min(pc.v0 + width, A.v_total);
-  if (split && pc.v0 >= pc.v1) return;
+  pc.tile = tile;
+  pc.split = p;
+  pc.nsplit = P;
+  // a split with no columns still owes its K range to the exchange
+  if (split && pc.v0 >= pc.v1 && !(MODE == MODE_FUSED && small && XCH)) return;
 
   const int nrk = (pc.r + 15) >> 4;
   if (MODE == MODE_EXPAND) {  // h from memory, scaled
@@ -495,19 +722,7 @@ __global__ __launch_bounds__(DT_THREADS) void delta_bf16_kernel(DeltaArgs A) {
       s_h[row * HS + j] = v;
     }
   }
-#define SGMV_PIECE(FN)                                               \
-  switch (nrk) {                                                     \
-    case 1: FN<MODE, 1, ALIGNED>(A, pc, s_tok, s_part, s_h); break;  \
-    case 2: FN<MODE, 2, ALIGNED>(A, pc, s_tok, s_part, s_h); break;  \
-    case 3: FN<MODE, 3, ALIGNED>(A, pc, s_tok, s_part, s_h); break;  \
-    default: FN<MODE, 4, ALIGNED>(A, pc, s_tok, s_part, s_h); break; \
-  }
-  if (small) {
-    SGMV_PIECE(small_piece)
-  } else {
-    SGMV_PIECE(large_piece)
-  }
-#undef SGMV_PIECE
+  run_piece<MODE, ALIGNED, NRKM, XCH>(A, pc, small, nrk, s_tok, s_part, s_h, &s_mask);
 
   if (MODE == MODE_SHRINK) {  // h (unscaled) of every row to memory; zeros up to R_max
     const int R = A.R_max;
@@ -518,26 +733,15 @@ __global__ __launch_bounds__(DT_THREADS) void delta_bf16_kernel(DeltaArgs A) {
   }
 }
 
-hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, LaunchEvents ev,
-                             hipStream_t stream) {
+
+// Grid and dynamic LDS of a launch; the kernel arguments get the class boundary.
+inline void delta_geometry(int mode, DeltaArgs& A, int& grid, size_t& lds) {
   const bool split = mode != MODE_SHRINK;
   A.grid_large = class_grid(A.large_cap, split ? A.n_split_large : 1);
-  const int grid = A.grid_large + class_grid(A.small_cap, split ? A.n_split_small : 1);
-  if (grid <= 0) return hipSuccess;
-  const dim3 g(grid), b(DT_THREADS);
-  // partial tiles of every wave; at least 16 KB, which also holds the h fragments
-  const size_t lds = (size_t)DT_WAVES * (A.R_pad / 16) * 256 * sizeof(float);
-#define SGMV_LAUNCH(M_, AL_) \
-  hipExtLaunchKernelGGL((delta_bf16_kernel<M_, AL_>), g, b, lds, stream, ev.start, ev.stop, 0, A)
-  if (mode == MODE_FUSED) {
-    if (aligned) SGMV_LAUNCH(MODE_FUSED, true); else SGMV_LAUNCH(MODE_FUSED, false);
-  } else if (mode == MODE_SHRINK) {
-    if (aligned) SGMV_LAUNCH(MODE_SHRINK, true); else SGMV_LAUNCH(MODE_SHRINK, false);
-  } else {
-    if (aligned) SGMV_LAUNCH(MODE_EXPAND, true); else SGMV_LAUNCH(MODE_EXPAND, false);
-  }
-#undef SGMV_LAUNCH
-  return hipGetLastError();
+  grid = A.grid_large + class_grid(A.small_cap, split ? A.n_split_small : 1);
+  // partial tiles of every wave (8 waves x R_pad/16 rank tiles x 1 KB); large pieces reuse
+  // them for their h fragments, which fit for every rank
+  lds = (size_t)DT_WAVES * (A.R_pad / 16) * 256 * sizeof(float);
 }
 
 }  // namespace sgmv

@@ -14,7 +14,8 @@
 //    segments, large and small descriptors) places every bucket;
 //  * larger batches: the same in rounds of 1024 tokens with a running count per key, lanes
 //    of equal keys grouped by ballots.
-// Every global write index is checked against its array bound.
+// Every global write index is checked against its array bound. Both kernels also clear the
+// control words of the fused call's exchange workspace, when the segments carry one.
 #include <climits>
 
 #include "common.h"
@@ -153,7 +154,8 @@ size_t build_small_lds_bytes(int L) {
 __global__ __launch_bounds__(BUILD_THREADS) void build_segments_small_kernel(
     const int32_t* __restrict__ ids, int M, int L, int C, int32_t* __restrict__ sorted,
     int32_t* __restrict__ indptr, int32_t* __restrict__ seg_lora, int32_t* __restrict__ tiles,
-    int32_t* __restrict__ info, int seg_cap, int large_cap, int small_cap) {
+    int32_t* __restrict__ info, int seg_cap, int large_cap, int small_cap,
+    int32_t* __restrict__ xctl, int n_xctl) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int NK = L + 1;
   uint8_t* rc = smem;                                                              // [NK][16]
@@ -164,6 +166,7 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_small_kernel(
 
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
   const bool valid = t < M;
+  for (int i = t; i < n_xctl; i += BUILD_THREADS) xctl[i] = 0;
   for (int i = t; i < NK * (BUILD_WAVES / 4); i += BUILD_THREADS)
     reinterpret_cast<uint32_t*>(rc)[i] = 0;
   if (t == 0) s_bad = 0;
@@ -266,7 +269,8 @@ __device__ int match_rank(bool valid, int key, int t, uint8_t* rc, int* first, i
 __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
     const int32_t* __restrict__ ids, int M, int L, int C, int32_t* __restrict__ sorted,
     int32_t* __restrict__ indptr, int32_t* __restrict__ seg_lora, int32_t* __restrict__ tiles,
-    int32_t* __restrict__ info, int seg_cap, int large_cap, int small_cap) {
+    int32_t* __restrict__ info, int seg_cap, int large_cap, int small_cap,
+    int32_t* __restrict__ xctl, int n_xctl) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int NK = L + 1;  // key L = "no adapter"
   uint8_t* rc = smem;
@@ -282,6 +286,7 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
+  for (int i = tid; i < n_xctl; i += BUILD_THREADS) xctl[i] = 0;
   for (int i = tid; i < NK * (BUILD_WAVES / 4); i += BUILD_THREADS)
     reinterpret_cast<uint32_t*>(rc)[i] = 0;
   for (int i = tid; i < NK; i += BUILD_THREADS) {
@@ -426,15 +431,18 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
 hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_t* sorted,
                                  int32_t* indptr, int32_t* seg_lora, int32_t* tiles,
                                  int32_t* info, int seg_cap, int large_cap, int small_cap,
-                                 LaunchEvents ev, hipStream_t stream) {
+                                 int32_t* xctl, int n_xctl, LaunchEvents ev,
+                                 hipStream_t stream) {
   if (M <= BUILD_THREADS) {
     hipExtLaunchKernelGGL(build_segments_small_kernel, dim3(1), dim3(BUILD_THREADS),
                           build_small_lds_bytes(L), stream, ev.start, ev.stop, 0, ids, M, L, C,
-                          sorted, indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap);
+                          sorted, indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap,
+                          xctl, n_xctl);
   } else {
     hipExtLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(BUILD_THREADS),
                           build_lds_bytes(L), stream, ev.start, ev.stop, 0, ids, M, L, C, sorted,
-                          indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap);
+                          indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap, xctl,
+                          n_xctl);
   }
   return hipGetLastError();
 }

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "sgmv.h"
+#include "workspace.h"
 
 namespace sgmv {
 

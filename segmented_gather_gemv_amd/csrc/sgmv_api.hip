@@ -11,7 +11,8 @@ size_t build_lds_bytes(int L);
 hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_t* sorted,
                                  int32_t* indptr, int32_t* seg_lora, int32_t* tiles,
                                  int32_t* info, int seg_cap, int large_cap, int small_cap,
-                                 LaunchEvents ev, hipStream_t stream);
+                                 int32_t* xctl, int n_xctl, LaunchEvents ev,
+                                 hipStream_t stream);
 hipError_t launch_pool_pack(const void* a_user, const void* b_user, const sgmv_pool& p,
                             hipStream_t stream);
 hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, LaunchEvents ev,
@@ -38,7 +39,9 @@ bool seg_ok(const sgmv_segments* s, int32_t M, int32_t L) {
   if (s->M != M || s->L != L || s->chunk_size < 0) return false;
   int32_t sc, lc, smc;
   segment_capacities(M, L, s->chunk_size, &sc, &lc, &smc);
-  return s->seg_cap == sc && s->large_cap == lc && s->small_cap == smc;
+  if (s->seg_cap != sc || s->large_cap != lc || s->small_cap != smc) return false;
+  return !s->exchange || (s->exchange_bytes >= exchange_bytes(smc) &&
+                          (reinterpret_cast<uintptr_t>(s->exchange) % 256) == 0);
 }
 
 inline bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -107,7 +110,25 @@ void choose_splits(int v_total, const sgmv_launch_opts* opts, DeltaArgs& A) {
 
 bool opts_ok(const sgmv_launch_opts* o) {
   return !o || (o->n_split_small >= 0 && o->n_split_small <= 64 && o->n_split_large >= 0 &&
-                o->n_split_large <= 64);
+                o->n_split_large <= 64 && o->exchange >= -1 && o->exchange <= 1 &&
+                o->exchange_wait >= -1);
+}
+
+// K-split exchange for the small pieces of a fused call: needs the workspace and 2..8 column
+// splits; by default also at least two 128-wide K steps per split, so that every workgroup
+// has work of its own.
+void choose_exchange(const sgmv_segments* seg, const sgmv_launch_opts* o, DeltaArgs& A) {
+  const int want = o ? o->exchange : 0;
+  const int P = A.n_split_small;
+  bool on = want >= 0 && seg->exchange && P >= 2 && P <= SGMV_EXCHANGE_MAX_SPLITS;
+  if (on && want == 0) on = A.K >= 256 * P;
+  A.exchange = on ? 1 : 0;
+  if (!on) return;
+  A.xctl = static_cast<int32_t*>(seg->exchange);
+  A.xpart = reinterpret_cast<float*>(static_cast<char*>(seg->exchange) +
+                                     exchange_counter_bytes(seg->small_cap));
+  const int wait = o ? o->exchange_wait : 0;
+  A.xwait = wait == 0 ? 2000 : (wait < 0 ? -1 : wait);
 }
 
 LaunchEvents events_of(const sgmv_launch_opts* o) {
@@ -165,6 +186,7 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
   } else {
     choose_splits(A.v_total, opts, A);
   }
+  if (mode == MODE_FUSED && pool->dtype == SGMV_BF16) choose_exchange(seg, opts, A);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LaunchEvents ev = events_of(opts);
   if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, ev, s));
@@ -242,6 +264,7 @@ sgmv_status sgmv_segments_init(int32_t M, int32_t L, int32_t chunk_size, sgmv_se
   seg->L = L;
   seg->chunk_size = chunk_size;
   segment_capacities(M, L, chunk_size, &seg->seg_cap, &seg->large_cap, &seg->small_cap);
+  seg->exchange_bytes = exchange_bytes(seg->small_cap);
   return SGMV_OK;
 }
 
@@ -259,10 +282,13 @@ sgmv_status sgmv_build_segments_ex(const int32_t* lora_indices, int32_t M, int32
                                             seg->small_cap);
   }
   if (L > SGMV_DEVICE_BUILDER_MAX_L) return SGMV_EUNSUPPORTED;
+  int32_t* xctl = static_cast<int32_t*>(seg->exchange);
+  const int n_xctl = xctl ? seg->small_cap * XCH_CTL_INTS : 0;
   return hip_status(launch_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
                                           seg->seg_indptr, seg->seg_lora_ids, seg->tiles,
                                           seg->info, seg->seg_cap, seg->large_cap, seg->small_cap,
-                                          events_of(opts), static_cast<hipStream_t>(stream)));
+                                          xctl, n_xctl, events_of(opts),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 sgmv_status sgmv_build_segments(const int32_t* lora_indices, int32_t M, int32_t L,

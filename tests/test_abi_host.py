@@ -183,6 +183,13 @@ def test_segments_init_errors():
     assert (s.seg_cap, s.large_cap, s.small_cap) == (64, 256 // 17, 64)
     assert lib.sgmv_segments_init(2048, 128, 64, ctypes.byref(s)) == sg.SGMV_OK
     assert s.seg_cap == min(2048, 128 + 2048 // 64)
+    # exchange workspace: control words [small_cap][16] padded to 256 B, then partial tiles
+    assert lib.sgmv_segments_init(256, 64, 0, ctypes.byref(s)) == sg.SGMV_OK
+    assert s.exchange_bytes == 64 * 16 * 4 + 64 * 8 * 16 * 64 * 4
+    assert lib.sgmv_segments_init(7, 3, 0, ctypes.byref(s)) == sg.SGMV_OK
+    assert s.exchange_bytes == 256 + 3 * 8 * 16 * 64 * 4
+    assert lib.sgmv_segments_init(0, 4, 0, ctypes.byref(s)) == sg.SGMV_OK
+    assert s.exchange_bytes == 0
 
 
 def test_build_segments_errors():
@@ -250,6 +257,27 @@ def test_delta_argument_errors():
     # expand: null h
     assert lib.sgmv_expand(None, 16, 8, ctypes.byref(pool), ctypes.byref(seg.desc),
                            ctypes.byref(y), 1, None) == sg.SGMV_EINVAL
+
+
+def test_exchange_and_option_errors():
+    """Workspace and option checks happen before any launch."""
+    lib = sg.library()
+    pool = _fake_pool()
+    seg = sg.sgmv_segments_alloc(8, 4, 0, "cpu")
+    y = sg._Slice(0x2000, 256, 0, 256)
+    x = ctypes.c_void_p(0x3000)
+    call = lambda d, o: lib.sgmv_lora_delta_ex(x, 128, 8, ctypes.byref(pool), ctypes.byref(d),
+                                              ctypes.byref(y), 1, o, None)
+    d = sg._Segments()
+    ctypes.memmove(ctypes.byref(d), ctypes.byref(seg.desc), ctypes.sizeof(d))
+    d.exchange = 0x10080  # not 256-byte aligned
+    assert call(d, None) == sg.SGMV_EINVAL
+    d.exchange = 0x10000
+    d.exchange_bytes = seg.desc.exchange_bytes - 1  # too small
+    assert call(d, None) == sg.SGMV_EINVAL
+    for kw in [dict(exchange=2), dict(exchange=-2), dict(exchange_wait=-2),
+               dict(n_split_small=65), dict(n_split_large=-1)]:
+        assert call(seg.desc, sg.LaunchOpts(**kw).ref()) == sg.SGMV_EINVAL, kw
 
 
 def test_empty_batch_is_a_noop():

@@ -392,3 +392,96 @@ def test_unfused_full_size(sg, name):
     assert np.linalg.norm(hg[lora] - hr[lora]) / np.linalg.norm(hr[lora]) <= 1e-4
     ref = oracle_y(w, np32(w.y0), rows=rows)
     compare(np32(y), ref, w.dtype, rows=rows, what=name + " unfused")
+
+
+# ---------------------------------------------------------------------------------------
+# K-split exchange of small pieces (fused calls): column-split workgroups of one piece share
+# the shrink over K through the segments' workspace
+# ---------------------------------------------------------------------------------------
+XCH_CASES = {
+    "xch_decode": dict(M=200, K=2048, N=1024, L=40, R=16, no_lora_frac=0.05),
+    "xch_mixed_rank": dict(M=180, K=1536, N=768, L=30, R=64, ranks=[5, 16, 31, 64]),
+    "xch_odd": dict(M=90, K=1000, N=300, L=20, R=24),          # unaligned kernel, ragged K
+    "xch_narrow": dict(M=64, K=1024, N=64, L=8, R=16),          # splits without columns
+    "xch_chunked": dict(M=240, K=1024, N=512, L=4, R=32, chunk=5, no_lora_frac=0.1),
+}
+
+
+def _xch_control(sg, seg):
+    """Control words [small_cap][16]: word 0 of each small piece is its arrival counter."""
+    n = seg.desc.small_cap * 16
+    return seg.exchange[:n * 4].view(torch.int32).view(-1, 16).cpu()
+
+
+def _check_control(sg, seg, calls):
+    """Every exchange call advances the counter of every small piece by exactly 64."""
+    ctl = _xch_control(sg, seg)
+    ns = int(seg.info[2].item())
+    assert torch.all(ctl[:ns, 0] == 64 * calls), ctl[:ns, 0]
+    assert torch.all(ctl[ns:, 0] == 0) and torch.all(ctl[:, 1:] == 0)
+
+
+def _fused_opts(sg, w, seg, pool, x, y0, **kw):
+    y = y0.clone()
+    sg.sgmv_lora_delta(x, pool, seg, y, opts=sg.LaunchOpts(**kw))
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("name", sorted(XCH_CASES))
+@pytest.mark.parametrize("P", [2, 3, 4, 8])
+def test_exchange_parity_and_determinism(sg, name, P):
+    w = workloads.custom(name=name, seed=11, **XCH_CASES[name])
+    pool, x, y0, ids = upload(w, sg)
+    seg = sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True)
+    assert seg.exchange is not None
+    torch.cuda.synchronize()
+    _check_control(sg, seg, 0)
+    ref = oracle_y(w, np32(w.y0))
+    off = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, exchange=-1)
+    _check_control(sg, seg, 0)
+    on = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, exchange=1)
+    compare(np32(off), ref, w.dtype, what=f"{name} P={P} no exchange")
+    compare(np32(on), ref, w.dtype, what=f"{name} P={P} exchange")
+    check_no_adapter_rows(w, on, w.y0)
+    _check_control(sg, seg, 1)
+    # the sum is taken in split order: the same bits on every call, and when the partials
+    # of late partners are recomputed locally (no wait at all)
+    again = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, exchange=1)
+    local = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, exchange=1,
+                        exchange_wait=-1)
+    assert torch.equal(on, again)
+    assert torch.equal(on, local)
+    _check_control(sg, seg, 3)
+    # a rebuild clears the control words
+    sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True, out=seg)
+    torch.cuda.synchronize()
+    _check_control(sg, seg, 0)
+
+
+def test_exchange_workspace_optional(sg):
+    """Segments without a workspace take the path without exchange; results agree."""
+    w = workloads.custom(name="xch_opt", seed=12, **XCH_CASES["xch_decode"])
+    pool, x, y0, ids = upload(w, sg)
+    seg = sg.sgmv_build_segments(ids, w.L, 0, on_device=True)
+    bare = sg.sgmv_segments_alloc(w.M, w.L, 0, DEV, exchange=False)
+    sg.sgmv_build_segments(ids, w.L, 0, on_device=True, out=bare)
+    assert bare.exchange is None
+    a = _fused_opts(sg, w, seg, pool, x, y0)
+    b = _fused_opts(sg, w, bare, pool, x, y0)
+    ref = oracle_y(w, np32(w.y0))
+    compare(np32(a), ref, w.dtype, what="with workspace")
+    compare(np32(b), ref, w.dtype, what="without workspace")
+
+
+def test_exchange_full_decode_forced_local(sg):
+    """The decode workload with every missing partial computed locally, on sampled rows,
+    bit-identical to the default call."""
+    w = workloads.get("decode")
+    pool, x, y0, ids = upload(w, sg)
+    seg = sg.sgmv_build_segments(ids, w.L, 0, on_device=True)
+    a = _fused_opts(sg, w, seg, pool, x, y0)
+    b = _fused_opts(sg, w, seg, pool, x, y0, exchange_wait=-1)
+    assert torch.equal(a, b)
+    rows = sample_rows(w, 64)
+    compare(np32(a), oracle_y(w, np32(w.y0), rows=rows), w.dtype, rows=rows, what="decode")
