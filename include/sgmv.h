@@ -129,7 +129,7 @@ sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t
  * Capacities: seg_cap = min(M, L) without chunking, min(M, min(M, L) + M / C) with;
  * large_cap = M / (SGMV_SMALL_ROWS + 1); small_cap = seg_cap.
  * Array sizes: sorted_token_ids [M], seg_indptr [seg_cap + 1], seg_lora_ids [seg_cap],
- * tiles [(large_cap + small_cap) * SGMV_TILE_INTS], info [4].
+ * tiles [(large_cap + small_cap) * SGMV_TILE_INTS] (16-byte aligned), info [4].
  *
  * exchange (optional, may be NULL): device workspace of exchange_bytes for the fused call.
  * With it, a small piece whose output columns are split over P workgroups (2 <= P <=

@@ -8,10 +8,10 @@
 // the batching-effect section). A token lands at bucket start + (equal keys before it).
 //
 // Two kernels:
-//  * small batches (M <= 1024, one token per thread): each wave ranks its 64 keys in
-//    registers (readlane loop), a per-(key, wave) byte table in LDS adds the counts of lower
-//    waves, and one workgroup scan over the tokens of (first-appearance flag, bucket size,
-//    segments, large and small descriptors) places every bucket;
+//  * small batches (M <= 1024, one token per thread, 4, 8 or 16 waves): each wave ranks its
+//    64 keys in registers (one ballot per lane), a per-(key, wave) byte table in LDS adds the
+//    counts of lower waves, and one workgroup scan over the tokens of (first-appearance flag,
+//    bucket size, segments, large and small descriptors) places every bucket;
 //  * larger batches: the same in rounds of 1024 tokens with a running count per key, lanes
 //    of equal keys grouped by ballots.
 // Every global write index is checked against its array bound. Both kernels also clear the
@@ -38,24 +38,24 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Exclusive scan of NV ints per thread across the workgroup. s_w holds NV * BUILD_WAVES
+// Exclusive scan of NV ints per thread across a workgroup of NW waves. s_w holds NV * NW
 // ints. Contains barriers: call from all threads.
-template <int NV>
+template <int NV, int NW = BUILD_WAVES>
 __device__ void block_scan(const int (&v)[NV], int (&ex)[NV], int (&tot)[NV], int* s_w) {
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
   int x[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     x[i] = wave_incl_scan(v[i]);
-    if (lane == WAVE - 1) s_w[i * BUILD_WAVES + w] = x[i];
+    if (lane == WAVE - 1) s_w[i * NW + w] = x[i];
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int4* q = reinterpret_cast<const int4*>(s_w + i * BUILD_WAVES);
+    const int4* q = reinterpret_cast<const int4*>(s_w + i * NW);
     int before = 0, all = 0;
 #pragma unroll
-    for (int j = 0; j < BUILD_WAVES / 4; ++j) {
+    for (int j = 0; j < NW / 4; ++j) {
       const int4 s = q[j];
       const int vals[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
@@ -71,14 +71,15 @@ __device__ void block_scan(const int (&v)[NV], int (&ex)[NV], int (&tot)[NV], in
 }
 
 // Counts of equal keys in lower waves (pre), in this wave (cw) and in higher waves (post),
-// from the per-(key, wave) byte table.
+// from the per-(key, wave) byte table of a workgroup of NW waves.
+template <int NW = BUILD_WAVES>
 __device__ __forceinline__ void wave_counts(const uint8_t* rc, int key, int& pre, int& cw,
                                             int& post) {
   const int w = threadIdx.x / WAVE;
-  const u32x4_t q = *reinterpret_cast<const u32x4_t*>(rc + key * BUILD_WAVES);
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(rc + key * NW);
   pre = cw = post = 0;
 #pragma unroll
-  for (int i = 0; i < BUILD_WAVES; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int v = (q[i >> 2] >> (8 * (i & 3))) & 0xff;
     if (i < w) pre += v;
     else if (i == w) cw = v;
@@ -113,14 +114,21 @@ __device__ void write_bucket(int lora, int cnt, int C, int start, int seg0, int 
       const bool small = rows <= SGMV_SMALL_ROWS;
       const int idx = small ? st++ : lt++;
       if (small ? idx >= small_cap : idx >= large_cap) continue;
-      int32_t* d = tiles + (size_t)(small ? large_cap + idx : idx) * SGMV_TILE_INTS;
-      d[0] = lora;
-      d[1] = s0 + r0;
-      d[2] = rows;
-      d[3] = seg;
+      int4* d = reinterpret_cast<int4*>(tiles + (size_t)(small ? large_cap + idx : idx) *
+                                                    SGMV_TILE_INTS);
+      d[0] = make_int4(lora, s0 + r0, rows, seg);
+      d[1] = d[2] = d[3] = make_int4(0, 0, 0, 0);
+      // token slots past the piece's rows; the others belong to the tokens' own threads
+      const int first_free = small ? rows : 0;
 #pragma unroll
-      for (int e = 4; e < 16; ++e) d[e] = 0;
-      for (int e = small ? rows : 0; e < 16; ++e) d[16 + e] = -1;
+      for (int q = 0; q < 4; ++q) {
+        if (4 * q >= first_free) {
+          d[4 + q] = make_int4(-1, -1, -1, -1);
+        } else if (4 * q + 4 > first_free) {
+          int32_t* e = reinterpret_cast<int32_t*>(d + 4 + q);
+          for (int i = first_free - 4 * q; i < 4; ++i) e[i] = -1;
+        }
+      }
     }
   }
 }
@@ -146,29 +154,31 @@ __device__ __forceinline__ void token_slot(int t, int rank, int cnt, int C, int 
 // ---------------------------------------------------------------------------------------
 // small batches: M <= 1024
 // ---------------------------------------------------------------------------------------
-size_t build_small_lds_bytes(int L) {
+size_t build_small_lds_bytes(int L, int nw) {
   const size_t nk = (size_t)L + 1;
-  return align16(nk * BUILD_WAVES) + 2 * align16(nk * sizeof(int));
+  return align16(nk * nw) + 2 * align16(nk * sizeof(int));
 }
 
-__global__ __launch_bounds__(BUILD_THREADS) void build_segments_small_kernel(
+// One token per thread, NW waves (the fewest that cover M).
+template <int NW>
+__global__ __launch_bounds__(NW * WAVE) void build_segments_small_kernel(
     const int32_t* __restrict__ ids, int M, int L, int C, int32_t* __restrict__ sorted,
     int32_t* __restrict__ indptr, int32_t* __restrict__ seg_lora, int32_t* __restrict__ tiles,
     int32_t* __restrict__ info, int seg_cap, int large_cap, int small_cap,
     int32_t* __restrict__ xctl, int n_xctl) {
+  constexpr int NT = NW * WAVE;
   extern __shared__ __align__(16) unsigned char smem[];
   const int NK = L + 1;
-  uint8_t* rc = smem;                                                              // [NK][16]
-  int* s_base = reinterpret_cast<int*>(smem + align16((size_t)NK * BUILD_WAVES));  // [NK]
-  int* s_sbase = s_base + align16((size_t)NK * sizeof(int)) / sizeof(int);        // [NK]
-  __shared__ __align__(16) int s_w[5 * BUILD_WAVES];
+  uint8_t* rc = smem;                                                     // [NK][NW]
+  int* s_base = reinterpret_cast<int*>(smem + align16((size_t)NK * NW));  // [NK]
+  int* s_sbase = s_base + align16((size_t)NK * sizeof(int)) / sizeof(int);  // [NK]
+  __shared__ __align__(16) int s_w[5 * NW];
   __shared__ int s_bad;
 
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
   const bool valid = t < M;
-  for (int i = t; i < n_xctl; i += BUILD_THREADS) xctl[i] = 0;
-  for (int i = t; i < NK * (BUILD_WAVES / 4); i += BUILD_THREADS)
-    reinterpret_cast<uint32_t*>(rc)[i] = 0;
+  for (int i = t; i < n_xctl; i += NT) xctl[i] = 0;
+  for (int i = t; i < NK * (NW / 4); i += NT) reinterpret_cast<uint32_t*>(rc)[i] = 0;
   if (t == 0) s_bad = 0;
   int key = -2;  // never equal to a real key (0..L)
   if (valid) {
@@ -179,20 +189,23 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_small_kernel(
     }
     key = id < 0 ? L : id;
   }
-  // rank among equal keys of lower lanes, and the count in this wave, in registers
-  const int n_in_wave = min(WAVE, max(0, M - w * WAVE));
-  int rk = 0, cw = 0;
-  for (int j = 0; j < n_in_wave; ++j) {
-    const int kj = __builtin_amdgcn_readlane(key, j);
-    const int eq = kj == key ? 1 : 0;
-    cw += eq;
-    rk += j < lane ? eq : 0;
+  // rank among equal keys of lower lanes, and the count in this wave: lane j keeps the
+  // ballot of the lanes holding its key (lanes past M hold a key no token has)
+  uint64_t same = 0;
+  if (w * WAVE < M) {  // uniform; waves without tokens skip it
+#pragma unroll
+    for (int j = 0; j < WAVE; ++j) {
+      const uint64_t m = __ballot(key == __builtin_amdgcn_readlane(key, j));
+      same = lane == j ? m : same;
+    }
   }
+  const int rk = __popcll(same & lanemask_lt(lane));
+  const int cw = __popcll(same);
   __syncthreads();
-  if (valid && rk == 0) rc[key * BUILD_WAVES + w] = (uint8_t)cw;
+  if (valid && rk == 0) rc[key * NW + w] = (uint8_t)cw;
   __syncthreads();
   int pre = 0, cwt = 0, post = 0;
-  if (valid) wave_counts(rc, key, pre, cwt, post);
+  if (valid) wave_counts<NW>(rc, key, pre, cwt, post);
   const int rank = pre + rk;
   const int cnt = pre + cwt + post;
   const bool first = valid && key < L && rank == 0;
@@ -210,7 +223,7 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_small_kernel(
     v[4] = (np - 1) * ns + ns1;
   }
   int ex[5], tot[5];
-  block_scan<5>(v, ex, tot, s_w);
+  block_scan<5, NW>(v, ex, tot, s_w);
   const int n_lora = tot[1], n_seg = tot[2], n_large = tot[3], n_small = tot[4];
   const bool overflow = n_seg > seg_cap || n_large > large_cap || n_small > small_cap;
   if (first) {
@@ -434,10 +447,15 @@ hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_
                                  int32_t* xctl, int n_xctl, LaunchEvents ev,
                                  hipStream_t stream) {
   if (M <= BUILD_THREADS) {
-    hipExtLaunchKernelGGL(build_segments_small_kernel, dim3(1), dim3(BUILD_THREADS),
-                          build_small_lds_bytes(L), stream, ev.start, ev.stop, 0, ids, M, L, C,
-                          sorted, indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap,
-                          xctl, n_xctl);
+#define SGMV_SMALL_BUILD(NW_)                                                                 \
+  hipExtLaunchKernelGGL(build_segments_small_kernel<NW_>, dim3(1), dim3(NW_ * WAVE),         \
+                        build_small_lds_bytes(L, NW_), stream, ev.start, ev.stop, 0, ids, M, \
+                        L, C, sorted, indptr, seg_lora, tiles, info, seg_cap, large_cap,     \
+                        small_cap, xctl, n_xctl)
+    if (M <= 4 * WAVE) SGMV_SMALL_BUILD(4);
+    else if (M <= 8 * WAVE) SGMV_SMALL_BUILD(8);
+    else SGMV_SMALL_BUILD(16);
+#undef SGMV_SMALL_BUILD
   } else {
     hipExtLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(BUILD_THREADS),
                           build_lds_bytes(L), stream, ev.start, ev.stop, 0, ids, M, L, C, sorted,

@@ -37,6 +37,7 @@ bool seg_ok(const sgmv_segments* s, int32_t M, int32_t L) {
   if (!s || !s->sorted_token_ids || !s->seg_indptr || !s->seg_lora_ids || !s->tiles || !s->info)
     return false;
   if (s->M != M || s->L != L || s->chunk_size < 0) return false;
+  if ((reinterpret_cast<uintptr_t>(s->tiles) % 16) != 0) return false;
   int32_t sc, lc, smc;
   segment_capacities(M, L, s->chunk_size, &sc, &lc, &smc);
   if (s->seg_cap != sc || s->large_cap != lc || s->small_cap != smc) return false;

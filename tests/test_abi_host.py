@@ -203,6 +203,12 @@ def test_build_segments_errors():
                                    ctypes.byref(seg.desc), None) == sg.SGMV_EINVAL
     assert lib.sgmv_build_segments(None, 8, 4, 0, 0, ctypes.byref(seg.desc),
                                    None) == sg.SGMV_EINVAL
+    # descriptor records must be 16-byte aligned
+    d = sg._Segments()
+    ctypes.memmove(ctypes.byref(d), ctypes.byref(seg.desc), ctypes.sizeof(d))
+    d.tiles = seg.desc.tiles + 4
+    assert lib.sgmv_build_segments(ctypes.c_void_p(ids.data_ptr()), 8, 4, 0, 0, ctypes.byref(d),
+                                   None) == sg.SGMV_EINVAL
     # device builder limit on the pool size is checked before any launch
     big = sg.sgmv_segments_alloc(8, 5000, 0, "cpu")
     assert lib.sgmv_build_segments(ctypes.c_void_p(ids.data_ptr()), 8, 5000, 0, 1,

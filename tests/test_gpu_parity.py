@@ -136,6 +136,12 @@ def builder_cases():
         ("fast_all_distinct", rng.permutation(1024), 1024, 0),
         ("fast_runs_c64", np.repeat(rng.integers(0, 9, 12), rng.integers(1, 90, 12)), 9, 64),
         ("fast_pool_1024", rng.integers(-1, 1024, 700), 1024, 5),
+        # fewest waves covering M: 4 waves up to 256 tokens, 8 up to 512
+        ("fast_256_distinct", rng.permutation(256), 256, 0),
+        ("fast_257", rng.integers(-1, 30, 257), 30, 0),
+        ("fast_300_c3", rng.integers(-1, 90, 300), 90, 3),
+        ("fast_512_one_key", np.full(512, 7), 8, 16),
+        ("fast_513", rng.integers(-1, 600, 513), 600, 0),
     ]
     for name in ("decode", "prefill", "mixed", "qkv"):
         w = workloads.get(name)
