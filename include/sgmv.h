@@ -132,20 +132,24 @@ sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t
  * tiles [(large_cap + small_cap) * SGMV_TILE_INTS] (16-byte aligned), info [4].
  *
  * exchange (optional, may be NULL): device workspace of exchange_bytes for the fused call.
- * With it, a small piece whose output columns are split over P workgroups (2 <= P <=
- * SGMV_EXCHANGE_MAX_SPLITS) also splits its shrink over K among them: each workgroup sums
- * its K range, publishes that fp32 partial M x r tile here, and adds all P partials in split
- * order, so A and x are read once per piece instead of once per workgroup (Ascend article
- * 3.3: the decode kernel's weight traffic; the full intermediate still never leaves the
- * chip, only K-range partial sums pass through this buffer). Results do not depend on
- * timing: a workgroup that waits too long for its partners computes their partials itself,
- * bit-identically. Layout: [small_cap][16] int32 control words (word 0: the piece's arrival
- * counter, which every call advances by exactly 64; the rest reserved), padded to 256 bytes,
- * then [small_cap][SGMV_EXCHANGE_MAX_SPLITS][16][64] fp32 partials. Zero-fill it when it is
- * allocated; the device builder clears the control words on every build. Fused calls that
- * share one segments object with an exchange workspace must be ordered on one stream.
+ * With it, a piece whose output columns are split over P workgroups (2 <= P <=
+ * SGMV_EXCHANGE_MAX_SPLITS for small pieces, <= SGMV_EXCHANGE_MAX_SPLITS_LARGE for large
+ * ones) also splits its shrink over K among them: each workgroup sums its K range, publishes
+ * that fp32 partial rows x r tile here, and adds all P partials in split order, so A and x
+ * are read once per piece instead of once per workgroup (Ascend article 3.3: weight traffic
+ * of the decode kernel; the full intermediate still never leaves the chip, only K-range
+ * partial sums pass through this buffer). Results do not depend on timing: a workgroup that
+ * waits too long for its partners computes their partials itself, bit-identically.
+ * Layout: [large_cap + small_cap][16] int32 control words indexed like the descriptor records
+ * (word 0: the piece's arrival counter, which every call advances by exactly 64; the rest
+ * reserved), padded to 256 bytes; then [small_cap][SGMV_EXCHANGE_MAX_SPLITS][16][64] fp32
+ * small-piece partials; then [large_cap][SGMV_EXCHANGE_MAX_SPLITS_LARGE][64][64] fp32
+ * large-piece partials. Zero-fill it when it is allocated; the device builder clears the
+ * control words on every build. Fused calls that share one segments object with an exchange
+ * workspace must be ordered on one stream.
  * ------------------------------------------------------------------------------------ */
 #define SGMV_EXCHANGE_MAX_SPLITS 8
+#define SGMV_EXCHANGE_MAX_SPLITS_LARGE 4
 
 typedef struct {
   int32_t* sorted_token_ids;
@@ -227,11 +231,13 @@ sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_po
  *     owns and destroys them.
  *   n_split_small, n_split_large: workgroups across the output columns for each small /
  *     large work descriptor in expand and fused calls; 0 = the library's choice, else 1..64.
- *   exchange: fused calls only; 0 = the library's choice, 1 = split small pieces' shrink
- *     over K whenever seg->exchange is set and 2 <= n_split_small <= 8, -1 = never.
- *   exchange_wait: bound on a workgroup's wait for its partners' partial sums, in units of
- *     10 ns; 0 = default (20 us), -1 = no wait (every partial not yet published is computed
- *     locally; same results, for testing that path).
+ *   exchange: fused calls only; 0 = the library's choice, 1 = split a piece class's shrink
+ *     over K whenever seg->exchange is set and its split count is in range (small: 2..8,
+ *     large: 2..4), -1 = never.
+ *   exchange_wait: bound on a small piece's wait for its partners' partial sums, in units of
+ *     10 ns (large pieces wait up to 10 times as long); 0 = default (20 us), -1 = no wait
+ *     (every partial not yet published is computed locally; same results, for testing that
+ *     path).
  * Errors: EINVAL (a split outside 0..64, exchange outside -1..1, exchange_wait < -1).
  * ------------------------------------------------------------------------------------ */
 typedef struct {

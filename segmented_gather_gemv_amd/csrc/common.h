@@ -71,12 +71,14 @@ struct DeltaArgs {
   int32_t grid_large;     // workgroups [0, grid_large) take large pieces, the rest small ones
   int32_t n_slices;
   int32_t v_total;        // sum of slice widths
-  // K-split exchange of small pieces (fused calls): control words [small_cap][16] (arrival
-  // counter, tag of each split) and partial tiles [small_cap][SGMV_EXCHANGE_MAX_SPLITS][16][64]
+  // K-split exchange (fused calls): control words indexed like the records, partial tiles
+  // of small and of large pieces (layout in workspace.h)
   int32_t* xctl;
-  float* xpart;
-  int32_t exchange;       // nonzero: small pieces split their shrink over K
-  int32_t xwait;          // wait bound in 10 ns ticks; < 0: no wait
+  float* xpart_small;
+  float* xpart_large;
+  int32_t xch_small, xch_large;  // nonzero: that piece class splits its shrink over K
+  int32_t xwait;                 // small pieces' wait bound in 10 ns ticks; < 0: no wait
+  int32_t xwait_large;
   SliceArg slices[SGMV_MAX_SLICES];
 };
 

@@ -292,13 +292,45 @@ struct ShrinkSteps {
   }
 };
 
+// One K step of 128 for one wave, loaded and multiplied in two halves of 64: half the
+// registers of ShrinkSteps<NRK, 1> for the loads in flight, the same MFMAs in the same order.
+template <int NRK, bool ALIGNED>
+__device__ __forceinline__ void shrink_step_halves(const uint16_t* xr, bool vx,
+                                                   const uint16_t* ab, int K_pad, int K, int r,
+                                                   int ch, int c1, int c, int g,
+                                                   f32x4_t (&acc)[NRK]) {
+  const bool live = ch < c1;
+  const int kb = ch * KSTEP + 8 * g;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    u32x4_t xv[2], av[NRK][2];
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const int k = kb + 32 * (2 * hf + i2);
+      xv[i2] = load_x8<ALIGNED>(xr, k, K, vx && live);
+#pragma unroll
+      for (int rk = 0; rk < NRK; ++rk) {
+        const int j = rk * 16 + c;
+        av[rk][i2] = (live && j < r && k < K) ? load_u32x4(ab + (size_t)j * K_pad + k)
+                                               : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int rk = 0; rk < NRK; ++rk)
+        acc[rk] = mfma_16x16x32_bf16(as_bf16x8(xv[i2]), as_bf16x8(av[rk][i2]), acc[rk]);
+  }
+}
+
 // B fragments and old y of the first PF column groups of a wave (small pieces), loaded
 // before the shrink's MFMAs so their latency overlaps the shrink.
 template <int NE, int PF, bool ALIGNED>
 struct ExpandPrefetch {
-  ColMap cm[PF][4];
-  u32x4_t bq[PF][NE][4];
-  uint2 yv[PF][4];
+  static constexpr int N = PF > 0 ? PF : 1;  // PF = 0: no prefetch (never loaded)
+  ColMap cm[N][4];
+  u32x4_t bq[N][NE][4];
+  uint2 yv[N][4];
   __device__ __forceinline__ void load(const DeltaArgs& A, const uint16_t* bb, const Piece& pc,
                                        const int* s_tok, int w, int c, int g) {
 #pragma unroll
@@ -312,10 +344,10 @@ struct ExpandPrefetch {
 };
 
 // ---------------------------------------------------------------------------------------
-// K-split exchange between the column-split workgroups of one small piece
+// K-split exchange between the column-split workgroups of one piece
 // ---------------------------------------------------------------------------------------
-// Workgroup p of the P that share a small piece reduces K steps [p*nch/P, (p+1)*nch/P) of the
-// shrink, publishes that fp32 partial tile (16 rows x 64 ranks) to the workspace and adds its
+// Workgroup p of the P that share a piece reduces K steps [p*nch/P, (p+1)*nch/P) of the
+// shrink, publishes that fp32 partial tile (rows x ranks) to the workspace and adds its
 // share to the piece's arrival counter: 1 for every split but the last, which adds 64 - (P-1),
 // so that every call advances the counter by exactly 64 and a workgroup knows that all P
 // partials are in once the counter has moved 64 past the multiple of 64 it found (no reset is
@@ -338,14 +370,30 @@ __device__ __forceinline__ void wait_stores() {
   __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
-// Wave partials of one (row, rank), summed in wave order (zero for j >= r).
+// How the 8 waves of a workgroup share a piece's shrink: wave w takes row tile w % ntp and
+// K slice w / ntp (ks slices). Small pieces: one row tile, 8 K slices; large pieces: 2 row
+// tiles x 4 slices or 4 row tiles (3 or 4 used) x 2 slices.
+struct ShrinkGeom {
+  int nrt, ntp, ks;
+};
+
+__device__ __forceinline__ ShrinkGeom shrink_geom(bool small, int rows) {
+  ShrinkGeom G;
+  G.nrt = small ? 1 : (rows + 15) >> 4;
+  G.ntp = small ? 1 : (G.nrt == 2 ? 2 : 4);
+  G.ks = DT_WAVES / G.ntp;
+  return G;
+}
+
+// Partial h of (row, rank j) of a piece: the wave partials in s_part
+// ([wave][rank tile][16][16]) summed over the K slices in slice order; zero for j >= r.
 template <int NRK>
-__device__ __forceinline__ float wave_sum(const float* s_part, int row, int j, int r) {
-  const int rk = j >> 4, cc = j & 15;
+__device__ __forceinline__ float part_sum(const float* s_part, const ShrinkGeom& G, int row,
+                                          int j, int r) {
+  const int rt = row >> 4, rr = row & 15, rk = j >> 4, cc = j & 15;
   float s = 0.f;
   if (j < r) {
-#pragma unroll
-    for (int q = 0; q < DT_WAVES; ++q) s += s_part[((q * NRK + rk) * 16 + row) * 16 + cc];
+    for (int q = 0; q < G.ks; ++q) s += s_part[(((q * G.ntp + rt) * NRK + rk) * 16 + rr) * 16 + cc];
   }
   return s;
 }
@@ -360,47 +408,62 @@ __device__ __forceinline__ void store_wave_partial(float* s_part, int w, int c, 
     for (int e = 0; e < 4; ++e) s_part[((w * NRK + rk) * 16 + 4 * g + e) * 16 + c] = acc[rk][e];
 }
 
-// Entries of a partial tile per thread: 16 rows x NCOL ranks (whole 32-rank expand tiles);
-// thread t holds entries t and t + DT_THREADS.
-template <int NRK>
+// Entries of a partial tile per thread: up to 16 (small) or 64 (large) rows x NCOL ranks
+// (whole 32-rank expand tiles); thread t holds entries t, t + DT_THREADS, ...
+template <int NRK, bool LARGE>
 struct XchShape {
   static constexpr int NCOL = (NRK + 1) / 2 * 32;
-  static constexpr int PER = (16 * NCOL + DT_THREADS - 1) / DT_THREADS;
+  static constexpr int ROWS = LARGE ? 64 : 16;
+  static constexpr int PER = (ROWS * NCOL + DT_THREADS - 1) / DT_THREADS;
+  static constexpr int MAXS = LARGE ? SGMV_EXCHANGE_MAX_SPLITS_LARGE : SGMV_EXCHANGE_MAX_SPLITS;
+  static constexpr int64_t TILE = LARGE ? XCH_LARGE_TILE : XCH_SMALL_TILE;
 };
 
-// Wave w's part of the shrink over K steps [k0, k1) of a split, one step at a time (the
-// order of the MFMAs is the same as with several steps per load round).
+// Wave w's part of the shrink over K steps [k0, k1) of a split, one step at a time, into
+// s_part. The MFMAs run in the same order as in the pieces' own loops, which issue several
+// steps per load round, so the partial is bit-identical to its owner's.
 template <int NRK, bool ALIGNED>
-__device__ void shrink_split(const DeltaArgs& A, const Piece& pc, const int* s_tok, int k0,
-                             int k1, float* s_part) {
+__device__ void shrink_range(const DeltaArgs& A, const Piece& pc, const ShrinkGeom& G,
+                             const int* s_tok, int k0, int k1, float* s_part) {
   const int w = threadIdx.x / WAVE, lane = threadIdx.x & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
-  const bool vx = c < pc.rows;
+  const int rt = w % G.ntp, kslice = w / G.ntp;
+  const int row = rt * 16 + c;
+  const bool vx = rt < G.nrt && row < pc.rows;
   const uint16_t* xr =
-      static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[c] : 0) * (size_t)A.ldx;
+      static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[row] : 0) * (size_t)A.ldx;
   const uint16_t* ab = static_cast<const uint16_t*>(A.a) + (size_t)pc.lora * A.R_pad * A.K_pad;
   const int n = k1 - k0;
-  const int c0 = k0 + w * n / DT_WAVES, c1 = k0 + (w + 1) * n / DT_WAVES;
+  const int c0 = k0 + kslice * n / G.ks, c1 = k0 + (kslice + 1) * n / G.ks;
   f32x4_t acc[NRK];
 #pragma unroll
   for (int i = 0; i < NRK; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int ch = c0; ch < c1; ++ch) {
-    ShrinkSteps<NRK, 1, ALIGNED> S;
-    S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
-    S.mfma(acc);
+  if (rt < G.nrt) {
+    for (int ch = c0; ch < c1; ++ch) {
+      if constexpr (NRK >= 3) {
+        shrink_step_halves<NRK, ALIGNED>(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g, acc);
+      } else {
+        ShrinkSteps<NRK, 1, ALIGNED> S;
+        S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
+        S.mfma(acc);
+      }
+    }
   }
   store_wave_partial<NRK>(s_part, w, c, g, acc);
 }
 
 // Called by all threads once the wave partials of this workgroup's K range are in s_part.
-// Leaves the scaled full h tile in s_h (16 rows x NCOL ranks).
-template <int NRK, bool ALIGNED>
-__device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const int* s_tok, int nch,
-                           float* s_part, float* s_h, int* s_flag) {
-  using S = XchShape<NRK>;
+// Leaves the scaled full h tile in s_h (nrt * 16 rows x NCOL ranks).
+template <int NRK, bool ALIGNED, bool LARGE>
+__device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom& G,
+                           const int* s_tok, int nch, float* s_part, float* s_h, int* s_flag) {
+  using S = XchShape<NRK, LARGE>;
   const int tid = threadIdx.x, P = pc.nsplit, p = pc.split;
-  uint32_t* counter = reinterpret_cast<uint32_t*>(A.xctl) + (size_t)pc.tile * XCH_CTL_INTS;
-  float* part = A.xpart + (size_t)pc.tile * SGMV_EXCHANGE_MAX_SPLITS * XCH_TILE_FLOATS;
+  const int entries = G.nrt * 16 * S::NCOL;
+  const size_t rec = LARGE ? (size_t)pc.tile : (size_t)A.large_cap + pc.tile;
+  uint32_t* counter = reinterpret_cast<uint32_t*>(A.xctl) + rec * XCH_CTL_INTS;
+  float* part = (LARGE ? A.xpart_large : A.xpart_small) + (size_t)pc.tile * S::MAXS * S::TILE;
+  const int64_t wait = LARGE ? A.xwait_large : A.xwait;
 
   // own partial: kept, and published
   float own[S::PER];
@@ -409,9 +472,9 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const int* s_tok
     const int idx = tid + e * DT_THREADS;
     const int row = idx / S::NCOL, j = idx - row * S::NCOL;
     own[e] = 0.f;
-    if (idx < 16 * S::NCOL) {
-      own[e] = wave_sum<NRK>(s_part, row, j, pc.r);
-      __hip_atomic_store(part + (p * 16 + row) * 64 + j, own[e], __ATOMIC_RELAXED,
+    if (idx < entries) {
+      own[e] = part_sum<NRK>(s_part, G, row, j, pc.r);
+      __hip_atomic_store(part + p * S::TILE + row * 64 + j, own[e], __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -423,12 +486,12 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const int* s_tok
         __hip_atomic_fetch_add(counter, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t base = old & ~63u;
     uint32_t cur = old + inc;
-    if (cur - base < 64u && A.xwait >= 0) {
+    if (cur - base < 64u && wait >= 0) {
       const uint64_t t0 = wall_clock64();
       do {
         __builtin_amdgcn_s_sleep(2);
         cur = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } while (cur - base < 64u && wall_clock64() - t0 < (uint64_t)A.xwait);
+      } while (cur - base < 64u && wall_clock64() - t0 < (uint64_t)wait);
     }
     *s_flag = cur - base >= 64u ? 1 : 0;
   }
@@ -438,20 +501,20 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const int* s_tok
 #pragma unroll
   for (int e = 0; e < S::PER; ++e) h[e] = 0.f;
   if (*s_flag) {  // uniform: every partial is in
-    float pv[SGMV_EXCHANGE_MAX_SPLITS][S::PER];
+    float pv[S::MAXS][S::PER];
 #pragma unroll
-    for (int q = 0; q < SGMV_EXCHANGE_MAX_SPLITS; ++q)
+    for (int q = 0; q < S::MAXS; ++q)
 #pragma unroll
       for (int e = 0; e < S::PER; ++e) {
         const int idx = tid + e * DT_THREADS;
         const int row = idx / S::NCOL, j = idx - row * S::NCOL;
-        pv[q][e] = (q < P && q != p && idx < 16 * S::NCOL)
-                       ? __hip_atomic_load(part + (q * 16 + row) * 64 + j, __ATOMIC_RELAXED,
+        pv[q][e] = (q < P && q != p && idx < entries)
+                       ? __hip_atomic_load(part + q * S::TILE + row * 64 + j, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT)
                        : own[e];
       }
 #pragma unroll
-    for (int q = 0; q < SGMV_EXCHANGE_MAX_SPLITS; ++q)
+    for (int q = 0; q < S::MAXS; ++q)
 #pragma unroll
       for (int e = 0; e < S::PER; ++e)
         if (q < P) h[e] += pv[q][e];
@@ -459,21 +522,21 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const int* s_tok
     for (int q = 0; q < P; ++q) {
       if (q != p) {
         __syncthreads();
-        shrink_split<NRK, ALIGNED>(A, pc, s_tok, q * nch / P, (q + 1) * nch / P, s_part);
+        shrink_range<NRK, ALIGNED>(A, pc, G, s_tok, q * nch / P, (q + 1) * nch / P, s_part);
         __syncthreads();
       }
 #pragma unroll
       for (int e = 0; e < S::PER; ++e) {
         const int idx = tid + e * DT_THREADS;
         const int row = idx / S::NCOL, j = idx - row * S::NCOL;
-        h[e] += q == p ? own[e] : (idx < 16 * S::NCOL ? wave_sum<NRK>(s_part, row, j, pc.r) : 0.f);
+        h[e] += q == p ? own[e] : (idx < entries ? part_sum<NRK>(s_part, G, row, j, pc.r) : 0.f);
       }
     }
   }
 #pragma unroll
   for (int e = 0; e < S::PER; ++e) {
     const int idx = tid + e * DT_THREADS;
-    if (idx < 16 * S::NCOL) {
+    if (idx < entries) {
       const int row = idx / S::NCOL, j = idx - row * S::NCOL;
       s_h[row * HS + j] = h[e] * pc.scale;
     }
@@ -488,13 +551,14 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc,
                                             float* s_part, float* s_h, int* s_mask) {
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
-  constexpr bool xch = XCH && MODE == MODE_FUSED;
+  constexpr bool xkernel = XCH && MODE == MODE_FUSED;
+  const bool xch = xkernel && A.xch_small;
   // K steps whose loads are issued together, and column groups per wave whose B and y are
   // prefetched, sized so that everything in flight fits in registers. With the exchange a
   // workgroup covers a fraction of K, one step per load round suffices, and the smaller
   // register footprint lets two workgroups share a CU.
-  constexpr int NSTEP = xch ? 1 : (NRK == 1 ? 4 : (NRK == 2 ? 2 : 1));
-  constexpr int PF = NRK == 1 ? 2 : 1;
+  constexpr int NSTEP = xkernel ? 1 : (NRK == 1 ? 4 : (NRK == 2 ? 2 : 1));
+  constexpr int PF = NRK == 1 ? 2 : ((xkernel && NRK >= 3) ? 0 : 1);
   constexpr int NE = (NRK + 1) / 2;  // expand rank tiles of 32
   const uint16_t* bb =
       static_cast<const uint16_t*>(A.b) + (size_t)pc.lora * (A.R_pad / 8) * A.N_pad * 8;
@@ -516,20 +580,25 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc,
     const int k1 = xch ? (pc.split + 1) * nch / pc.nsplit : nch;
     const int c0 = k0 + w * (k1 - k0) / DT_WAVES, c1 = k0 + (w + 1) * (k1 - k0) / DT_WAVES;
     for (int ch = c0; ch < c1; ch += NSTEP) {
-      ShrinkSteps<NRK, NSTEP, ALIGNED> S;
-      S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
-      if (MODE == MODE_FUSED && !fetched) {  // rides along the first loads
-        pf.load(A, bb, pc, s_tok, w, c, g);
-        fetched = true;
+      if constexpr (xkernel && NRK >= 3) {
+        shrink_step_halves<NRK, ALIGNED>(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g, acc);
+      } else {
+        ShrinkSteps<NRK, NSTEP, ALIGNED> S;
+        S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
+        if (MODE == MODE_FUSED && PF > 0 && !fetched) {  // rides along the first loads
+          pf.load(A, bb, pc, s_tok, w, c, g);
+          fetched = true;
+        }
+        S.mfma(acc);
       }
-      S.mfma(acc);
     }
     store_wave_partial<NRK>(s_part, w, c, g, acc);
   }
-  if (MODE != MODE_SHRINK && !fetched) pf.load(A, bb, pc, s_tok, w, c, g);
+  if (MODE != MODE_SHRINK && PF > 0 && !fetched) pf.load(A, bb, pc, s_tok, w, c, g);
   __syncthreads();
-  if constexpr (xch)
-    exchange_h<NRK, ALIGNED>(A, pc, s_tok, nch, s_part, s_h, s_mask);
+  if (xch)
+    exchange_h<NRK, ALIGNED, false>(A, pc, shrink_geom(true, pc.rows), s_tok, nch, s_part, s_h,
+                                    s_mask);
   else if (MODE != MODE_EXPAND)
     reduce_partials<NRK>(1, 1, DT_WAVES, pc.r, MODE == MODE_SHRINK ? 1.f : pc.scale, s_part, s_h);
   __syncthreads();
@@ -569,16 +638,17 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc,
 // ---------------------------------------------------------------------------------------
 // large pieces (17..64 rows): waves cover (row tile, K slice) pairs and stream K
 // ---------------------------------------------------------------------------------------
-template <int MODE, int NRK, bool ALIGNED>
+template <int MODE, int NRK, bool ALIGNED, bool XCH>
 __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc, const int* s_tok,
-                                            float* s_part, float* s_h, int*) {
+                                            float* s_part, float* s_h, int* s_mask) {
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
-  const int nrt = (pc.rows + 15) >> 4;  // 2..4
-  const int ntp = nrt == 2 ? 2 : 4;
-  const int ks = DT_WAVES / ntp;
+  const ShrinkGeom G = shrink_geom(false, pc.rows);
+  const int nrt = G.nrt, ntp = G.ntp, ks = G.ks;  // 2..4 row tiles
+  constexpr bool xkernel = XCH && MODE == MODE_FUSED;
+  const bool xch = xkernel && A.xch_large;
   if (MODE != MODE_EXPAND) {
-    constexpr int NSTEP = NRK <= 2 ? 2 : 1;
+    constexpr int NSTEP = xkernel ? 1 : (NRK <= 2 ? 2 : 1);
     const int rt = w % ntp, kslice = w / ntp;
     f32x4_t acc[NRK];
 #pragma unroll
@@ -591,19 +661,28 @@ __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc,
       const uint16_t* ab =
           static_cast<const uint16_t*>(A.a) + (size_t)pc.lora * A.R_pad * A.K_pad;
       const int nch = (A.K + KSTEP - 1) / KSTEP;
-      const int c0 = kslice * nch / ks, c1 = (kslice + 1) * nch / ks;
+      // K steps of this workgroup (all of K, or its split's range), then of this K slice
+      const int k0 = xch ? pc.split * nch / pc.nsplit : 0;
+      const int k1 = xch ? (pc.split + 1) * nch / pc.nsplit : nch;
+      const int c0 = k0 + kslice * (k1 - k0) / ks, c1 = k0 + (kslice + 1) * (k1 - k0) / ks;
       for (int ch = c0; ch < c1; ch += NSTEP) {
-        ShrinkSteps<NRK, NSTEP, ALIGNED> S;
-        S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
-        S.mfma(acc);
+        if constexpr (xkernel && NRK >= 3) {
+          shrink_step_halves<NRK, ALIGNED>(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g, acc);
+        } else {
+          ShrinkSteps<NRK, NSTEP, ALIGNED> S;
+          S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
+          S.mfma(acc);
+        }
       }
     }
-#pragma unroll
-    for (int rk = 0; rk < NRK; ++rk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_part[((w * NRK + rk) * 16 + 4 * g + e) * 16 + c] = acc[rk][e];
+    store_wave_partial<NRK>(s_part, w, c, g, acc);
     __syncthreads();
-    reduce_partials<NRK>(nrt, ntp, ks, pc.r, MODE == MODE_SHRINK ? 1.f : pc.scale, s_part, s_h);
+    if (xch)
+      exchange_h<NRK, ALIGNED, true>(A, pc, G, s_tok, (A.K + KSTEP - 1) / KSTEP, s_part, s_h,
+                                     s_mask);
+    else
+      reduce_partials<NRK>(nrt, ntp, ks, pc.r, MODE == MODE_SHRINK ? 1.f : pc.scale, s_part,
+                           s_h);
   }
   __syncthreads();
   if (MODE == MODE_SHRINK) return;
@@ -642,7 +721,7 @@ __device__ __forceinline__ void piece_of(const DeltaArgs& A, const Piece& pc, bo
   if (small)
     small_piece<MODE, NRK, ALIGNED, XCH>(A, pc, s_tok, s_part, s_h, s_mask);
   else
-    large_piece<MODE, NRK, ALIGNED>(A, pc, s_tok, s_part, s_h, s_mask);
+    large_piece<MODE, NRK, ALIGNED, XCH>(A, pc, s_tok, s_part, s_h, s_mask);
 }
 
 template <int MODE, bool ALIGNED, int NRKM, bool XCH>
@@ -667,7 +746,7 @@ __device__ __forceinline__ void run_piece(const DeltaArgs& A, const Piece& pc, b
 // Pieces of rank tiles up to NRKM (ranks up to 16 NRKM); XCH: small pieces of fused calls
 // split their shrink over K with the other column splits of the piece.
 template <int MODE, bool ALIGNED, int NRKM, bool XCH>
-__global__ __launch_bounds__(DT_THREADS) void delta_bf16_kernel(DeltaArgs A) {
+__global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH ? 4 : 1))) void delta_bf16_kernel(DeltaArgs A) {
   __shared__ int s_tok[SGMV_TILE_ROWS];
   __shared__ __align__(16) float s_h[SGMV_TILE_ROWS * HS];
   __shared__ int s_rank[RANK_TABLE_MAX];
@@ -711,7 +790,9 @@ __global__ __launch_bounds__(DT_THREADS) void delta_bf16_kernel(DeltaArgs A) {
   pc.split = p;
   pc.nsplit = P;
   // a split with no columns still owes its K range to the exchange
-  if (split && pc.v0 >= pc.v1 && !(MODE == MODE_FUSED && small && XCH)) return;
+  if (split && pc.v0 >= pc.v1 &&
+      !(MODE == MODE_FUSED && XCH && (small ? A.xch_small : A.xch_large)))
+    return;
 
   const int nrk = (pc.r + 15) >> 4;
   if (MODE == MODE_EXPAND) {  // h from memory, scaled

@@ -41,7 +41,7 @@ bool seg_ok(const sgmv_segments* s, int32_t M, int32_t L) {
   int32_t sc, lc, smc;
   segment_capacities(M, L, s->chunk_size, &sc, &lc, &smc);
   if (s->seg_cap != sc || s->large_cap != lc || s->small_cap != smc) return false;
-  return !s->exchange || (s->exchange_bytes >= exchange_bytes(smc) &&
+  return !s->exchange || (s->exchange_bytes >= exchange_layout(lc, smc).bytes &&
                           (reinterpret_cast<uintptr_t>(s->exchange) % 256) == 0);
 }
 
@@ -99,12 +99,13 @@ void fill_common(const sgmv_pool* p, const sgmv_segments* seg, DeltaArgs& A) {
 
 // Column splits per work descriptor: enough workgroups to cover the chip for decode-like
 // pieces, few enough that x rows and A are not re-read too often for prefill-like ones
-// (every split of a piece recomputes its shrink). Caller overrides win.
-void choose_splits(int v_total, const sgmv_launch_opts* opts, DeltaArgs& A) {
-  int ps = v_total / 1024;
-  int pl = v_total / 2048;
-  ps = ps < 1 ? 1 : (ps > 16 ? 16 : ps);
-  pl = pl < 1 ? 1 : (pl > 16 ? 16 : pl);
+// (every split of a piece recomputes its shrink unless the K-split exchange is on, in which
+// case the splits share it and more of them pay). Caller overrides win.
+void choose_splits(int v_total, bool exchange, const sgmv_launch_opts* opts, DeltaArgs& A) {
+  auto clamp = [](int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); };
+  const int ps = clamp(v_total / 1024, 1, exchange ? SGMV_EXCHANGE_MAX_SPLITS : 16);
+  const int pl = exchange ? clamp(v_total / 1024, 1, SGMV_EXCHANGE_MAX_SPLITS_LARGE)
+                          : clamp(v_total / 2048, 1, 16);
   A.n_split_small = (opts && opts->n_split_small > 0) ? opts->n_split_small : ps;
   A.n_split_large = (opts && opts->n_split_large > 0) ? opts->n_split_large : pl;
 }
@@ -115,21 +116,27 @@ bool opts_ok(const sgmv_launch_opts* o) {
                 o->exchange_wait >= -1);
 }
 
-// K-split exchange for the small pieces of a fused call: needs the workspace and 2..8 column
-// splits; by default also at least two 128-wide K steps per split, so that every workgroup
-// has work of its own.
+// K-split exchange of a fused call, per piece class: needs the workspace and a split count
+// in range (small pieces 2..8, large 2..4); by default also at least two 128-wide K steps per
+// split, so that every workgroup has work of its own.
 void choose_exchange(const sgmv_segments* seg, const sgmv_launch_opts* o, DeltaArgs& A) {
   const int want = o ? o->exchange : 0;
-  const int P = A.n_split_small;
-  bool on = want >= 0 && seg->exchange && P >= 2 && P <= SGMV_EXCHANGE_MAX_SPLITS;
-  if (on && want == 0) on = A.K >= 256 * P;
-  A.exchange = on ? 1 : 0;
-  if (!on) return;
-  A.xctl = static_cast<int32_t*>(seg->exchange);
-  A.xpart = reinterpret_cast<float*>(static_cast<char*>(seg->exchange) +
-                                     exchange_counter_bytes(seg->small_cap));
+  auto on = [&](int P, int pmax) {
+    bool v = want >= 0 && seg->exchange && P >= 2 && P <= pmax;
+    if (v && want == 0) v = A.K >= 256 * P;
+    return v;
+  };
+  A.xch_small = on(A.n_split_small, SGMV_EXCHANGE_MAX_SPLITS) ? 1 : 0;
+  A.xch_large = on(A.n_split_large, SGMV_EXCHANGE_MAX_SPLITS_LARGE) ? 1 : 0;
+  if (!A.xch_small && !A.xch_large) return;
+  const ExchangeLayout x = exchange_layout(seg->large_cap, seg->small_cap);
+  char* base = static_cast<char*>(seg->exchange);
+  A.xctl = reinterpret_cast<int32_t*>(base);
+  A.xpart_small = reinterpret_cast<float*>(base + x.small_off);
+  A.xpart_large = reinterpret_cast<float*>(base + x.large_off);
   const int wait = o ? o->exchange_wait : 0;
   A.xwait = wait == 0 ? 2000 : (wait < 0 ? -1 : wait);
+  A.xwait_large = A.xwait < 0 ? -1 : 10 * A.xwait;
 }
 
 LaunchEvents events_of(const sgmv_launch_opts* o) {
@@ -185,7 +192,9 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
   if (mode == MODE_SHRINK) {
     A.n_split_large = A.n_split_small = 1;
   } else {
-    choose_splits(A.v_total, opts, A);
+    const bool xch = mode == MODE_FUSED && pool->dtype == SGMV_BF16 && seg->exchange &&
+                     !(opts && opts->exchange < 0);
+    choose_splits(A.v_total, xch, opts, A);
   }
   if (mode == MODE_FUSED && pool->dtype == SGMV_BF16) choose_exchange(seg, opts, A);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -265,7 +274,7 @@ sgmv_status sgmv_segments_init(int32_t M, int32_t L, int32_t chunk_size, sgmv_se
   seg->L = L;
   seg->chunk_size = chunk_size;
   segment_capacities(M, L, chunk_size, &seg->seg_cap, &seg->large_cap, &seg->small_cap);
-  seg->exchange_bytes = exchange_bytes(seg->small_cap);
+  seg->exchange_bytes = exchange_layout(seg->large_cap, seg->small_cap).bytes;
   return SGMV_OK;
 }
 
@@ -284,7 +293,7 @@ sgmv_status sgmv_build_segments_ex(const int32_t* lora_indices, int32_t M, int32
   }
   if (L > SGMV_DEVICE_BUILDER_MAX_L) return SGMV_EUNSUPPORTED;
   int32_t* xctl = static_cast<int32_t*>(seg->exchange);
-  const int n_xctl = xctl ? seg->small_cap * XCH_CTL_INTS : 0;
+  const int n_xctl = xctl ? (seg->large_cap + seg->small_cap) * XCH_CTL_INTS : 0;
   return hip_status(launch_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
                                           seg->seg_indptr, seg->seg_lora_ids, seg->tiles,
                                           seg->info, seg->seg_cap, seg->large_cap, seg->small_cap,

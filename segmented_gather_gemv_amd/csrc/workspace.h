@@ -7,18 +7,26 @@
 
 namespace sgmv {
 
-// Exchange workspace of the fused call: [small_cap][XCH_CTL_INTS] int32 control words (word 0
-// is the piece's arrival counter, the rest are reserved and kept zero) padded to 256 bytes,
-// then
-// [small_cap][SGMV_EXCHANGE_MAX_SPLITS][16][64] fp32 partial tiles.
+// Exchange workspace of the fused call:
+//   control words [large_cap + small_cap][XCH_CTL_INTS] int32, indexed like the descriptor
+//     records (large pieces first); word 0 is the piece's arrival counter, the rest reserved
+//     and kept zero; padded to 256 bytes;
+//   small-piece partial tiles [small_cap][SGMV_EXCHANGE_MAX_SPLITS][16][64] fp32;
+//   large-piece partial tiles [large_cap][SGMV_EXCHANGE_MAX_SPLITS_LARGE][64][64] fp32.
 constexpr int XCH_CTL_INTS = 16;
-constexpr int64_t XCH_TILE_FLOATS = 16 * 64;
-inline int64_t exchange_counter_bytes(int32_t small_cap) {
-  return ((int64_t)small_cap * XCH_CTL_INTS * 4 + 255) / 256 * 256;
-}
-inline int64_t exchange_bytes(int32_t small_cap) {
-  return exchange_counter_bytes(small_cap) +
-         (int64_t)small_cap * SGMV_EXCHANGE_MAX_SPLITS * XCH_TILE_FLOATS * 4;
+constexpr int64_t XCH_SMALL_TILE = 16 * 64;  // floats per small partial tile
+constexpr int64_t XCH_LARGE_TILE = 64 * 64;  // floats per large partial tile
+
+struct ExchangeLayout {
+  int64_t small_off, large_off, bytes;  // byte offsets of the partial regions, total size
+};
+
+inline ExchangeLayout exchange_layout(int32_t large_cap, int32_t small_cap) {
+  ExchangeLayout x;
+  x.small_off = ((int64_t)(large_cap + small_cap) * XCH_CTL_INTS * 4 + 255) / 256 * 256;
+  x.large_off = x.small_off + (int64_t)small_cap * SGMV_EXCHANGE_MAX_SPLITS * XCH_SMALL_TILE * 4;
+  x.bytes = x.large_off + (int64_t)large_cap * SGMV_EXCHANGE_MAX_SPLITS_LARGE * XCH_LARGE_TILE * 4;
+  return x;
 }
 
 }  // namespace sgmv

@@ -183,9 +183,12 @@ def test_segments_init_errors():
     assert (s.seg_cap, s.large_cap, s.small_cap) == (64, 256 // 17, 64)
     assert lib.sgmv_segments_init(2048, 128, 64, ctypes.byref(s)) == sg.SGMV_OK
     assert s.seg_cap == min(2048, 128 + 2048 // 64)
-    # exchange workspace: control words [small_cap][16] padded to 256 B, then partial tiles
+    # exchange workspace
+    # (control words [large_cap + small_cap][16] padded to 256 B, small tiles [8][16][64],
+    # large tiles [4][64][64], fp32)
     assert lib.sgmv_segments_init(256, 64, 0, ctypes.byref(s)) == sg.SGMV_OK
-    assert s.exchange_bytes == 64 * 16 * 4 + 64 * 8 * 16 * 64 * 4
+    assert (s.large_cap, s.small_cap) == (15, 64)
+    assert s.exchange_bytes == 5120 + 64 * 8 * 16 * 64 * 4 + 15 * 4 * 64 * 64 * 4
     assert lib.sgmv_segments_init(7, 3, 0, ctypes.byref(s)) == sg.SGMV_OK
     assert s.exchange_bytes == 256 + 3 * 8 * 16 * 64 * 4
     assert lib.sgmv_segments_init(0, 4, 0, ctypes.byref(s)) == sg.SGMV_OK

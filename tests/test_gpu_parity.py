@@ -410,21 +410,30 @@ XCH_CASES = {
     "xch_odd": dict(M=90, K=1000, N=300, L=20, R=24),          # unaligned kernel, ragged K
     "xch_narrow": dict(M=64, K=1024, N=64, L=8, R=16),          # splits without columns
     "xch_chunked": dict(M=240, K=1024, N=512, L=4, R=32, chunk=5, no_lora_frac=0.1),
+    # large pieces (17..64 rows) and ragged tails, several rank tiles
+    "xch_prefill": dict(M=400, K=2048, N=768, L=6, R=64, ranks=[16, 40, 64],
+                        seq_lens=[200, 17, 64, 119]),
+    "xch_prefill_r16": dict(M=300, K=1024, N=512, L=3, R=16, seq_lens=[100, 150, 50]),
+    "xch_prefill_odd": dict(M=150, K=700, N=200, L=4, R=48, seq_lens=[33, 90, 27]),
 }
 
 
 def _xch_control(sg, seg):
-    """Control words [small_cap][16]: word 0 of each small piece is its arrival counter."""
-    n = seg.desc.small_cap * 16
+    """Control words [large_cap + small_cap][16], indexed like the records: word 0 of each
+    piece is its arrival counter."""
+    n = (seg.desc.large_cap + seg.desc.small_cap) * 16
     return seg.exchange[:n * 4].view(torch.int32).view(-1, 16).cpu()
 
 
 def _check_control(sg, seg, calls):
-    """Every exchange call advances the counter of every small piece by exactly 64."""
+    """Every exchange call advances the counter of every piece by exactly 64."""
     ctl = _xch_control(sg, seg)
-    ns = int(seg.info[2].item())
-    assert torch.all(ctl[:ns, 0] == 64 * calls), ctl[:ns, 0]
-    assert torch.all(ctl[ns:, 0] == 0) and torch.all(ctl[:, 1:] == 0)
+    nl, ns = int(seg.info[1].item()), int(seg.info[2].item())
+    lc = seg.desc.large_cap
+    assert torch.all(ctl[:nl, 0] == 64 * calls), ctl[:nl, 0]
+    assert torch.all(ctl[nl:lc, 0] == 0)
+    assert torch.all(ctl[lc:lc + ns, 0] == 64 * calls), ctl[lc:lc + ns, 0]
+    assert torch.all(ctl[lc + ns:, 0] == 0) and torch.all(ctl[:, 1:] == 0)
 
 
 def _fused_opts(sg, w, seg, pool, x, y0, **kw):
@@ -444,17 +453,18 @@ def test_exchange_parity_and_determinism(sg, name, P):
     torch.cuda.synchronize()
     _check_control(sg, seg, 0)
     ref = oracle_y(w, np32(w.y0))
-    off = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, exchange=-1)
+    PL = min(P, 4)
+    off = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, n_split_large=PL, exchange=-1)
     _check_control(sg, seg, 0)
-    on = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, exchange=1)
+    on = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, n_split_large=PL, exchange=1)
     compare(np32(off), ref, w.dtype, what=f"{name} P={P} no exchange")
     compare(np32(on), ref, w.dtype, what=f"{name} P={P} exchange")
     check_no_adapter_rows(w, on, w.y0)
     _check_control(sg, seg, 1)
     # the sum is taken in split order: the same bits on every call, and when the partials
     # of late partners are recomputed locally (no wait at all)
-    again = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, exchange=1)
-    local = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, exchange=1,
+    again = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, n_split_large=PL, exchange=1)
+    local = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, n_split_large=PL, exchange=1,
                         exchange_wait=-1)
     assert torch.equal(on, again)
     assert torch.equal(on, local)
@@ -491,3 +501,28 @@ def test_exchange_full_decode_forced_local(sg):
     assert torch.equal(a, b)
     rows = sample_rows(w, 64)
     compare(np32(a), oracle_y(w, np32(w.y0), rows=rows), w.dtype, rows=rows, what="decode")
+
+
+@pytest.mark.parametrize("name", ["prefill", "mixed", "qkv"])
+def test_exchange_full_size_forced_local(sg, name):
+    """Full-size workloads with large pieces: the default call (large and small pieces split
+    their shrink over K) is bit-identical to the call that computes every partner's partial
+    locally, and matches the oracle on sampled rows."""
+    w = workloads.get(name)
+    pool, x, y0, ids = upload(w, sg)
+    seg = sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True)
+    def call(**kw):
+        y = y0.clone()
+        views = [(y[:, n0:n0 + n].contiguous(), n0) for n0, n in w.slices]
+        sg.sgmv_lora_delta(x, pool, seg, views if len(views) > 1 else views[0][0],
+                           opts=sg.LaunchOpts(**kw))
+        torch.cuda.synchronize()
+        for t, n0 in views:
+            y[:, n0:n0 + t.shape[1]] = t
+        return y
+
+    a = call()
+    b = call(exchange_wait=-1)
+    assert torch.equal(a, b)
+    rows = sample_rows(w, 64)
+    compare(np32(a), oracle_y(w, np32(w.y0), rows=rows), w.dtype, rows=rows, what=name)
