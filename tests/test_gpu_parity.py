@@ -142,6 +142,14 @@ def builder_cases():
         ("fast_300_c3", rng.integers(-1, 90, 300), 90, 3),
         ("fast_512_one_key", np.full(512, 7), 8, 16),
         ("fast_513", rng.integers(-1, 600, 513), 600, 0),
+        # mid-size kernel (ids staged in LDS, per-wave ranges), its bounds, and beyond them
+        ("mid_1025_c3", rng.integers(-1, 7, 1025), 7, 3),
+        ("mid_L600", rng.integers(-1, 600, 2000), 600, 0),
+        ("beyond_mid_lds", rng.integers(-1, 900, 2000), 900, 0),
+        ("mid_runs_c64", np.repeat(rng.integers(-1, 40, 90), rng.integers(1, 400, 90)), 40, 64),
+        ("mid_16k", rng.integers(-1, 50, 16384), 50, 0),
+        ("mid_29k_c7", rng.integers(-1, 10, 29000), 10, 7),
+        ("mid_over", rng.integers(-1, 50, 32769), 50, 16),
     ]
     for name in ("decode", "prefill", "mixed", "qkv"):
         w = workloads.get(name)
@@ -167,14 +175,22 @@ def test_device_builder_bit_exact(sg, case):
     check_records(dev, ref)
 
 
-def test_device_builder_bad_ids_flagged(sg):
-    ids = torch.tensor([0, 5, 1, -3, 0, 2], dtype=torch.int32)
-    dev = sg.sgmv_build_segments(ids.to(DEV), 3, 0, on_device=True).host()
+@pytest.mark.parametrize("M", [6, 700, 5000, 40000])  # each builder kernel
+def test_device_builder_bad_ids_flagged(sg, M):
+    rng = np.random.default_rng(M)
+    ids = rng.integers(-1, 3, M).astype(np.int32)
+    bad = rng.choice(M, size=max(1, M // 100), replace=False)
+    ids[bad] = rng.choice([5, -3, 3, 1 << 20], size=bad.size)
+    dev = sg.sgmv_build_segments(torch.from_numpy(ids).to(DEV), 3, 0, on_device=True).host()
     assert dev["status"] == sg.SGMV_EBADID
-    clean = torch.tensor([0, -1, 1, -1, 0, 2], dtype=torch.int32)
-    ref = oracle.segments(clean.numpy(), 3, 0)
+    clean = ids.copy()
+    clean[bad] = -1
+    ref = oracle.segments(clean, 3, 0)
     assert np.array_equal(dev["sorted_token_ids"].numpy(), ref["sorted_token_ids"])
     assert np.array_equal(dev["seg_indptr"].numpy(), ref["seg_indptr"])
+    # the same ids without the bad ones are clean
+    ok = sg.sgmv_build_segments(torch.from_numpy(clean).to(DEV), 3, 0, on_device=True).host()
+    assert ok["status"] == sg.SGMV_OK
 
 
 def test_device_builder_reuse_of_buffers(sg):
