@@ -452,8 +452,94 @@ __device__ void shrink_range(const DeltaArgs& A, const Piece& pc, const ShrinkGe
   store_wave_partial<NRK>(s_part, w, c, g, acc);
 }
 
-// Called by all threads once the wave partials of this workgroup's K range are in s_part.
-// Leaves the scaled full h tile in s_h (nrt * 16 rows x NCOL ranks).
+// Shrink of a large piece over K steps [k0, k1) of KSTEP: the 8 waves split the range into
+// 8 slices of 32-wide substeps, and each wave accumulates every row tile x rank tile of the
+// piece over its slice, so x and A are each read once per workgroup. The wave partials are
+// then summed in wave order, one row tile at a time, into s_h rows (times mult; zero at ranks
+// >= r). The same steps in the same order serve a piece's own partial and the local
+// recomputation of a partner's, so both are bit-identical.
+template <int NRK, bool ALIGNED>
+__device__ void large_shrink(const DeltaArgs& A, const Piece& pc, int nrt, const int* s_tok,
+                             int k0, int k1, float mult, float* s_part, float* s_h) {
+  constexpr int NCOL = (NRK + 1) / 2 * 32;  // whole 32-rank expand tiles
+  const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
+  const int c = lane & 15, g = lane >> 4;
+  const int n = 4 * (k1 - k0);  // 32-wide substeps of the range
+  const int u0 = 4 * k0 + w * n / DT_WAVES, u1 = 4 * k0 + (w + 1) * n / DT_WAVES;
+  const uint16_t* ab = static_cast<const uint16_t*>(A.a) + (size_t)pc.lora * A.R_pad * A.K_pad;
+  const uint16_t* xr[4];
+  bool vx[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int row = rt * 16 + c;
+    vx[rt] = rt < nrt && row < pc.rows;
+    xr[rt] = static_cast<const uint16_t*>(A.x) + (size_t)(vx[rt] ? s_tok[row] : 0) * (size_t)A.ldx;
+  }
+  f32x4_t acc[4][NRK];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int rk = 0; rk < NRK; ++rk) acc[rt][rk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int u = u0; u < u1; ++u) {
+    const int k = 32 * u + 8 * g;
+    u32x4_t xv[4], av[NRK];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) xv[rt] = load_x8<ALIGNED>(xr[rt], k, A.K, vx[rt]);
+#pragma unroll
+    for (int rk = 0; rk < NRK; ++rk) {
+      const int j = rk * 16 + c;
+      av[rk] = (j < pc.r && k < A.K) ? load_u32x4(ab + (size_t)j * A.K_pad + k)
+                                      : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt < nrt) {  // uniform
+#pragma unroll
+        for (int rk = 0; rk < NRK; ++rk)
+          acc[rt][rk] = mfma_16x16x32_bf16(as_bf16x8(xv[rt]), as_bf16x8(av[rk]), acc[rt][rk]);
+      }
+    }
+  }
+  const ShrinkGeom G1{1, 1, DT_WAVES};  // one row tile, 8 K slices (the waves)
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    if (rt >= nrt) break;  // uniform
+    store_wave_partial<NRK>(s_part, w, c, g, acc[rt]);
+    __syncthreads();
+    for (int idx = tid; idx < 16 * NCOL; idx += DT_THREADS) {
+      const int row = idx / NCOL, j = idx - row * NCOL;
+      s_h[(rt * 16 + row) * HS + j] = part_sum<NRK>(s_part, G1, row, j, pc.r) * mult;
+    }
+    __syncthreads();
+  }
+}
+
+// Writes partial tile `slot` of a piece from this workgroup's partial: large pieces have it
+// summed in s_h, small pieces as wave partials in s_part. Call from all threads.
+template <int NRK, bool LARGE>
+__device__ __forceinline__ void store_partial(const Piece& pc, const ShrinkGeom& G,
+                                              const float* s_part, const float* s_h,
+                                              float* slot) {
+  using S = XchShape<NRK, LARGE>;
+  const int entries = G.nrt * 16 * S::NCOL;
+#pragma unroll
+  for (int e = 0; e < S::PER; ++e) {
+    const int idx = threadIdx.x + e * DT_THREADS;
+    if (idx < entries) {
+      const int row = idx / S::NCOL, j = idx - row * S::NCOL;
+      float v;
+      if constexpr (LARGE)
+        v = s_h[row * HS + j];
+      else
+        v = part_sum<NRK>(s_part, G, row, j, pc.r);
+      __hip_atomic_store(slot + row * 64 + j, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Called by all threads once this workgroup's partial for its K range is in s_part (small
+// pieces: wave partials) or s_h (large pieces: summed). Leaves the scaled full h tile in s_h
+// (nrt * 16 rows x NCOL ranks).
 template <int NRK, bool ALIGNED, bool LARGE>
 __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom& G,
                            const int* s_tok, int nch, float* s_part, float* s_h, int* s_flag) {
@@ -465,19 +551,7 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
   float* part = (LARGE ? A.xpart_large : A.xpart_small) + (size_t)pc.tile * S::MAXS * S::TILE;
   const int64_t wait = LARGE ? A.xwait_large : A.xwait;
 
-  // own partial: kept, and published
-  float own[S::PER];
-#pragma unroll
-  for (int e = 0; e < S::PER; ++e) {
-    const int idx = tid + e * DT_THREADS;
-    const int row = idx / S::NCOL, j = idx - row * S::NCOL;
-    own[e] = 0.f;
-    if (idx < entries) {
-      own[e] = part_sum<NRK>(s_part, G, row, j, pc.r);
-      __hip_atomic_store(part + p * S::TILE + row * 64 + j, own[e], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  store_partial<NRK, LARGE>(pc, G, s_part, s_h, part + p * S::TILE);
   wait_stores();
   __syncthreads();
   if (tid == 0) {
@@ -497,48 +571,47 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
   }
   __syncthreads();
 
-  float h[S::PER];
-#pragma unroll
-  for (int e = 0; e < S::PER; ++e) h[e] = 0.f;
-  if (*s_flag) {  // uniform: every partial is in
-    float pv[S::MAXS][S::PER];
-#pragma unroll
-    for (int q = 0; q < S::MAXS; ++q)
-#pragma unroll
-      for (int e = 0; e < S::PER; ++e) {
-        const int idx = tid + e * DT_THREADS;
-        const int row = idx / S::NCOL, j = idx - row * S::NCOL;
-        pv[q][e] = (q < P && q != p && idx < entries)
-                       ? __hip_atomic_load(part + q * S::TILE + row * 64 + j, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT)
-                       : own[e];
-      }
-#pragma unroll
-    for (int q = 0; q < S::MAXS; ++q)
-#pragma unroll
-      for (int e = 0; e < S::PER; ++e)
-        if (q < P) h[e] += pv[q][e];
-  } else {  // a partner is late: every other partial is computed here, in split order
+  if (!*s_flag) {  // uniform: a partner is late. Every other partial is computed here, by the
+                   // same steps as its owner's, and written to its slot (the owner, if it is
+                   // still running, writes the same bits)
     for (int q = 0; q < P; ++q) {
-      if (q != p) {
-        __syncthreads();
+      if (q == p) continue;
+      __syncthreads();  // the previous round's readers of s_part / s_h are done
+      if constexpr (LARGE)
+        large_shrink<NRK, ALIGNED>(A, pc, G.nrt, s_tok, q * nch / P, (q + 1) * nch / P, 1.f,
+                                   s_part, s_h);
+      else
         shrink_range<NRK, ALIGNED>(A, pc, G, s_tok, q * nch / P, (q + 1) * nch / P, s_part);
-        __syncthreads();
-      }
-#pragma unroll
-      for (int e = 0; e < S::PER; ++e) {
-        const int idx = tid + e * DT_THREADS;
-        const int row = idx / S::NCOL, j = idx - row * S::NCOL;
-        h[e] += q == p ? own[e] : (idx < entries ? part_sum<NRK>(s_part, G, row, j, pc.r) : 0.f);
-      }
+      __syncthreads();
+      store_partial<NRK, LARGE>(pc, G, s_part, s_h, part + q * S::TILE);
     }
+    wait_stores();
+    __syncthreads();
   }
+
+  // every partial is in its slot: the sum in split order, scaled
+  float pv[S::MAXS][S::PER];
+#pragma unroll
+  for (int q = 0; q < S::MAXS; ++q)
+#pragma unroll
+    for (int e = 0; e < S::PER; ++e) {
+      const int idx = tid + e * DT_THREADS;
+      const int row = idx / S::NCOL, j = idx - row * S::NCOL;
+      pv[q][e] = (q < P && idx < entries)
+                     ? __hip_atomic_load(part + q * S::TILE + row * 64 + j, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : 0.f;
+    }
 #pragma unroll
   for (int e = 0; e < S::PER; ++e) {
     const int idx = tid + e * DT_THREADS;
+    float h = 0.f;
+#pragma unroll
+    for (int q = 0; q < S::MAXS; ++q)
+      if (q < P) h += pv[q][e];
     if (idx < entries) {
       const int row = idx / S::NCOL, j = idx - row * S::NCOL;
-      s_h[row * HS + j] = h[e] * pc.scale;
+      s_h[row * HS + j] = h * pc.scale;
     }
   }
 }
@@ -648,41 +721,13 @@ __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc,
   constexpr bool xkernel = XCH && MODE == MODE_FUSED;
   const bool xch = xkernel && A.xch_large;
   if (MODE != MODE_EXPAND) {
-    constexpr int NSTEP = xkernel ? 1 : (NRK <= 2 ? 2 : 1);
-    const int rt = w % ntp, kslice = w / ntp;
-    f32x4_t acc[NRK];
-#pragma unroll
-    for (int i = 0; i < NRK; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (rt < nrt) {
-      const int row = rt * 16 + c;
-      const bool vx = row < pc.rows;
-      const uint16_t* xr =
-          static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[row] : 0) * (size_t)A.ldx;
-      const uint16_t* ab =
-          static_cast<const uint16_t*>(A.a) + (size_t)pc.lora * A.R_pad * A.K_pad;
-      const int nch = (A.K + KSTEP - 1) / KSTEP;
-      // K steps of this workgroup (all of K, or its split's range), then of this K slice
-      const int k0 = xch ? pc.split * nch / pc.nsplit : 0;
-      const int k1 = xch ? (pc.split + 1) * nch / pc.nsplit : nch;
-      const int c0 = k0 + kslice * (k1 - k0) / ks, c1 = k0 + (kslice + 1) * (k1 - k0) / ks;
-      for (int ch = c0; ch < c1; ch += NSTEP) {
-        if constexpr (xkernel && NRK >= 3) {
-          shrink_step_halves<NRK, ALIGNED>(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g, acc);
-        } else {
-          ShrinkSteps<NRK, NSTEP, ALIGNED> S;
-          S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
-          S.mfma(acc);
-        }
-      }
-    }
-    store_wave_partial<NRK>(s_part, w, c, g, acc);
-    __syncthreads();
-    if (xch)
-      exchange_h<NRK, ALIGNED, true>(A, pc, G, s_tok, (A.K + KSTEP - 1) / KSTEP, s_part, s_h,
-                                     s_mask);
-    else
-      reduce_partials<NRK>(nrt, ntp, ks, pc.r, MODE == MODE_SHRINK ? 1.f : pc.scale, s_part,
-                           s_h);
+    const int nch = (A.K + KSTEP - 1) / KSTEP;
+    // K steps of this workgroup: all of K, or its split's range
+    const int k0 = xch ? pc.split * nch / pc.nsplit : 0;
+    const int k1 = xch ? (pc.split + 1) * nch / pc.nsplit : nch;
+    large_shrink<NRK, ALIGNED>(A, pc, nrt, s_tok, k0, k1,
+                               (MODE == MODE_FUSED && !xch) ? pc.scale : 1.f, s_part, s_h);
+    if (xch) exchange_h<NRK, ALIGNED, true>(A, pc, G, s_tok, nch, s_part, s_h, s_mask);
   }
   __syncthreads();
   if (MODE == MODE_SHRINK) return;
@@ -699,16 +744,22 @@ __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc,
     map_group<ALIGNED>(A, vl, cm);
     u32x4_t bq[NE][4];  // kept across the row tiles
     load_b_group<NE>(bb, A.N_pad, pc.r, vl, pc.v1, g, cm, bq);
-    for (int rt = 0; rt < nrt; ++rt) {
-      uint2 yv[4];
-      load_y<ALIGNED>(s_tok, pc.rows, rt, g, vl, pc.v1, cm, yv);
+    // old y of every row tile, loaded together with B (one memory round trip per group)
+    uint2 yv[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt < nrt) load_y<ALIGNED>(s_tok, pc.rows, rt, g, vl, pc.v1, cm, yv[rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt >= nrt) break;
       bf16x8_t P[NE][2];
       read_fragments<NE>(s_pf, rt, lane, P);
       f32x4_t yacc[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) yacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       expand_mfma<NE>(P, bq, yacc);
-      store_y<ALIGNED>(s_tok, pc.rows, rt, g, vl, pc.v1, cm, yv, yacc);
+      store_y<ALIGNED>(s_tok, pc.rows, rt, g, vl, pc.v1, cm, yv[rt], yacc);
     }
   }
 }

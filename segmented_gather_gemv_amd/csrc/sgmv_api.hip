@@ -101,11 +101,18 @@ void fill_common(const sgmv_pool* p, const sgmv_segments* seg, DeltaArgs& A) {
 // pieces, few enough that x rows and A are not re-read too often for prefill-like ones
 // (every split of a piece recomputes its shrink unless the K-split exchange is on, in which
 // case the splits share it and more of them pay). Caller overrides win.
-void choose_splits(int v_total, bool exchange, const sgmv_launch_opts* opts, DeltaArgs& A) {
+void choose_splits(int v_total, int M, int L, bool exchange, const sgmv_launch_opts* opts,
+                   DeltaArgs& A) {
   auto clamp = [](int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); };
   const int ps = clamp(v_total / 1024, 1, exchange ? SGMV_EXCHANGE_MAX_SPLITS : 16);
-  const int pl = exchange ? clamp(v_total / 1024, 1, SGMV_EXCHANGE_MAX_SPLITS_LARGE)
-                          : clamp(v_total / 2048, 1, 16);
+  int pl = clamp(v_total / 2048, 1, 16);
+  if (exchange) {
+    // large pieces are long-running: keep their workgroups within what is resident at once
+    // (two per CU); about M/64 pieces plus one ragged piece per segment
+    const int pieces = M / SGMV_TILE_ROWS + (L < 64 ? L : 64);
+    const int fit = (2 * 256) / (pieces > 0 ? pieces : 1);
+    pl = clamp(v_total / 1024, 1, clamp(fit, 2, SGMV_EXCHANGE_MAX_SPLITS_LARGE));
+  }
   A.n_split_small = (opts && opts->n_split_small > 0) ? opts->n_split_small : ps;
   A.n_split_large = (opts && opts->n_split_large > 0) ? opts->n_split_large : pl;
 }
@@ -194,7 +201,7 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
   } else {
     const bool xch = mode == MODE_FUSED && pool->dtype == SGMV_BF16 && seg->exchange &&
                      !(opts && opts->exchange < 0);
-    choose_splits(A.v_total, xch, opts, A);
+    choose_splits(A.v_total, M, pool->L, xch, opts, A);
   }
   if (mode == MODE_FUSED && pool->dtype == SGMV_BF16) choose_exchange(seg, opts, A);
   hipStream_t s = static_cast<hipStream_t>(stream);
