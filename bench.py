@@ -3,8 +3,11 @@
 
 One step = one pass of the whole hot path over one batch: the on-device segment build
 (counting sort of the tokens by adapter, work descriptors) followed by the fused delta
-y += scale * (x A^T) B^T, both through the libsgmv C-ABI on one HIP stream. Inputs are
-synthetic and already resident in HBM when the timed region starts.
+y += scale * (x A^T) B^T, both through the libsgmv C-ABI on one HIP stream. For bf16 batches
+of at most 512 tokens the step is one call of sgmv_lora_delta_ids, whose single launch does
+both (--step one, the default there); --step two times the builder launch and the delta
+launch as separate calls. Inputs are synthetic and already resident in HBM when the timed
+region starts.
 
 Default workload: decode, 256 tokens (one per sequence), d_in = d_out = 4096, rank 16, a pool
 of 64 adapters, bf16 with fp32 accumulation. The step cycles through several independent
@@ -14,9 +17,11 @@ cache.
 
 Timing: W untimed warm-up steps, then K steps between two device synchronisations
 (ms_per_step, value = tokens with an adapter per second). Inside the same timed region every
-eighth step's launches of the segment builder and of the delta kernel record a pair of HIP
-events as part of their own dispatch on the launch stream (start and end of the kernel, no
-extra stream packets); their averages give the per-launch durations used for the roofline.
+eighth step's kernel launches (the single build + delta kernel, or the builder and the
+delta kernel) record a pair of HIP events as part of their own dispatch on the launch stream
+(start and end of the kernel, no extra stream packets); their averages give the per-launch
+durations used for the roofline, which takes the kernel that does the delta (including the
+build it does itself in the single-launch step).
 Events on every launch would slow the host's launch path and lengthen the step. The roofline
 figure divides the algorithmic bytes of one delta launch (x rows and y rows read and written
 for every token with an adapter, each used adapter's true-rank A and B once, 12 bytes of
@@ -47,7 +52,8 @@ MALL_BYTES = 256 * 2 ** 20
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the fused delta kernel: byte-counter results are kept only while these match
 KERNEL_SOURCES = [os.path.join(ROOT, "segmented_gather_gemv_amd", "csrc", f)
-                  for f in ("delta_bf16.h", "delta_bf16_fused.hip", "common.h", "workspace.h")]
+                  for f in ("delta_bf16.h", "delta_bf16_fused.hip", "delta_bf16_build.hip",
+                            "common.h", "workspace.h", "segments_common.h")]
 
 
 def log(*a):
@@ -91,10 +97,15 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, launches_units: int):
+def traffic_path(workload: str, one_launch: bool) -> str:
+    entry = "sgmv_lora_delta_ids" if one_launch else "sgmv_lora_delta"
+    return os.path.join(PROFILES, f"{entry}_{workload}_traffic.json")
+
+
+def load_traffic(workload: str, one_launch: bool):
     """HBM bytes per delta launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
-    p = os.path.join(PROFILES, f"sgmv_lora_delta_{workload}_traffic.json")
+    p = traffic_path(workload, one_launch)
     if not os.path.exists(p):
         return None
     try:
@@ -123,7 +134,7 @@ def _counter_per_dispatch(csv_path: str, counter: str, name_part: str):
 
 def write_traffic(args):
     """Turn four rocprofv3 counter CSVs (delta FETCH_SIZE, delta WRITE_SIZE, copy FETCH_SIZE,
-    copy WRITE_SIZE) into profiles/sgmv_lora_delta_<workload>_traffic.json. The counters read
+    copy WRITE_SIZE) into profiles/<entry point>_<workload>_traffic.json. The counters read
     KiB per dispatch; each is scaled by bytes-moved / counter-reading of a plain device copy
     of known size measured the same way."""
     d_fetch, d_wr, c_fetch, c_wr = args.write_traffic
@@ -136,7 +147,8 @@ def write_traffic(args):
     w_scale = copy_bytes / cw_kib
     out = {
         "workload": args.workload,
-        "kernel": "delta_bf16_kernel<fused, aligned>",
+        "kernel": ("delta_bf16_kernel<fused, aligned, build>" if args.step == "one"
+                   else "delta_bf16_kernel<fused, aligned>"),
         "kernel_sha": kernel_source_sha(),
         "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
         "dispatches": [n1, n2],
@@ -144,7 +156,7 @@ def write_traffic(args):
         "fetch_bytes_per_kib": f_scale, "write_bytes_per_kib": w_scale,
         "hbm_bytes_per_launch": f_kib * f_scale + w_kib * w_scale,
     }
-    path = os.path.join(PROFILES, f"sgmv_lora_delta_{args.workload}_traffic.json")
+    path = traffic_path(args.workload, args.step == "one")
     json.dump(out, open(path, "w"), indent=1)
     print(json.dumps(out))
 
@@ -214,12 +226,18 @@ def main():
                     help="column splits per large piece (0: library choice)")
     ap.add_argument("--exchange", type=int, default=0, choices=[-1, 0, 1],
                     help="K-split exchange of small pieces: 0 library choice, 1 on, -1 off")
+    ap.add_argument("--step", default="auto", choices=["auto", "one", "two"],
+                    help="one: sgmv_lora_delta_ids (build inside the delta launch; bf16, "
+                         "M <= 512); two: builder launch + delta launch; auto: one where it "
+                         "applies")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain device copy of --copy-mib MiB (counter scale)")
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
                     help="delta FETCH, delta WRITE, copy FETCH, copy WRITE counter CSVs")
     args = ap.parse_args()
+    if args.write_traffic and args.step == "auto":
+        args.step = "one" if args.workload == "decode" else "two"
     if args.write_traffic:
         write_traffic(args)
         return
@@ -246,6 +264,11 @@ def main():
 
     w = workloads.get(args.workload)
     log(f"workload: {w.note}")
+    fits_one = w.dtype == torch.bfloat16 and 1 <= w.M <= 512
+    if args.step == "one" and not fits_one:
+        print("--step one needs a bf16 batch of 1..512 tokens", file=sys.stderr)
+        sys.exit(2)
+    one_launch = args.step == "one" or (args.step == "auto" and fits_one)
     elem = 2 if w.dtype == torch.bfloat16 else 4
     per_set = (w.a.numel() + w.b.numel() + w.x.numel() + w.y0.numel()) * elem
     n_sets = args.sets or max(2, min(64, -(-2 * MALL_BYTES // per_set)))
@@ -269,6 +292,7 @@ def main():
 
     s_handle = ctypes.c_void_p(stream.cuda_stream)
     build_fn, delta_fn = lib.sgmv_build_segments_ex, lib.sgmv_lora_delta_ex
+    ids_fn = lib.sgmv_lora_delta_ids_ex
     K = args.steps
     # per timed step: events the kernels' own dispatches record (start, end) -- no extra
     # packets in the stream
@@ -292,6 +316,8 @@ def main():
     def step(i, timed=False):
         bargs, dargs = calls[i % n_sets]
         sample = timed and i in evs
+        if one_launch:
+            return ids_fn(bargs[0], *dargs, opts_d[i].ref() if sample else plain.ref(), s_handle)
         rc = build_fn(*bargs, opts_b[i].ref() if sample else None, s_handle)
         rc |= delta_fn(*dargs, opts_d[i].ref() if sample else plain.ref(), s_handle)
         return rc
@@ -311,7 +337,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     assert rc == 0, f"library call failed with status {rc}"
-    build_ms = [ev.elapsed_ms(e[0], e[1]) for e in evs.values()]
+    build_ms = [0.0 if one_launch else ev.elapsed_ms(e[0], e[1]) for e in evs.values()]
     delta_ms = [ev.elapsed_ms(e[2], e[3]) for e in evs.values()]
     for e in evs.values():
         ev.destroy(e)
@@ -326,11 +352,13 @@ def main():
     b_avg = sum(build_ms) / n_ev / 1e3
     srt = sorted(delta_ms)
     achieved = alg_bytes / d_avg / 1e9
-    traffic = load_traffic(args.workload, 1)
-    log(f"step {wall / K * 1e6:.2f} us | delta kernel avg {d_avg * 1e6:.2f} us "
+    traffic = load_traffic(args.workload, one_launch)
+    kname = "build + delta kernel" if one_launch else "delta kernel"
+    log(f"step {wall / K * 1e6:.2f} us | {kname} avg {d_avg * 1e6:.2f} us "
         f"(p10 {srt[n_ev // 10] * 1e3:.2f}, p50 {srt[n_ev // 2] * 1e3:.2f}, "
         f"p90 {srt[9 * n_ev // 10] * 1e3:.2f}, {n_ev} sampled launches) "
-        f"| builder avg {b_avg * 1e6:.2f} us | {achieved:.0f} GB/s algorithmic "
+        f"| builder avg {'(inside)' if one_launch else f'{b_avg * 1e6:.2f} us'} "
+        f"| {achieved:.0f} GB/s algorithmic "
         f"({achieved / HBM_PEAK_GBPS * 100:.1f}% of peak) | {alg_flops / d_avg / 1e12:.2f} TFLOP/s")
 
     result = {
@@ -351,10 +379,11 @@ def main():
             "tokens_per_step": w.M,
             "lora_tokens_per_step": n_lora,
             "buffer_sets": n_sets,
-            "step": "device segment build + fused delta",
+            "step": ("segment build + fused delta in one launch (sgmv_lora_delta_ids)"
+                     if one_launch else "device segment build launch + fused delta launch"),
             "timed_launches_sampled": n_ev,
             "delta_kernel_us": d_avg * 1e6,
-            "builder_kernel_us": b_avg * 1e6,
+            "builder_kernel_us": None if one_launch else b_avg * 1e6,
             "algorithmic_bytes_per_launch": alg_bytes,
             "algorithmic_flops_per_launch": alg_flops,
         },

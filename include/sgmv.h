@@ -65,6 +65,8 @@ typedef enum { SGMV_F32 = 0, SGMV_BF16 = 1 } sgmv_dtype;
 #define SGMV_DEVICE_BUILDER_MAX_L 1024
 /* Most output slices one call writes (e.g. 3 for a fused q/k/v projection). */
 #define SGMV_MAX_SLICES 4
+/* Largest batch for which sgmv_lora_delta_ids builds the segments inside the delta launch. */
+#define SGMV_FUSED_BUILD_MAX_M 512
 
 /* ------------------------------------------------------------------------------------ *
  * Adapter pool (Fused-LoRA page Step 1; Ascend article 2.1 and 4.2).
@@ -222,6 +224,23 @@ sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_po
                             const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
                             void* stream);
 
+/* Segment build and fused delta in one call (Fused-LoRA page Step 1 and Ascend article 4.2
+ * for the grouping, Ascend article 4.3 for the delta): the same results, in `seg` and in y,
+ * as sgmv_build_segments(lora_indices, M, pool->L, seg->chunk_size, 1, seg, stream)
+ * followed by sgmv_lora_delta(x, ldx, M, pool, seg, out, n_slices, stream).
+ *   lora_indices  [M] int32 DEVICE array; a bad id counts as -1 and sets info[3] to
+ *                 SGMV_EBADID, as in the device builder.
+ * For a bf16 pool with 1 <= M <= SGMV_FUSED_BUILD_MAX_M and pool->L <=
+ * SGMV_DEVICE_BUILDER_MAX_L this is ONE launch: every workgroup groups the batch's tokens
+ * itself in LDS, and one of them also writes the arrays of `seg`, which no other workgroup
+ * of the launch reads. That launch leaves the exchange control words of seg->exchange as it
+ * finds them (every completed fused call leaves them consistent). Otherwise it issues the two
+ * launches. Never synchronises with the host.
+ * Errors: EINVAL; EUNSUPPORTED; EHIP. */
+sgmv_status sgmv_lora_delta_ids(const int32_t* lora_indices, const void* x, int64_t ldx,
+                                int32_t M, const sgmv_pool* pool, const sgmv_segments* seg,
+                                const sgmv_slice* out, int32_t n_slices, void* stream);
+
 /* ------------------------------------------------------------------------------------ *
  * Launch options (optional; NULL means library defaults). Shared by the _ex variants below,
  * which behave exactly like the calls without the suffix otherwise.
@@ -262,6 +281,11 @@ sgmv_status sgmv_expand_ex(const float* h, int64_t ldh, int32_t M, const sgmv_po
 sgmv_status sgmv_lora_delta_ex(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
                                const sgmv_segments* seg, const sgmv_slice* out,
                                int32_t n_slices, const sgmv_launch_opts* opts, void* stream);
+/* With two launches, start_event is recorded by the build and stop_event by the delta. */
+sgmv_status sgmv_lora_delta_ids_ex(const int32_t* lora_indices, const void* x, int64_t ldx,
+                                   int32_t M, const sgmv_pool* pool, const sgmv_segments* seg,
+                                   const sgmv_slice* out, int32_t n_slices,
+                                   const sgmv_launch_opts* opts, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* sgmv_status_string(sgmv_status s);

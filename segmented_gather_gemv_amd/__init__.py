@@ -37,8 +37,8 @@ DEVICE_BUILDER_MAX_L = 1024
 EXPORTED = [
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
-    "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_status_string",
-    "sgmv_version",
+    "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
+    "sgmv_lora_delta_ids_ex", "sgmv_status_string", "sgmv_version",
 ]
 
 
@@ -114,9 +114,14 @@ def _load():
     lib.sgmv_expand_ex.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, O, vp]
     lib.sgmv_lora_delta_ex.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, O,
                                        vp]
+    lib.sgmv_lora_delta_ids.argtypes = [vp, vp, i64, i32, P(_Pool), P(_Segments), P(_Slice),
+                                        i32, vp]
+    lib.sgmv_lora_delta_ids_ex.argtypes = [vp, vp, i64, i32, P(_Pool), P(_Segments), P(_Slice),
+                                           i32, O, vp]
     for f in ["sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
               "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
-              "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex"]:
+              "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
+              "sgmv_lora_delta_ids_ex"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.sgmv_status_string.argtypes = [ctypes.c_int]
     lib.sgmv_status_string.restype = ctypes.c_char_p
@@ -400,8 +405,24 @@ def sgmv_lora_delta(x: torch.Tensor, pool: Pool, seg: Segments,
                                    _stream(x.device)), "sgmv_lora_delta")
 
 
+def sgmv_lora_delta_ids(ids: torch.Tensor, x: torch.Tensor, pool: Pool, seg: Segments,
+                        y: Union[torch.Tensor, Sequence[SliceSpec]],
+                        opts: Optional[LaunchOpts] = None) -> None:
+    """Build ``seg`` from the device ids and apply the fused delta, as sgmv_build_segments
+    (on device) followed by sgmv_lora_delta; a single launch for small bf16 batches."""
+    _check_x(x, pool)
+    M = x.shape[0]
+    if ids.dtype != torch.int32 or ids.device != x.device or ids.numel() != M:
+        raise TypeError("ids must be an int32 tensor of M entries on x's device")
+    ids = ids.contiguous()
+    arr, n = _slices(y, pool, M)
+    _check(_lib.sgmv_lora_delta_ids_ex(_ptr(ids), _ptr(x), x.stride(0), M,
+                                       ctypes.byref(pool.desc), ctypes.byref(seg.desc), arr, n,
+                                       _opts(opts), _stream(x.device)), "sgmv_lora_delta_ids")
+
+
 __all__ = [
     "LIB_PATH", "EXPORTED", "SgmvError", "Pool", "Segments", "LaunchOpts", "library",
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_alloc", "sgmv_build_segments",
-    "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta",
+    "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_lora_delta_ids",
 ]

@@ -79,6 +79,11 @@ struct DeltaArgs {
   int32_t xch_small, xch_large;  // nonzero: that piece class splits its shrink over K
   int32_t xwait;                 // small pieces' wait bound in 10 ns ticks; < 0: no wait
   int32_t xwait_large;
+  // fused build + delta launch: per-token adapter ids, and the segment arrays that workgroup 0
+  // writes as the device builder would
+  const int32_t* ids;
+  int32_t M, chunk, seg_cap;
+  int32_t *w_sorted, *w_indptr, *w_seg_lora, *w_tiles, *w_info;
   SliceArg slices[SGMV_MAX_SLICES];
 };
 

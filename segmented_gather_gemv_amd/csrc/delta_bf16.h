@@ -36,6 +36,7 @@
 #pragma once
 
 #include "common.h"
+#include "segments_common.h"
 
 namespace sgmv {
 
@@ -794,9 +795,10 @@ __device__ __forceinline__ void run_piece(const DeltaArgs& A, const Piece& pc, b
   }
 }
 
-// Pieces of rank tiles up to NRKM (ranks up to 16 NRKM); XCH: small pieces of fused calls
-// split their shrink over K with the other column splits of the piece.
-template <int MODE, bool ALIGNED, int NRKM, bool XCH>
+// Pieces of rank tiles up to NRKM (ranks up to 16 NRKM); XCH: pieces of fused calls split
+// their shrink over K with the other column splits of the piece; BUILD: every workgroup
+// first builds the segments of the batch itself (fused build + delta, M <= 512).
+template <int MODE, bool ALIGNED, int NRKM, bool XCH, bool BUILD>
 __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH ? 4 : 1))) void delta_bf16_kernel(DeltaArgs A) {
   __shared__ int s_tok[SGMV_TILE_ROWS];
   __shared__ __align__(16) float s_h[SGMV_TILE_ROWS * HS];
@@ -813,25 +815,46 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
   int tile, p, P;
   if (!locate_piece(A, split, small, tile, p, P)) return;
 
-  // ---- one round of loads: counts, the piece record, its tokens, the rank/scale table ----
   const int tid = threadIdx.x;
-  const int32_t* rec = A.tiles + (size_t)(small ? A.large_cap + tile : tile) * SGMV_TILE_INTS;
-  const int count = A.info[small ? 2 : 1];
-  Piece pc;
-  pc.lora = rec[0];
-  pc.start = rec[1];
-  pc.rows = rec[2];
   const bool table = A.L <= RANK_TABLE_MAX;
-  if (small && tid < SGMV_SMALL_ROWS) s_tok[tid] = rec[16 + tid];
-  if (table) {
-    for (int i = tid; i < A.L; i += DT_THREADS) {
-      s_rank[i] = A.rank[i];
-      s_scale[i] = A.scale[i];
+  Piece pc;
+  if constexpr (BUILD) {
+    // ---- the batch's segments, built here; the rank/scale table loads overlap the ids' ----
+    static_assert(DT_THREADS == FUSED_BUILD_WAVES * WAVE, "one token per thread");
+    if (table) {
+      for (int i = tid; i < A.L; i += DT_THREADS) {
+        s_rank[i] = A.rank[i];
+        s_scale[i] = A.scale[i];
+      }
     }
+    const WgBuildDst dst{A.w_sorted, A.w_indptr, A.w_seg_lora, A.w_tiles, A.w_info,
+                         A.seg_cap, A.large_cap, A.small_cap};
+    const WgBuildLds S = wg_build_lds(reinterpret_cast<unsigned char*>(s_part), A.L);
+    const WgBuildOut bo =
+        wg_build(A.ids, A.M, A.L, A.chunk, small, tile, blockIdx.x == 0, dst, S, s_tok);
+    if (tile >= (small ? bo.n_small : bo.n_large)) return;  // uniform across the workgroup
+    pc.lora = S.rec[0];
+    pc.start = S.rec[1];
+    pc.rows = S.rec[2];
+    __syncthreads();  // the build scratch aliases s_part, and the table is in LDS
+  } else {
+    // ---- one round of loads: counts, the piece record, its tokens, the rank/scale table ----
+    const int32_t* rec = A.tiles + (size_t)(small ? A.large_cap + tile : tile) * SGMV_TILE_INTS;
+    const int count = A.info[small ? 2 : 1];
+    pc.lora = rec[0];
+    pc.start = rec[1];
+    pc.rows = rec[2];
+    if (small && tid < SGMV_SMALL_ROWS) s_tok[tid] = rec[16 + tid];
+    if (table) {
+      for (int i = tid; i < A.L; i += DT_THREADS) {
+        s_rank[i] = A.rank[i];
+        s_scale[i] = A.scale[i];
+      }
+    }
+    if (tile >= count) return;  // uniform across the workgroup
+    if (!small && tid < pc.rows) s_tok[tid] = A.sorted[pc.start + tid];
+    __syncthreads();
   }
-  if (tile >= count) return;  // uniform across the workgroup
-  if (!small && tid < pc.rows) s_tok[tid] = A.sorted[pc.start + tid];
-  __syncthreads();
   pc.r = table ? s_rank[pc.lora] : A.rank[pc.lora];
   pc.scale = table ? s_scale[pc.lora] : A.scale[pc.lora];
   const int width = (((A.v_total + P - 1) / P) + 63) & ~63;
@@ -867,13 +890,14 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
 
 
 // Grid and dynamic LDS of a launch; the kernel arguments get the class boundary.
-inline void delta_geometry(int mode, DeltaArgs& A, int& grid, size_t& lds) {
+inline void delta_geometry(int mode, DeltaArgs& A, int& grid, size_t& lds, bool build = false) {
   const bool split = mode != MODE_SHRINK;
   A.grid_large = class_grid(A.large_cap, split ? A.n_split_large : 1);
   grid = A.grid_large + class_grid(A.small_cap, split ? A.n_split_small : 1);
   // partial tiles of every wave (8 waves x R_pad/16 rank tiles x 1 KB); large pieces reuse
   // them for their h fragments, which fit for every rank
   lds = (size_t)DT_WAVES * (A.R_pad / 16) * 256 * sizeof(float);
+  if (build && wg_build_lds_bytes(A.L) > lds) lds = wg_build_lds_bytes(A.L);  // aliases s_part
 }
 
 }  // namespace sgmv

@@ -1,0 +1,34 @@
+// Fused build + delta: instantiations of the bf16 delta kernel whose workgroups first build
+// the batch's segments themselves (M <= 512), so a decode step needs a single launch.
+#include "delta_bf16.h"
+
+namespace sgmv {
+
+hipError_t launch_delta_bf16_build(bool aligned, DeltaArgs A, LaunchEvents ev,
+                                   hipStream_t stream) {
+  int grid;
+  size_t lds;
+  delta_geometry(MODE_FUSED, A, grid, lds, true);
+  if (grid <= 0) return hipSuccess;
+  const dim3 g(grid), b(DT_THREADS);
+  const int nrkm = A.R_pad / 16;
+  const bool x = A.xch_small != 0 || A.xch_large != 0;
+#define SGMV_LAUNCH(AL_, NR_, X_)                                                              \
+  hipExtLaunchKernelGGL((delta_bf16_kernel<MODE_FUSED, AL_, NR_, X_, true>), g, b, lds, stream, \
+                        ev.start, ev.stop, 0, A)
+  if (aligned) {
+    if (nrkm == 1) {
+      if (x) SGMV_LAUNCH(true, 1, true); else SGMV_LAUNCH(true, 1, false);
+    } else if (nrkm == 2) {
+      if (x) SGMV_LAUNCH(true, 2, true); else SGMV_LAUNCH(true, 2, false);
+    } else {
+      if (x) SGMV_LAUNCH(true, 4, true); else SGMV_LAUNCH(true, 4, false);
+    }
+  } else {
+    if (x) SGMV_LAUNCH(false, 4, true); else SGMV_LAUNCH(false, 4, false);
+  }
+#undef SGMV_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace sgmv

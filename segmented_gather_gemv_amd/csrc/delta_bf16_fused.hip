@@ -19,7 +19,7 @@ hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, LaunchEvents e
   const int nrkm = A.R_pad / 16;
   const bool x = A.xch_small != 0 || A.xch_large != 0;
 #define SGMV_LAUNCH(AL_, NR_, X_)                                                              \
-  hipExtLaunchKernelGGL((delta_bf16_kernel<MODE_FUSED, AL_, NR_, X_>), g, b, lds, stream,     \
+  hipExtLaunchKernelGGL((delta_bf16_kernel<MODE_FUSED, AL_, NR_, X_, false>), g, b, lds, stream,     \
                         ev.start, ev.stop, 0, A)
   if (aligned) {
     if (nrkm == 1) {

@@ -11,7 +11,7 @@ hipError_t launch_delta_bf16_unfused(int mode, bool aligned, DeltaArgs A, Launch
   if (grid <= 0) return hipSuccess;
   const dim3 g(grid), b(DT_THREADS);
 #define SGMV_LAUNCH(M_, AL_)                                                                  \
-  hipExtLaunchKernelGGL((delta_bf16_kernel<M_, AL_, 4, false>), g, b, lds, stream, ev.start, \
+  hipExtLaunchKernelGGL((delta_bf16_kernel<M_, AL_, 4, false, false>), g, b, lds, stream, ev.start, \
                         ev.stop, 0, A)
   if (mode == MODE_SHRINK) {
     if (aligned) SGMV_LAUNCH(MODE_SHRINK, true); else SGMV_LAUNCH(MODE_SHRINK, false);

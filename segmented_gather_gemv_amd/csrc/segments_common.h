@@ -1,0 +1,350 @@
+// Device helpers shared by the segment builders and the fused build + delta launch: the
+// workgroup scan, per-wave key counts, descriptor counts of a segment, descriptor records and
+// token slots, and the position of a piece inside its bucket. The counting sort itself is
+// described in segments_device.hip.
+#pragma once
+
+#include "common.h"
+
+namespace sgmv {
+
+constexpr int BUILD_THREADS = 1024;
+constexpr int BUILD_WAVES = BUILD_THREADS / WAVE;
+
+__host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
+
+// Inclusive scan across the 64 lanes of a wave with DPP row shifts and row broadcasts.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Exclusive scan of NV ints per thread across a workgroup of NW waves. s_w holds NV * NW
+// ints. Contains barriers: call from all threads.
+template <int NV, int NW = BUILD_WAVES>
+__device__ void block_scan(const int (&v)[NV], int (&ex)[NV], int (&tot)[NV], int* s_w) {
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  int x[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    x[i] = wave_incl_scan(v[i]);
+    if (lane == WAVE - 1) s_w[i * NW + w] = x[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int4* q = reinterpret_cast<const int4*>(s_w + i * NW);
+    int before = 0, all = 0;
+#pragma unroll
+    for (int j = 0; j < NW / 4; ++j) {
+      const int4 s = q[j];
+      const int vals[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        all += vals[e];
+        before += (4 * j + e < w) ? vals[e] : 0;
+      }
+    }
+    ex[i] = before + x[i] - v[i];
+    tot[i] = all;
+  }
+  __syncthreads();
+}
+
+// Counts of equal keys in lower waves (pre), in this wave (cw) and in higher waves (post),
+// from the per-(key, wave) byte table of a workgroup of NW waves.
+template <int NW = BUILD_WAVES>
+__device__ __forceinline__ void wave_counts(const uint8_t* rc, int key, int& pre, int& cw,
+                                            int& post) {
+  const int w = threadIdx.x / WAVE;
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(rc + key * NW);
+  pre = cw = post = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int v = (q[i >> 2] >> (8 * (i & 3))) & 0xff;
+    if (i < w) pre += v;
+    else if (i == w) cw = v;
+    else post += v;
+  }
+}
+
+// Descriptor counts of one segment of `len` rows.
+__device__ __forceinline__ void piece_tiles(int len, int& nl, int& ns) {
+  const int rem = len % SGMV_TILE_ROWS;
+  nl = len / SGMV_TILE_ROWS + (rem > SGMV_SMALL_ROWS ? 1 : 0);
+  ns = (rem > 0 && rem <= SGMV_SMALL_ROWS) ? 1 : 0;
+}
+
+// Writes the descriptors of one bucket (adapter `lora`, `cnt` rows from sorted row `start`,
+// chunk size C) and its segments. Token slots of small descriptors are left to the tokens'
+// own threads (token_slot); every other token slot gets -1.
+__device__ void write_bucket(int lora, int cnt, int C, int start, int seg0, int lt, int st,
+                             int32_t* indptr, int32_t* seg_lora, int32_t* tiles, int seg_cap,
+                             int large_cap, int small_cap) {
+  const int np = C > 0 ? (cnt + C - 1) / C : 1;
+  for (int i = 0; i < np; ++i) {
+    const int seg = seg0 + i;
+    const int s0 = start + (C > 0 ? i * C : 0);
+    const int len = C > 0 ? min(C, cnt - i * C) : cnt;
+    if (seg < seg_cap) {
+      indptr[seg] = s0;
+      seg_lora[seg] = lora;
+    }
+    for (int r0 = 0; r0 < len; r0 += SGMV_TILE_ROWS) {
+      const int rows = min(SGMV_TILE_ROWS, len - r0);
+      const bool small = rows <= SGMV_SMALL_ROWS;
+      const int idx = small ? st++ : lt++;
+      if (small ? idx >= small_cap : idx >= large_cap) continue;
+      int4* d = reinterpret_cast<int4*>(tiles + (size_t)(small ? large_cap + idx : idx) *
+                                                    SGMV_TILE_INTS);
+      d[0] = make_int4(lora, s0 + r0, rows, seg);
+      d[1] = d[2] = d[3] = make_int4(0, 0, 0, 0);
+      // token slots past the piece's rows; the others belong to the tokens' own threads
+      const int first_free = small ? rows : 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * q >= first_free) {
+          d[4 + q] = make_int4(-1, -1, -1, -1);
+        } else if (4 * q + 4 > first_free) {
+          int32_t* e = reinterpret_cast<int32_t*>(d + 4 + q);
+          for (int i = first_free - 4 * q; i < 4; ++i) e[i] = -1;
+        }
+      }
+    }
+  }
+}
+
+// The token with in-bucket rank `rank` of a bucket of `cnt` rows whose first small
+// descriptor is `sbase`: if it lands in a small descriptor, store its id in that record.
+__device__ __forceinline__ void token_slot(int t, int rank, int cnt, int C, int sbase,
+                                           int32_t* tiles, int large_cap, int small_cap) {
+  const int i = C > 0 ? rank / C : 0;                  // segment (chunk) inside the bucket
+  const int in_seg = C > 0 ? rank - i * C : rank;
+  const int len = C > 0 ? min(C, cnt - i * C) : cnt;
+  const int piece = in_seg / SGMV_TILE_ROWS;
+  const int rows = min(SGMV_TILE_ROWS, len - piece * SGMV_TILE_ROWS);
+  if (rows > SGMV_SMALL_ROWS) return;
+  int nl_full, ns_full;
+  piece_tiles(C > 0 ? C : cnt, nl_full, ns_full);
+  const int sidx = sbase + (C > 0 ? i * ns_full : 0);  // one small piece at most per segment
+  const int slot = in_seg - piece * SGMV_TILE_ROWS;
+  if (sidx < small_cap && slot < SGMV_SMALL_ROWS)
+    tiles[(size_t)(large_cap + sidx) * SGMV_TILE_INTS + 16 + slot] = t;
+}
+
+// Largest b in [0, n) with a[b] <= x, for a non-decreasing a with a[0] <= x.
+__device__ __forceinline__ int last_at_most(const int* a, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// First sorted row, rows and segment of one piece of a bucket of cnt rows that starts at
+// sorted row `start` and segment `seg0` (chunk size C, 0 = no chunks). Pieces are numbered
+// chunk by chunk, then by row within a chunk; every chunk holds at most one small piece.
+struct PieceDesc {
+  int start, rows, seg;
+};
+
+// li-th large piece (17..64 rows) of the bucket.
+__device__ __forceinline__ PieceDesc large_piece_desc(int li, int C, int cnt, int start,
+                                                      int seg0) {
+  int chunk = 0, p = li;
+  if (C > 0) {
+    const int np = (cnt + C - 1) / C;
+    int nlf, nsf;
+    piece_tiles(C, nlf, nsf);  // large pieces of every chunk but the last
+    if (nlf > 0 && li < (np - 1) * nlf) {
+      chunk = li / nlf;
+      p = li - chunk * nlf;
+    } else {
+      chunk = np - 1;
+      p = li - (np - 1) * nlf;
+    }
+  }
+  const int len = C > 0 ? min(C, cnt - chunk * C) : cnt;
+  const int r0 = SGMV_TILE_ROWS * p;
+  return PieceDesc{start + (C > 0 ? chunk * C : 0) + r0, min(SGMV_TILE_ROWS, len - r0),
+                   seg0 + chunk};
+}
+
+// si-th small piece (1..16 rows) of the bucket: the tail of a chunk.
+__device__ __forceinline__ PieceDesc small_piece_desc(int si, int C, int cnt, int start,
+                                                      int seg0) {
+  int chunk = 0;
+  if (C > 0) {
+    int nlf, nsf;
+    piece_tiles(C, nlf, nsf);  // nsf: whether every full chunk ends in a small piece
+    chunk = nsf ? si : (cnt + C - 1) / C - 1;
+  }
+  const int len = C > 0 ? min(C, cnt - chunk * C) : cnt;
+  const int r0 = SGMV_TILE_ROWS * (len / SGMV_TILE_ROWS);
+  return PieceDesc{start + (C > 0 ? chunk * C : 0) + r0, len - r0, seg0 + chunk};
+}
+
+
+// ---------------------------------------------------------------------------------------
+// In-workgroup segment build for the fused build + delta launch
+// ---------------------------------------------------------------------------------------
+// A workgroup of 8 waves, one token per thread (M <= 512), ranks the adapter ids exactly as
+// the device builder does (buckets in order of first appearance, tokens ascending inside a
+// bucket, ids -1 and bad ids last): every workgroup of the launch does it, then takes its own
+// descriptor from the result without any global round trip. The `writer` workgroup also
+// writes the segment arrays, records and info exactly as the builder does, so that later
+// calls can use them.
+constexpr int FUSED_BUILD_WAVES = 8;
+constexpr int FUSED_BUILD_MAX_M = FUSED_BUILD_WAVES * WAVE;
+static_assert(FUSED_BUILD_MAX_M == SGMV_FUSED_BUILD_MAX_M, "one token per thread");
+
+struct WgBuildLds {
+  uint8_t* rc;  // [L + 1][8] per-(key, wave) counts
+  int* base;    // [L + 1] first sorted row of each bucket (L: the tail)
+  int* sbase;   // [L + 1] first small descriptor of each bucket
+  int* w;       // [6 * 8] workgroup scan scratch
+  int* rec;     // [4] this workgroup's descriptor: adapter, first row, rows, segment
+};
+
+inline size_t wg_build_lds_bytes(int L) {
+  const size_t nk = (size_t)L + 1;
+  return align16(nk * FUSED_BUILD_WAVES) + 2 * align16(nk * sizeof(int)) +
+         align16(6 * FUSED_BUILD_WAVES * sizeof(int)) + 16;
+}
+
+__device__ __forceinline__ WgBuildLds wg_build_lds(unsigned char* p, int L) {
+  const size_t nk = (size_t)L + 1;
+  WgBuildLds s;
+  s.rc = p;
+  p += align16(nk * FUSED_BUILD_WAVES);
+  s.base = reinterpret_cast<int*>(p);
+  p += align16(nk * sizeof(int));
+  s.sbase = reinterpret_cast<int*>(p);
+  p += align16(nk * sizeof(int));
+  s.w = reinterpret_cast<int*>(p);
+  p += align16(6 * FUSED_BUILD_WAVES * sizeof(int));
+  s.rec = reinterpret_cast<int*>(p);
+  return s;
+}
+
+struct WgBuildOut {
+  int n_large, n_small;  // 0 when an array would overflow
+};
+
+struct WgBuildDst {  // the builder's outputs, written by the writer workgroup only
+  int32_t *sorted, *indptr, *seg_lora, *tiles, *info;
+  int seg_cap, large_cap, small_cap;
+};
+
+// Call from all 512 threads. For descriptor `tile` of class `small`, leaves its record in
+// S.rec and its token ids in s_tok (when the descriptor exists).
+__device__ WgBuildOut wg_build(const int32_t* ids, int M, int L, int C, bool small, int tile,
+                               bool writer, const WgBuildDst& D, const WgBuildLds& S,
+                               int* s_tok) {
+  constexpr int NW = FUSED_BUILD_WAVES;
+  const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+  const int NK = L + 1;
+  const bool valid = t < M;
+  for (int i = t; i < NK * (NW / 4); i += NW * WAVE) reinterpret_cast<uint32_t*>(S.rc)[i] = 0;
+  int key = -2;  // never equal to a real key (0..L)
+  bool bad = false;
+  if (valid) {
+    int id = ids[t];
+    if (id < -1 || id >= L) {
+      bad = true;
+      id = -1;
+    }
+    key = id < 0 ? L : id;
+  }
+  // rank among equal keys of lower lanes, and the count in this wave: lane j keeps the
+  // ballot of the lanes holding its key
+  uint64_t same = 0;
+  if (w * WAVE < M) {
+#pragma unroll
+    for (int j = 0; j < WAVE; ++j) {
+      const uint64_t m = __ballot(key == __builtin_amdgcn_readlane(key, j));
+      same = lane == j ? m : same;
+    }
+  }
+  const int rk = __popcll(same & lanemask_lt(lane));
+  const int cw = __popcll(same);
+  __syncthreads();
+  if (valid && rk == 0) S.rc[key * NW + w] = (uint8_t)cw;
+  __syncthreads();
+  int pre = 0, cwt = 0, post = 0;
+  if (valid) wave_counts<NW>(S.rc, key, pre, cwt, post);
+  const int rank = pre + rk;
+  const int cnt = pre + cwt + post;
+  const bool first = valid && key < L && rank == 0;
+  int v[6] = {0, 0, 0, 0, 0, bad ? 1 : 0};
+  if (first) {
+    const int np = C > 0 ? (cnt + C - 1) / C : 1;
+    const int last = C > 0 ? cnt - C * (np - 1) : cnt;
+    int nl, ns, nl1, ns1;
+    piece_tiles(C > 0 ? C : cnt, nl, ns);
+    piece_tiles(last, nl1, ns1);
+    v[0] = 1;
+    v[1] = cnt;
+    v[2] = np;
+    v[3] = (np - 1) * nl + nl1;
+    v[4] = (np - 1) * ns + ns1;
+  }
+  int ex[6], tot[6];
+  block_scan<6, NW>(v, ex, tot, S.w);
+  const int n_lora = tot[1], n_seg = tot[2], n_large = tot[3], n_small = tot[4];
+  const bool overflow = n_seg > D.seg_cap || n_large > D.large_cap || n_small > D.small_cap;
+  if (first) {
+    S.base[key] = ex[1];
+    S.sbase[key] = ex[4];
+    if (!overflow) {
+      // this workgroup's descriptor, if it belongs to this bucket
+      const int first_d = small ? ex[4] : ex[3], nd = small ? v[4] : v[3];
+      if (tile >= first_d && tile < first_d + nd) {
+        const PieceDesc pd = small ? small_piece_desc(tile - first_d, C, cnt, ex[1], ex[2])
+                                   : large_piece_desc(tile - first_d, C, cnt, ex[1], ex[2]);
+        S.rec[0] = key;
+        S.rec[1] = pd.start;
+        S.rec[2] = pd.rows;
+        S.rec[3] = pd.seg;
+      }
+      if (writer)
+        write_bucket(key, cnt, C, ex[1], ex[2], ex[3], ex[4], D.indptr, D.seg_lora, D.tiles,
+                     D.seg_cap, D.large_cap, D.small_cap);
+    }
+  }
+  if (t == 0) {
+    S.base[L] = n_lora;
+    if (writer) {
+      if (!overflow) D.indptr[n_seg] = n_lora;
+      D.info[0] = overflow ? 0 : n_seg;
+      D.info[1] = overflow ? 0 : n_large;
+      D.info[2] = overflow ? 0 : n_small;
+      D.info[3] = overflow ? SGMV_ECAPACITY : (tot[5] > 0 ? SGMV_EBADID : SGMV_OK);
+    }
+  }
+  __syncthreads();
+  WgBuildOut out;
+  out.n_large = overflow ? 0 : n_large;
+  out.n_small = overflow ? 0 : n_small;
+  const bool mine = tile < (small ? out.n_small : out.n_large);
+  if (valid) {
+    const int pos = S.base[key] + rank;
+    if (mine && key < L && pos >= S.rec[1] && pos < S.rec[1] + S.rec[2]) s_tok[pos - S.rec[1]] = t;
+    if (writer) {
+      if (pos < M) D.sorted[pos] = t;
+      if (key < L && !overflow)
+        token_slot(t, rank, cnt, C, S.sbase[key], D.tiles, D.large_cap, D.small_cap);
+    }
+  }
+  __syncthreads();
+  return out;
+}
+
+}  // namespace sgmv

@@ -20,138 +20,9 @@
 // control words of the fused call's exchange workspace, when the segments carry one.
 #include <climits>
 
-#include "common.h"
+#include "segments_common.h"
 
 namespace sgmv {
-
-constexpr int BUILD_THREADS = 1024;
-constexpr int BUILD_WAVES = BUILD_THREADS / WAVE;
-
-__host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
-
-// Inclusive scan across the 64 lanes of a wave with DPP row shifts and row broadcasts.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
-
-// Exclusive scan of NV ints per thread across a workgroup of NW waves. s_w holds NV * NW
-// ints. Contains barriers: call from all threads.
-template <int NV, int NW = BUILD_WAVES>
-__device__ void block_scan(const int (&v)[NV], int (&ex)[NV], int (&tot)[NV], int* s_w) {
-  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  int x[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    x[i] = wave_incl_scan(v[i]);
-    if (lane == WAVE - 1) s_w[i * NW + w] = x[i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int4* q = reinterpret_cast<const int4*>(s_w + i * NW);
-    int before = 0, all = 0;
-#pragma unroll
-    for (int j = 0; j < NW / 4; ++j) {
-      const int4 s = q[j];
-      const int vals[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        all += vals[e];
-        before += (4 * j + e < w) ? vals[e] : 0;
-      }
-    }
-    ex[i] = before + x[i] - v[i];
-    tot[i] = all;
-  }
-  __syncthreads();
-}
-
-// Counts of equal keys in lower waves (pre), in this wave (cw) and in higher waves (post),
-// from the per-(key, wave) byte table of a workgroup of NW waves.
-template <int NW = BUILD_WAVES>
-__device__ __forceinline__ void wave_counts(const uint8_t* rc, int key, int& pre, int& cw,
-                                            int& post) {
-  const int w = threadIdx.x / WAVE;
-  const uint32_t* q = reinterpret_cast<const uint32_t*>(rc + key * NW);
-  pre = cw = post = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int v = (q[i >> 2] >> (8 * (i & 3))) & 0xff;
-    if (i < w) pre += v;
-    else if (i == w) cw = v;
-    else post += v;
-  }
-}
-
-// Descriptor counts of one segment of `len` rows.
-__device__ __forceinline__ void piece_tiles(int len, int& nl, int& ns) {
-  const int rem = len % SGMV_TILE_ROWS;
-  nl = len / SGMV_TILE_ROWS + (rem > SGMV_SMALL_ROWS ? 1 : 0);
-  ns = (rem > 0 && rem <= SGMV_SMALL_ROWS) ? 1 : 0;
-}
-
-// Writes the descriptors of one bucket (adapter `lora`, `cnt` rows from sorted row `start`,
-// chunk size C) and its segments. Token slots of small descriptors are left to the tokens'
-// own threads (token_slot); every other token slot gets -1.
-__device__ void write_bucket(int lora, int cnt, int C, int start, int seg0, int lt, int st,
-                             int32_t* indptr, int32_t* seg_lora, int32_t* tiles, int seg_cap,
-                             int large_cap, int small_cap) {
-  const int np = C > 0 ? (cnt + C - 1) / C : 1;
-  for (int i = 0; i < np; ++i) {
-    const int seg = seg0 + i;
-    const int s0 = start + (C > 0 ? i * C : 0);
-    const int len = C > 0 ? min(C, cnt - i * C) : cnt;
-    if (seg < seg_cap) {
-      indptr[seg] = s0;
-      seg_lora[seg] = lora;
-    }
-    for (int r0 = 0; r0 < len; r0 += SGMV_TILE_ROWS) {
-      const int rows = min(SGMV_TILE_ROWS, len - r0);
-      const bool small = rows <= SGMV_SMALL_ROWS;
-      const int idx = small ? st++ : lt++;
-      if (small ? idx >= small_cap : idx >= large_cap) continue;
-      int4* d = reinterpret_cast<int4*>(tiles + (size_t)(small ? large_cap + idx : idx) *
-                                                    SGMV_TILE_INTS);
-      d[0] = make_int4(lora, s0 + r0, rows, seg);
-      d[1] = d[2] = d[3] = make_int4(0, 0, 0, 0);
-      // token slots past the piece's rows; the others belong to the tokens' own threads
-      const int first_free = small ? rows : 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (4 * q >= first_free) {
-          d[4 + q] = make_int4(-1, -1, -1, -1);
-        } else if (4 * q + 4 > first_free) {
-          int32_t* e = reinterpret_cast<int32_t*>(d + 4 + q);
-          for (int i = first_free - 4 * q; i < 4; ++i) e[i] = -1;
-        }
-      }
-    }
-  }
-}
-
-// The token with in-bucket rank `rank` of a bucket of `cnt` rows whose first small
-// descriptor is `sbase`: if it lands in a small descriptor, store its id in that record.
-__device__ __forceinline__ void token_slot(int t, int rank, int cnt, int C, int sbase,
-                                           int32_t* tiles, int large_cap, int small_cap) {
-  const int i = C > 0 ? rank / C : 0;                  // segment (chunk) inside the bucket
-  const int in_seg = C > 0 ? rank - i * C : rank;
-  const int len = C > 0 ? min(C, cnt - i * C) : cnt;
-  const int piece = in_seg / SGMV_TILE_ROWS;
-  const int rows = min(SGMV_TILE_ROWS, len - piece * SGMV_TILE_ROWS);
-  if (rows > SGMV_SMALL_ROWS) return;
-  int nl_full, ns_full;
-  piece_tiles(C > 0 ? C : cnt, nl_full, ns_full);
-  const int sidx = sbase + (C > 0 ? i * ns_full : 0);  // one small piece at most per segment
-  const int slot = in_seg - piece * SGMV_TILE_ROWS;
-  if (sidx < small_cap && slot < SGMV_SMALL_ROWS)
-    tiles[(size_t)(large_cap + sidx) * SGMV_TILE_INTS + 16 + slot] = t;
-}
 
 // ---------------------------------------------------------------------------------------
 // small batches: M <= 1024
@@ -522,69 +393,6 @@ __device__ __forceinline__ void group_lanes(bool valid, int key, int* s_k, int& 
   }
 }
 
-// Largest b in [0, n) with a[b] <= x, for a non-decreasing a with a[0] <= x.
-__device__ __forceinline__ int last_at_most(const int* a, int n, int x) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a[mid] <= x) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
-// First sorted row, rows and segment of a bucket's piece (chunk size C, 0 = no chunks),
-// in the order the pieces are numbered: chunk by chunk, then by row within a chunk.
-struct PieceDesc {
-  int start, rows, seg;
-};
-
-__device__ __forceinline__ PieceDesc piece_at(int b, int chunk, int r0, const int* bstart,
-                                              const int* pstart, int C, int rows) {
-  PieceDesc d;
-  d.start = bstart[b] + (C > 0 ? chunk * C : 0) + r0;
-  d.rows = rows;
-  d.seg = pstart[b] + chunk;
-  return d;
-}
-
-// li-th large piece (17..64 rows) of bucket b.
-__device__ __forceinline__ PieceDesc large_piece_desc(int b, int li, int C, const int* bstart,
-                                                      const int* pstart) {
-  const int cnt = bstart[b + 1] - bstart[b];
-  int chunk = 0, p = li;
-  if (C > 0) {
-    const int np = (cnt + C - 1) / C;
-    int nlf, nsf;
-    piece_tiles(C, nlf, nsf);  // large pieces of every chunk but the last
-    if (nlf > 0 && li < (np - 1) * nlf) {
-      chunk = li / nlf;
-      p = li - chunk * nlf;
-    } else {
-      chunk = np - 1;
-      p = li - (np - 1) * nlf;
-    }
-  }
-  const int len = C > 0 ? min(C, cnt - chunk * C) : cnt;
-  const int r0 = SGMV_TILE_ROWS * p;
-  return piece_at(b, chunk, r0, bstart, pstart, C, min(SGMV_TILE_ROWS, len - r0));
-}
-
-// si-th small piece (1..16 rows) of bucket b: the tail of a chunk (each chunk has at most one).
-__device__ __forceinline__ PieceDesc small_piece_desc(int b, int si, int C, const int* bstart,
-                                                      const int* pstart) {
-  const int cnt = bstart[b + 1] - bstart[b];
-  int chunk = 0;
-  if (C > 0) {
-    int nlf, nsf;
-    piece_tiles(C, nlf, nsf);  // nsf: whether every full chunk ends in a small piece
-    chunk = nsf ? si : (cnt + C - 1) / C - 1;
-  }
-  const int len = C > 0 ? min(C, cnt - chunk * C) : cnt;
-  const int r0 = SGMV_TILE_ROWS * (len / SGMV_TILE_ROWS);
-  return piece_at(b, chunk, r0, bstart, pstart, C, len - r0);
-}
-
 __global__ __launch_bounds__(BUILD_THREADS) void build_segments_mid_kernel(
     const int32_t* __restrict__ ids, int M, int L, int C, int32_t* __restrict__ sorted,
     int32_t* __restrict__ indptr, int32_t* __restrict__ seg_lora, int32_t* __restrict__ tiles,
@@ -725,8 +533,9 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_mid_kernel(
       const bool small = rec >= n_large;
       const int r = small ? rec - n_large : rec;
       const int b = last_at_most(small ? sbase : lstart, n_buckets, r);
-      const PieceDesc pd = small ? small_piece_desc(b, r - sbase[b], C, bstart, pstart)
-                                 : large_piece_desc(b, r - lstart[b], C, bstart, pstart);
+      const int cnt_b = bstart[b + 1] - bstart[b];
+      const PieceDesc pd = small ? small_piece_desc(r - sbase[b], C, cnt_b, bstart[b], pstart[b])
+                                 : large_piece_desc(r - lstart[b], C, cnt_b, bstart[b], pstart[b]);
       int4* d = reinterpret_cast<int4*>(tiles + (size_t)(small ? large_cap + r : r) *
                                                     SGMV_TILE_INTS) + q;
       if (q == 0) {

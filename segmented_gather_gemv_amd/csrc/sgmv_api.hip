@@ -18,6 +18,8 @@ hipError_t launch_pool_pack(const void* a_user, const void* b_user, const sgmv_p
 hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, LaunchEvents ev,
                              hipStream_t stream);
 hipError_t launch_delta_f32(int mode, DeltaArgs A, LaunchEvents ev, hipStream_t stream);
+hipError_t launch_delta_bf16_build(bool aligned, DeltaArgs A, LaunchEvents ev,
+                                   hipStream_t stream);
 
 namespace {
 
@@ -157,10 +159,12 @@ LaunchEvents events_of(const sgmv_launch_opts* o) {
 
 sgmv_status hip_status(hipError_t e) { return e == hipSuccess ? SGMV_OK : SGMV_EHIP; }
 
+// `ids` (fused mode, bf16, 1 <= M <= SGMV_FUSED_BUILD_MAX_M only): the launch also builds
+// the segments of seg from these device ids.
 sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, float* h_out,
                       int64_t ldh, int32_t M, const sgmv_pool* pool, const sgmv_segments* seg,
                       const sgmv_slice* out, int32_t n_slices, const sgmv_launch_opts* opts,
-                      void* stream) {
+                      void* stream, const int32_t* ids = nullptr) {
   if (M < 0 || !pool_ok(pool) || !opts_ok(opts)) return SGMV_EINVAL;
   if (pool->R_max > SGMV_MAX_RANK) return SGMV_EUNSUPPORTED;
   if (!seg_ok(seg, M, pool->L)) return SGMV_EINVAL;
@@ -206,6 +210,18 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
   if (mode == MODE_FUSED && pool->dtype == SGMV_BF16) choose_exchange(seg, opts, A);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LaunchEvents ev = events_of(opts);
+  if (ids) {
+    A.ids = ids;
+    A.M = M;
+    A.chunk = seg->chunk_size;
+    A.seg_cap = seg->seg_cap;
+    A.w_sorted = seg->sorted_token_ids;
+    A.w_indptr = seg->seg_indptr;
+    A.w_seg_lora = seg->seg_lora_ids;
+    A.w_tiles = seg->tiles;
+    A.w_info = seg->info;
+    return hip_status(launch_delta_bf16_build(aligned, A, ev, s));
+  }
   if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, ev, s));
   return hip_status(launch_delta_f32(mode, A, ev, s));
 }
@@ -349,6 +365,40 @@ sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_po
                             const sgmv_segments* seg, const sgmv_slice* out, int32_t n_slices,
                             void* stream) {
   return sgmv_lora_delta_ex(x, ldx, M, pool, seg, out, n_slices, nullptr, stream);
+}
+
+sgmv_status sgmv_lora_delta_ids_ex(const int32_t* lora_indices, const void* x, int64_t ldx,
+                                   int32_t M, const sgmv_pool* pool, const sgmv_segments* seg,
+                                   const sgmv_slice* out, int32_t n_slices,
+                                   const sgmv_launch_opts* opts, void* stream) {
+  if (M < 0 || (M > 0 && !lora_indices) || !pool_ok(pool) || !opts_ok(opts)) return SGMV_EINVAL;
+  if (!seg_ok(seg, M, pool->L)) return SGMV_EINVAL;
+  if (pool->dtype == SGMV_BF16 && M >= 1 && M <= SGMV_FUSED_BUILD_MAX_M &&
+      pool->L <= SGMV_DEVICE_BUILDER_MAX_L)
+    return run_delta(MODE_FUSED, x, ldx, nullptr, nullptr, 0, M, pool, seg, out, n_slices, opts,
+                     stream, lora_indices);
+  // two launches: validate the delta's arguments first so that a bad call changes nothing
+  if (M > 0 && (!x || ldx < pool->K)) return SGMV_EINVAL;
+  if (!out || n_slices < 1 || n_slices > SGMV_MAX_SLICES) return SGMV_EINVAL;
+  sgmv_launch_opts ob, od;
+  std::memset(&ob, 0, sizeof(ob));
+  std::memset(&od, 0, sizeof(od));
+  if (opts) {
+    od = *opts;
+    ob.start_event = opts->start_event;
+    od.start_event = nullptr;
+  }
+  const sgmv_status st = sgmv_build_segments_ex(lora_indices, M, pool->L, seg->chunk_size, 1,
+                                                seg, &ob, stream);
+  if (st != SGMV_OK) return st;
+  return sgmv_lora_delta_ex(x, ldx, M, pool, seg, out, n_slices, &od, stream);
+}
+
+sgmv_status sgmv_lora_delta_ids(const int32_t* lora_indices, const void* x, int64_t ldx,
+                                int32_t M, const sgmv_pool* pool, const sgmv_segments* seg,
+                                const sgmv_slice* out, int32_t n_slices, void* stream) {
+  return sgmv_lora_delta_ids_ex(lora_indices, x, ldx, M, pool, seg, out, n_slices, nullptr,
+                                stream);
 }
 
 }  // extern "C"

@@ -310,3 +310,23 @@ def test_pool_pack_rejects_bad_rank_before_launch():
     assert lib.sgmv_pool_pack(ctypes.c_void_p(0x10), ctypes.c_void_p(0x10),
                               ctypes.c_void_p(rank.data_ptr()), ctypes.c_void_p(alpha.data_ptr()),
                               ctypes.byref(pool), None) == sg.SGMV_EINVAL
+
+
+def test_delta_ids_argument_errors():
+    """The build-and-delta call checks its arguments before any launch, on both of its
+    paths (one launch for small bf16 batches, build + delta otherwise)."""
+    lib = sg.library()
+    y = sg._Slice(0x2000, 256, 0, 256)
+    x = ctypes.c_void_p(0x3000)
+    ids = ctypes.c_void_p(0x4000)
+    for M, dtype in [(8, sg.SGMV_BF16), (600, sg.SGMV_BF16), (8, sg.SGMV_F32)]:
+        pool = _fake_pool(dtype=dtype)
+        seg = sg.sgmv_segments_alloc(M, 4, 0, "cpu")
+        call = lambda i, xx, d, n=1, o=None: lib.sgmv_lora_delta_ids_ex(
+            i, xx, 128, M, ctypes.byref(pool), ctypes.byref(d), ctypes.byref(y), n, o, None)
+        assert call(None, x, seg.desc) == sg.SGMV_EINVAL           # no ids
+        assert call(ids, None, seg.desc) == sg.SGMV_EINVAL         # no x
+        assert call(ids, x, seg.desc, n=0) == sg.SGMV_EINVAL       # no slice
+        other = sg.sgmv_segments_alloc(M + 1, 4, 0, "cpu")
+        assert call(ids, x, other.desc) == sg.SGMV_EINVAL          # segments for another M
+        assert call(ids, x, seg.desc, o=sg.LaunchOpts(exchange=3).ref()) == sg.SGMV_EINVAL

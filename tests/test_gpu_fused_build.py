@@ -1,0 +1,174 @@
+"""GPU parity of sgmv_lora_delta_ids: segment build and fused delta in one call.
+
+Bar: bit-exact against the two-call path (device builder, then the fused delta) with the
+same launch options, for the segment arrays and for every element of y, plus the oracle bar
+of the fused delta on y. The single-launch path covers bf16 batches of 1..512 tokens; larger
+batches and fp32 pools take two launches and must agree the same way.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from test_gpu_parity import (DEV, _check_control, check_no_adapter_rows, compare, np32,
+                             oracle_y, sample_rows, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import segmented_gather_gemv_amd as m
+    return m
+
+
+def _ids_perm(M, L, seed):
+    return torch.from_numpy(np.random.default_rng(seed).permutation(M) % L).to(torch.int32)
+
+
+# name: (custom workload arguments, ids override or None)
+CASES = {
+    "one_token": (dict(M=1, K=512, N=256, L=4, R=16), None),
+    "small_16": (dict(M=16, K=1024, N=512, L=3, R=16, seq_lens=[16]), None),
+    "large_17": (dict(M=17, K=1024, N=512, L=3, R=16, seq_lens=[17]), None),
+    "max_one_adapter": (dict(M=512, K=1024, N=512, L=2, R=16, seq_lens=[512]), None),
+    "max_distinct": (dict(M=512, K=256, N=256, L=512, R=16), lambda: _ids_perm(512, 512, 1)),
+    "all_no_adapter": (dict(M=100, K=512, N=256, L=4, R=16, no_lora_frac=1.0), None),
+    "pool_1024": (dict(M=300, K=512, N=256, L=1024, R=16, no_lora_frac=0.1), None),
+    "chunked": (dict(M=300, K=1024, N=512, L=5, R=32, chunk=3, no_lora_frac=0.05), None),
+    "mixed_rank": (dict(M=180, K=1536, N=768, L=30, R=64, ranks=[5, 16, 31, 64]), None),
+    "unaligned": (dict(M=90, K=1000, N=300, L=20, R=24), None),
+    "prefill_like": (dict(M=400, K=2048, N=768, L=6, R=64, ranks=[16, 40, 64],
+                          seq_lens=[200, 17, 64, 119]), None),
+    "qkv_slices": (dict(M=128, K=1024, N=512, L=8, R=16, slices=[(0, 256), (256, 128),
+                                                                  (384, 128)]), None),
+    # two launches: beyond the single-launch batch size, and fp32
+    "two_launch_513": (dict(M=513, K=512, N=256, L=40, R=16, no_lora_frac=0.05), None),
+    "two_launch_f32": (dict(M=64, K=256, N=128, L=5, R=16, dtype=torch.float32), None),
+}
+
+
+def _workload(name, seed=7):
+    kw, ids = CASES[name]
+    w = workloads.custom(name=name, seed=seed, **kw)
+    if ids is not None:
+        w.ids = ids()
+    return w
+
+
+def _delta(sg, w, x, y0, fn, opts):
+    """Apply fn(views, opts) on a copy of y0, with one view per output slice."""
+    y = y0.clone()
+    views = [(y[:, n0:n0 + n].contiguous(), n0) for n0, n in w.slices]
+    fn(views if len(views) > 1 else views[0][0], opts)
+    torch.cuda.synchronize()
+    for t, n0 in views:
+        y[:, n0:n0 + t.shape[1]] = t
+    return y
+
+
+def _poisoned(sg, w):
+    seg = sg.sgmv_segments_alloc(w.M, w.L, w.chunk_size, DEV)
+    for t in (seg.sorted_token_ids, seg.seg_indptr, seg.seg_lora_ids, seg.tiles, seg.info):
+        t.fill_(-77)
+    return seg
+
+
+def _same_segments(a, b):
+    ha, hb = a.host(), b.host()
+    for k in ("sorted_token_ids", "seg_indptr", "seg_lora_ids", "large_tiles", "small_tiles"):
+        assert torch.equal(ha[k], hb[k]), k
+    assert ha["num_segments"] == hb["num_segments"]
+    assert ha["status"] == hb["status"]
+    return ha
+
+
+def _both(sg, w, pool, x, y0, ids, opts):
+    sep = sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True)
+    ya = _delta(sg, w, x, y0, lambda y, o: sg.sgmv_lora_delta(x, pool, sep, y, opts=o), opts)
+    one = _poisoned(sg, w)
+    yb = _delta(sg, w, x, y0,
+                lambda y, o: sg.sgmv_lora_delta_ids(ids, x, pool, one, y, opts=o), opts)
+    return sep, ya, one, yb
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_build_and_delta_match_two_calls(sg, name):
+    w = _workload(name)
+    pool, x, y0, ids = upload(w, sg)
+    sep, ya, one, yb = _both(sg, w, pool, x, y0, ids, None)
+    h = _same_segments(sep, one)
+    assert h["status"] == sg.SGMV_OK
+    assert torch.equal(ya, yb)
+    compare(np32(yb), oracle_y(w, np32(w.y0)), w.dtype, what=name)
+    check_no_adapter_rows(w, yb, w.y0)
+
+
+@pytest.mark.parametrize("name", ["max_one_adapter", "mixed_rank", "prefill_like", "chunked",
+                                  "unaligned"])
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_build_and_delta_with_exchange(sg, name, P):
+    """Every piece splits its shrink over K with its partners; the single launch advances
+    each piece's arrival counter by 64, as the two-call path does."""
+    w = _workload(name, seed=P)
+    pool, x, y0, ids = upload(w, sg)
+    opts = sg.LaunchOpts(n_split_small=P, n_split_large=min(P, 4), exchange=1)
+    sep, ya, one, yb = _both(sg, w, pool, x, y0, ids, opts)
+    _same_segments(sep, one)
+    assert torch.equal(ya, yb)
+    _check_control(sg, sep, 1)
+    _check_control(sg, one, 1)
+    # partials of late partners recomputed locally: the same bits
+    local = sg.LaunchOpts(n_split_small=P, n_split_large=min(P, 4), exchange=1, exchange_wait=-1)
+    yc = _delta(sg, w, x, y0, lambda y, o: sg.sgmv_lora_delta_ids(ids, x, pool, one, y, opts=o),
+                local)
+    assert torch.equal(ya, yc)
+    _check_control(sg, one, 2)
+    compare(np32(yb), oracle_y(w, np32(w.y0)), w.dtype, what=f"{name} P={P}")
+
+
+def test_build_and_delta_decode_full_size(sg):
+    """The decode workload (one token per sequence, ids uniform over the pool)."""
+    w = workloads.get("decode")
+    pool, x, y0, ids = upload(w, sg)
+    sep, ya, one, yb = _both(sg, w, pool, x, y0, ids, None)
+    _same_segments(sep, one)
+    assert torch.equal(ya, yb)
+    rows = sample_rows(w, 64)
+    compare(np32(yb), oracle_y(w, np32(w.y0), rows=rows), w.dtype, rows=rows, what="decode")
+
+
+def test_build_and_delta_reuse_per_step(sg):
+    """Successive steps with new ids reuse one segments object, as a serving loop does."""
+    w = _workload("mixed_rank")
+    pool, x, y0, _ = upload(w, sg)
+    seg = sg.sgmv_segments_alloc(w.M, w.L, 0, DEV)
+    for step in range(3):
+        ids = torch.from_numpy(np.random.default_rng(100 + step).integers(-1, w.L, w.M)
+                               .astype(np.int32)).to(DEV)
+        y = _delta(sg, w, x, y0, lambda v, o: sg.sgmv_lora_delta_ids(ids, x, pool, seg, v), None)
+        ref_seg = sg.sgmv_build_segments(ids, w.L, 0, on_device=True)
+        ref = _delta(sg, w, x, y0, lambda v, o: sg.sgmv_lora_delta(x, pool, ref_seg, v), None)
+        _same_segments(ref_seg, seg)
+        assert torch.equal(y, ref), step
+
+
+def test_build_and_delta_bad_ids(sg):
+    """Ids outside {-1} U [0, L) count as -1 and are flagged in info[3]."""
+    w = _workload("mixed_rank")
+    ids_np = w.ids.numpy().copy()
+    bad = np.array([3, 50, 51, 170])
+    ids_np[bad] = [w.L, -2, 1 << 20, -(1 << 30)]
+    pool, x, y0, _ = upload(w, sg)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    sep, ya, one, yb = _both(sg, w, pool, x, y0, ids, None)
+    h = _same_segments(sep, one)
+    assert h["status"] == sg.SGMV_EBADID
+    assert torch.equal(ya, yb)
+    assert torch.equal(yb[torch.from_numpy(bad)].cpu(), w.y0[torch.from_numpy(bad)])
+    clean = ids_np.copy()
+    clean[bad] = -1
+    w.ids = torch.from_numpy(clean)
+    compare(np32(yb), oracle_y(w, np32(w.y0)), w.dtype, what="bad ids")
