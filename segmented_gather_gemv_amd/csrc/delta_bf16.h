@@ -821,6 +821,7 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
   if constexpr (BUILD) {
     // ---- the batch's segments, built here; the rank/scale table loads overlap the ids' ----
     static_assert(DT_THREADS == FUSED_BUILD_WAVES * WAVE, "one token per thread");
+    const int id = tid < A.M ? A.ids[tid] : 0;  // issued first: one round trip with the table
     if (table) {
       for (int i = tid; i < A.L; i += DT_THREADS) {
         s_rank[i] = A.rank[i];
@@ -831,12 +832,12 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
                          A.seg_cap, A.large_cap, A.small_cap};
     const WgBuildLds S = wg_build_lds(reinterpret_cast<unsigned char*>(s_part), A.L);
     const WgBuildOut bo =
-        wg_build(A.ids, A.M, A.L, A.chunk, small, tile, blockIdx.x == 0, dst, S, s_tok);
+        wg_build(id, A.M, A.L, A.chunk, small, tile, blockIdx.x == 0, dst, S, s_tok);
     if (tile >= (small ? bo.n_small : bo.n_large)) return;  // uniform across the workgroup
-    pc.lora = S.rec[0];
-    pc.start = S.rec[1];
-    pc.rows = S.rec[2];
-    __syncthreads();  // the build scratch aliases s_part, and the table is in LDS
+    pc.lora = bo.lora;
+    pc.start = bo.start;
+    pc.rows = bo.rows;
+    __syncthreads();  // s_tok and the table are in LDS; the build scratch (s_part) is free
   } else {
     // ---- one round of loads: counts, the piece record, its tokens, the rank/scale table ----
     const int32_t* rec = A.tiles + (size_t)(small ? A.large_cap + tile : tile) * SGMV_TILE_INTS;

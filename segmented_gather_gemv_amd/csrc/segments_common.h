@@ -25,8 +25,9 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 }
 
 // Exclusive scan of NV ints per thread across a workgroup of NW waves. s_w holds NV * NW
-// ints. Contains barriers: call from all threads.
-template <int NV, int NW = BUILD_WAVES>
+// ints. Contains barriers: call from all threads. Without REUSE the final barrier, which
+// lets a later call write s_w again, is left out.
+template <int NV, int NW = BUILD_WAVES, bool REUSE = true>
 __device__ void block_scan(const int (&v)[NV], int (&ex)[NV], int (&tot)[NV], int* s_w) {
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
   int x[NV];
@@ -53,7 +54,7 @@ __device__ void block_scan(const int (&v)[NV], int (&ex)[NV], int (&tot)[NV], in
     ex[i] = before + x[i] - v[i];
     tot[i] = all;
   }
-  __syncthreads();
+  if (REUSE) __syncthreads();
 }
 
 // Counts of equal keys in lower waves (pre), in this wave (cw) and in higher waves (post),
@@ -191,6 +192,19 @@ __device__ __forceinline__ PieceDesc small_piece_desc(int si, int C, int cnt, in
   return PieceDesc{start + (C > 0 ? chunk * C : 0) + r0, len - r0, seg0 + chunk};
 }
 
+// Lanes of this wave that hold the same key as this lane (keys 0..L; lanes with `valid`
+// false are in no mask): one ballot per bit of the largest key, each lane keeping the lanes
+// that agree with it on that bit.
+__device__ __forceinline__ uint64_t match_key(int key, bool valid, int L) {
+  uint64_t same = __ballot(valid);
+  const int nb = 32 - __builtin_clz((unsigned)(L | 1));
+  for (int b = 0; b < nb; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
+  }
+  return same;
+}
 
 // ---------------------------------------------------------------------------------------
 // In-workgroup segment build for the fused build + delta launch
@@ -209,14 +223,14 @@ struct WgBuildLds {
   uint8_t* rc;  // [L + 1][8] per-(key, wave) counts
   int* base;    // [L + 1] first sorted row of each bucket (L: the tail)
   int* sbase;   // [L + 1] first small descriptor of each bucket
-  int* w;       // [6 * 8] workgroup scan scratch
+  int* w;       // [5 * 8] workgroup scan scratch
   int* rec;     // [4] this workgroup's descriptor: adapter, first row, rows, segment
 };
 
 inline size_t wg_build_lds_bytes(int L) {
   const size_t nk = (size_t)L + 1;
   return align16(nk * FUSED_BUILD_WAVES) + 2 * align16(nk * sizeof(int)) +
-         align16(6 * FUSED_BUILD_WAVES * sizeof(int)) + 16;
+         align16(5 * FUSED_BUILD_WAVES * sizeof(int)) + 16;
 }
 
 __device__ __forceinline__ WgBuildLds wg_build_lds(unsigned char* p, int L) {
@@ -229,13 +243,14 @@ __device__ __forceinline__ WgBuildLds wg_build_lds(unsigned char* p, int L) {
   s.sbase = reinterpret_cast<int*>(p);
   p += align16(nk * sizeof(int));
   s.w = reinterpret_cast<int*>(p);
-  p += align16(6 * FUSED_BUILD_WAVES * sizeof(int));
+  p += align16(5 * FUSED_BUILD_WAVES * sizeof(int));
   s.rec = reinterpret_cast<int*>(p);
   return s;
 }
 
 struct WgBuildOut {
   int n_large, n_small;  // 0 when an array would overflow
+  int lora, start, rows;  // this workgroup's descriptor, when tile < n_small / n_large
 };
 
 struct WgBuildDst {  // the builder's outputs, written by the writer workgroup only
@@ -243,11 +258,12 @@ struct WgBuildDst {  // the builder's outputs, written by the writer workgroup o
   int seg_cap, large_cap, small_cap;
 };
 
-// Call from all 512 threads. For descriptor `tile` of class `small`, leaves its record in
-// S.rec and its token ids in s_tok (when the descriptor exists).
-__device__ WgBuildOut wg_build(const int32_t* ids, int M, int L, int C, bool small, int tile,
-                               bool writer, const WgBuildDst& D, const WgBuildLds& S,
-                               int* s_tok) {
+// Call from all 512 threads; thread t passes the id of token t (any value for t >= M). For
+// descriptor `tile` of class `small` (when it exists), returns its adapter, first sorted row
+// and rows, and writes its token ids to s_tok. Ends without a barrier: the caller's next
+// barrier makes s_tok visible, and S may be written again only after it.
+__device__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile, bool writer,
+                               const WgBuildDst& D, const WgBuildLds& S, int* s_tok) {
   constexpr int NW = FUSED_BUILD_WAVES;
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
   const int NK = L + 1;
@@ -256,23 +272,15 @@ __device__ WgBuildOut wg_build(const int32_t* ids, int M, int L, int C, bool sma
   int key = -2;  // never equal to a real key (0..L)
   bool bad = false;
   if (valid) {
-    int id = ids[t];
     if (id < -1 || id >= L) {
       bad = true;
       id = -1;
     }
     key = id < 0 ? L : id;
   }
-  // rank among equal keys of lower lanes, and the count in this wave: lane j keeps the
-  // ballot of the lanes holding its key
+  // rank among equal keys of lower lanes, and the count in this wave
   uint64_t same = 0;
-  if (w * WAVE < M) {
-#pragma unroll
-    for (int j = 0; j < WAVE; ++j) {
-      const uint64_t m = __ballot(key == __builtin_amdgcn_readlane(key, j));
-      same = lane == j ? m : same;
-    }
-  }
+  if (w * WAVE < M) same = match_key(key, valid, L);  // uniform; waves without tokens skip it
   const int rk = __popcll(same & lanemask_lt(lane));
   const int cw = __popcll(same);
   __syncthreads();
@@ -283,39 +291,40 @@ __device__ WgBuildOut wg_build(const int32_t* ids, int M, int L, int C, bool sma
   const int rank = pre + rk;
   const int cnt = pre + cwt + post;
   const bool first = valid && key < L && rank == 0;
-  int v[6] = {0, 0, 0, 0, 0, bad ? 1 : 0};
+  // per bucket, at its first token: tokens, segments, large and small descriptors; and the
+  // bad-id count
+  int v[5] = {0, 0, 0, 0, bad ? 1 : 0};
   if (first) {
     const int np = C > 0 ? (cnt + C - 1) / C : 1;
     const int last = C > 0 ? cnt - C * (np - 1) : cnt;
     int nl, ns, nl1, ns1;
     piece_tiles(C > 0 ? C : cnt, nl, ns);
     piece_tiles(last, nl1, ns1);
-    v[0] = 1;
-    v[1] = cnt;
-    v[2] = np;
-    v[3] = (np - 1) * nl + nl1;
-    v[4] = (np - 1) * ns + ns1;
+    v[0] = cnt;
+    v[1] = np;
+    v[2] = (np - 1) * nl + nl1;
+    v[3] = (np - 1) * ns + ns1;
   }
-  int ex[6], tot[6];
-  block_scan<6, NW>(v, ex, tot, S.w);
-  const int n_lora = tot[1], n_seg = tot[2], n_large = tot[3], n_small = tot[4];
+  int ex[5], tot[5];
+  block_scan<5, NW, false>(v, ex, tot, S.w);
+  const int n_lora = tot[0], n_seg = tot[1], n_large = tot[2], n_small = tot[3];
   const bool overflow = n_seg > D.seg_cap || n_large > D.large_cap || n_small > D.small_cap;
   if (first) {
-    S.base[key] = ex[1];
-    S.sbase[key] = ex[4];
+    S.base[key] = ex[0];
+    S.sbase[key] = ex[3];
     if (!overflow) {
       // this workgroup's descriptor, if it belongs to this bucket
-      const int first_d = small ? ex[4] : ex[3], nd = small ? v[4] : v[3];
+      const int first_d = small ? ex[3] : ex[2], nd = small ? v[3] : v[2];
       if (tile >= first_d && tile < first_d + nd) {
-        const PieceDesc pd = small ? small_piece_desc(tile - first_d, C, cnt, ex[1], ex[2])
-                                   : large_piece_desc(tile - first_d, C, cnt, ex[1], ex[2]);
+        const PieceDesc pd = small ? small_piece_desc(tile - first_d, C, cnt, ex[0], ex[1])
+                                   : large_piece_desc(tile - first_d, C, cnt, ex[0], ex[1]);
         S.rec[0] = key;
         S.rec[1] = pd.start;
         S.rec[2] = pd.rows;
         S.rec[3] = pd.seg;
       }
       if (writer)
-        write_bucket(key, cnt, C, ex[1], ex[2], ex[3], ex[4], D.indptr, D.seg_lora, D.tiles,
+        write_bucket(key, cnt, C, ex[0], ex[1], ex[2], ex[3], D.indptr, D.seg_lora, D.tiles,
                      D.seg_cap, D.large_cap, D.small_cap);
     }
   }
@@ -326,7 +335,7 @@ __device__ WgBuildOut wg_build(const int32_t* ids, int M, int L, int C, bool sma
       D.info[0] = overflow ? 0 : n_seg;
       D.info[1] = overflow ? 0 : n_large;
       D.info[2] = overflow ? 0 : n_small;
-      D.info[3] = overflow ? SGMV_ECAPACITY : (tot[5] > 0 ? SGMV_EBADID : SGMV_OK);
+      D.info[3] = overflow ? SGMV_ECAPACITY : (tot[4] > 0 ? SGMV_EBADID : SGMV_OK);
     }
   }
   __syncthreads();
@@ -334,16 +343,18 @@ __device__ WgBuildOut wg_build(const int32_t* ids, int M, int L, int C, bool sma
   out.n_large = overflow ? 0 : n_large;
   out.n_small = overflow ? 0 : n_small;
   const bool mine = tile < (small ? out.n_small : out.n_large);
+  out.lora = mine ? S.rec[0] : 0;
+  out.start = mine ? S.rec[1] : 0;
+  out.rows = mine ? S.rec[2] : 0;
   if (valid) {
     const int pos = S.base[key] + rank;
-    if (mine && key < L && pos >= S.rec[1] && pos < S.rec[1] + S.rec[2]) s_tok[pos - S.rec[1]] = t;
+    if (key < L && pos >= out.start && pos < out.start + out.rows) s_tok[pos - out.start] = t;
     if (writer) {
       if (pos < M) D.sorted[pos] = t;
       if (key < L && !overflow)
         token_slot(t, rank, cnt, C, S.sbase[key], D.tiles, D.large_cap, D.small_cap);
     }
   }
-  __syncthreads();
   return out;
 }
 

@@ -61,16 +61,9 @@ __global__ __launch_bounds__(NW * WAVE) void build_segments_small_kernel(
     }
     key = id < 0 ? L : id;
   }
-  // rank among equal keys of lower lanes, and the count in this wave: lane j keeps the
-  // ballot of the lanes holding its key (lanes past M hold a key no token has)
+  // rank among equal keys of lower lanes, and the count in this wave
   uint64_t same = 0;
-  if (w * WAVE < M) {  // uniform; waves without tokens skip it
-#pragma unroll
-    for (int j = 0; j < WAVE; ++j) {
-      const uint64_t m = __ballot(key == __builtin_amdgcn_readlane(key, j));
-      same = lane == j ? m : same;
-    }
-  }
+  if (w * WAVE < M) same = match_key(key, valid, L);  // uniform; waves without tokens skip it
   const int rk = __popcll(same & lanemask_lt(lane));
   const int cw = __popcll(same);
   __syncthreads();
