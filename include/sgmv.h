@@ -233,7 +233,9 @@ sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_po
  * For a bf16 pool with 1 <= M <= SGMV_FUSED_BUILD_MAX_M and pool->L <=
  * SGMV_DEVICE_BUILDER_MAX_L this is ONE launch: every workgroup groups the batch's tokens
  * itself in LDS, and one of them also writes the arrays of `seg`, which no other workgroup
- * of the launch reads. That launch leaves the exchange control words of seg->exchange as it
+ * of the launch reads. Without chunking and with pool->L <= seg->small_cap, a small piece's
+ * exchange control word and partial tiles are those of slot large_cap + its adapter id
+ * rather than of its descriptor. That launch leaves the exchange control words of seg->exchange as it
  * finds them (every completed fused call leaves them consistent). Otherwise it issues the two
  * launches. Never synchronises with the host.
  * Errors: EINVAL; EUNSUPPORTED; EHIP. */

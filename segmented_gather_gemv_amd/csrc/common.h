@@ -83,6 +83,10 @@ struct DeltaArgs {
   // writes as the device builder would
   const int32_t* ids;
   int32_t M, chunk, seg_cap;
+  // adapter-major small pieces: without chunking and with L <= small_cap, small-piece slot
+  // t holds adapter t's small piece (its tokens found by one ballot per wave, no sort), and
+  // workgroup grid_writer builds and writes the segment arrays
+  int32_t amajor, grid_writer;
   int32_t *w_sorted, *w_indptr, *w_seg_lora, *w_tiles, *w_info;
   SliceArg slices[SGMV_MAX_SLICES];
 };

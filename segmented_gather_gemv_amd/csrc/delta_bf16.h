@@ -811,6 +811,16 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
 
   // ---- which piece and column split (from the workgroup index alone) ----
   const bool split = MODE != MODE_SHRINK;
+  if constexpr (BUILD) {
+    if (A.amajor && (int)blockIdx.x == A.grid_writer) {  // the segment arrays, no piece
+      const int id = threadIdx.x < (unsigned)A.M ? A.ids[threadIdx.x] : 0;
+      const WgBuildDst dst{A.w_sorted, A.w_indptr, A.w_seg_lora, A.w_tiles, A.w_info,
+                           A.seg_cap, A.large_cap, A.small_cap};
+      wg_build(id, A.M, A.L, A.chunk, false, A.large_cap, true, dst,
+               wg_build_lds(reinterpret_cast<unsigned char*>(s_part), A.L), s_tok);
+      return;
+    }
+  }
   bool small;
   int tile, p, P;
   if (!locate_piece(A, split, small, tile, p, P)) return;
@@ -818,7 +828,20 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
   const int tid = threadIdx.x;
   const bool table = A.L <= RANK_TABLE_MAX;
   Piece pc;
-  if constexpr (BUILD) {
+  if (BUILD && A.amajor && small) {
+    // ---- adapter-major small piece: slot `tile` is adapter `tile`; no sort needed ----
+    if (tile >= A.L) return;
+    const int id = tid < A.M ? A.ids[tid] : -1;
+    if (tid == 0) {
+      s_rank[tile] = A.rank[tile];
+      s_scale[tile] = A.scale[tile];
+    }
+    pc.rows = adapter_small_piece<DT_WAVES>(id, A.M, tile, reinterpret_cast<int*>(s_part), s_tok);
+    if (pc.rows == 0) return;  // uniform
+    pc.lora = tile;
+    pc.start = 0;
+    __syncthreads();  // s_tok and the table entry; s_part is free again
+  } else if constexpr (BUILD) {
     // ---- the batch's segments, built here; the rank/scale table loads overlap the ids' ----
     static_assert(DT_THREADS == FUSED_BUILD_WAVES * WAVE, "one token per thread");
     const int id = tid < A.M ? A.ids[tid] : 0;  // issued first: one round trip with the table
@@ -832,7 +855,7 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
                          A.seg_cap, A.large_cap, A.small_cap};
     const WgBuildLds S = wg_build_lds(reinterpret_cast<unsigned char*>(s_part), A.L);
     const WgBuildOut bo =
-        wg_build(id, A.M, A.L, A.chunk, small, tile, blockIdx.x == 0, dst, S, s_tok);
+        wg_build(id, A.M, A.L, A.chunk, small, tile, !A.amajor && blockIdx.x == 0, dst, S, s_tok);
     if (tile >= (small ? bo.n_small : bo.n_large)) return;  // uniform across the workgroup
     pc.lora = bo.lora;
     pc.start = bo.start;
@@ -899,6 +922,10 @@ inline void delta_geometry(int mode, DeltaArgs& A, int& grid, size_t& lds, bool 
   // them for their h fragments, which fit for every rank
   lds = (size_t)DT_WAVES * (A.R_pad / 16) * 256 * sizeof(float);
   if (build && wg_build_lds_bytes(A.L) > lds) lds = wg_build_lds_bytes(A.L);  // aliases s_part
+  if (build && A.amajor) {  // small slots per adapter, then the writer
+    grid = A.grid_large + class_grid(A.L, split ? A.n_split_small : 1) + 1;
+    A.grid_writer = grid - 1;
+  }
 }
 
 }  // namespace sgmv

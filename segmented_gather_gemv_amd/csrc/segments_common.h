@@ -206,6 +206,34 @@ __device__ __forceinline__ uint64_t match_key(int key, bool valid, int L) {
   return same;
 }
 
+// The small piece of adapter l's bucket when there is no chunking: its last c % 64 tokens
+// when that is 1..16 (c: the adapter's tokens), in token order, as the device builder makes
+// it. Call from all threads of a workgroup of NW waves, thread t passing the id of token t
+// (any value for t >= M); s_wc holds NW ints. Returns the piece's rows (0: no small piece;
+// uniform) and writes its tokens to s_tok, visible after the caller's next barrier.
+template <int NW>
+__device__ int adapter_small_piece(int id, int M, int l, int* s_wc, int* s_tok) {
+  const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+  const bool mine = t < M && id == l;
+  const uint64_t m = __ballot(mine);
+  if (lane == 0) s_wc[w] = __popcll(m);
+  __syncthreads();
+  int before = 0, c = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int v = s_wc[i];
+    c += v;
+    before += i < w ? v : 0;
+  }
+  const int rem = c % SGMV_TILE_ROWS;
+  const int rows = rem <= SGMV_SMALL_ROWS ? rem : 0;
+  if (mine) {
+    const int r = before + __popcll(m & lanemask_lt(lane)) - (c - rows);
+    if (r >= 0) s_tok[r] = t;
+  }
+  return rows;
+}
+
 // ---------------------------------------------------------------------------------------
 // In-workgroup segment build for the fused build + delta launch
 // ---------------------------------------------------------------------------------------

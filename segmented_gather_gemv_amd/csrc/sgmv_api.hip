@@ -220,6 +220,7 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
     A.w_seg_lora = seg->seg_lora_ids;
     A.w_tiles = seg->tiles;
     A.w_info = seg->info;
+    A.amajor = (seg->chunk_size == 0 && pool->L <= seg->small_cap) ? 1 : 0;
     return hip_status(launch_delta_bf16_build(aligned, A, ev, s));
   }
   if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, ev, s));
