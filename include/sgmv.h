@@ -87,7 +87,9 @@ typedef struct {
   int32_t* rank;
   float* scale;
   int32_t L, R_max, R_pad, K, N, K_pad, N_pad;
-  int32_t dtype; /* sgmv_dtype */
+  int32_t dtype;    /* sgmv_dtype */
+  int32_t rank_min; /* smallest r_l, set by sgmv_pool_pack (0 before): when it equals R_pad,
+                       no adapter has padding and loads may start before r_l is read */
 } sgmv_pool;
 
 /* Fill the dimensions of `pool` for L adapters of rank at most R_max, K inputs and N
@@ -104,10 +106,10 @@ sgmv_status sgmv_pool_init(int32_t L, int32_t R_max, int32_t K, int32_t N, int32
  *   rank     host, [L] int32, each in [1, R_max]
  *   alpha    host, [L] fp32; scale_l = alpha_l / rank_l     (Ascend article 2.1, 3.2)
  * Entries of a_user/b_user at ranks >= rank[l] are ignored. pool->a, b, rank, scale must
- * point to allocations of the sizes sgmv_pool_init reported.
+ * point to allocations of the sizes sgmv_pool_init reported. Sets pool->rank_min.
  * Errors: EINVAL (null pointers, rank out of range, non-finite alpha); EHIP. */
 sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t* rank,
-                           const float* alpha, const sgmv_pool* pool, void* stream);
+                           const float* alpha, sgmv_pool* pool, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
  * Segments (Punica page, batching-effect and code sections; Ascend article 3.3, 4.2).

@@ -52,7 +52,8 @@ class _Pool(ctypes.Structure):
     _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("rank", ctypes.c_void_p),
                 ("scale", ctypes.c_void_p), ("L", ctypes.c_int32), ("R_max", ctypes.c_int32),
                 ("R_pad", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
-                ("K_pad", ctypes.c_int32), ("N_pad", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("K_pad", ctypes.c_int32), ("N_pad", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rank_min", ctypes.c_int32)]
 
 
 class _Segments(ctypes.Structure):

@@ -87,6 +87,7 @@ struct DeltaArgs {
   // t holds adapter t's small piece (its tokens found by one ballot per wave, no sort), and
   // workgroup grid_writer builds and writes the segment arrays
   int32_t amajor, grid_writer;
+  int32_t spec;  // with amajor: A and B of a small piece loaded before its tokens are known
   int32_t *w_sorted, *w_indptr, *w_seg_lora, *w_tiles, *w_info;
   SliceArg slices[SGMV_MAX_SLICES];
 };

@@ -282,6 +282,48 @@ struct ShrinkSteps {
       }
     }
   }
+  // The same loads in two parts: the adapter's A rows (all 16 NRK of them; rows at or past
+  // r are zeroed by mask_rank once r is known), then the tokens' x rows. load_a issues its
+  // loads unconditionally (an element outside the step reads the row's first 16 bytes and is
+  // zeroed), so that later waits can count them exactly.
+  __device__ __forceinline__ void load_a(const uint16_t* ab, int K_pad, int K, int ch, int c1,
+                                         int c, int g) {
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      const bool live = ch + st < c1;
+      const int kb = (ch + st) * KSTEP + 8 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = kb + 32 * i;
+        const bool in = live && k < K;
+#pragma unroll
+        for (int rk = 0; rk < NRK; ++rk) {
+          const int j = rk * 16 + c;
+          const u32x4_t v = load_u32x4(ab + (size_t)j * K_pad + (in ? k : 0));
+          av[st][rk][i] = in ? v : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void mask_rank(int r, int c) {
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+      for (int rk = 0; rk < NRK; ++rk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (rk * 16 + c >= r) av[st][rk][i] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __device__ __forceinline__ void load_x(const uint16_t* xr, bool vx, int K, int ch, int c1,
+                                         int g) {
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      const bool live = ch + st < c1;
+      const int kb = (ch + st) * KSTEP + 8 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[st][i] = load_x8<ALIGNED>(xr, kb + 32 * i, K, vx && live);
+    }
+  }
   __device__ __forceinline__ void mfma(f32x4_t (&acc)[NRK]) const {
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st)
@@ -339,7 +381,38 @@ struct ExpandPrefetch {
       const int vl = pc.v0 + 64 * (w + DT_WAVES * f) + 4 * c;
       map_group<ALIGNED>(A, vl, cm[f]);
       load_b_group<NE>(bb, A.N_pad, pc.r, vl, pc.v1, g, cm[f], bq[f]);
-      load_y<ALIGNED>(s_tok, pc.rows, 0, g, vl, pc.v1, cm[f], yv[f]);
+      sgmv::load_y<ALIGNED>(s_tok, pc.rows, 0, g, vl, pc.v1, cm[f], yv[f]);
+    }
+  }
+  // The same loads in two parts: B of the adapter at rank r (the pool's full rank, before
+  // the adapter's own is known; mask_rank trims it), then the tokens' y rows.
+  __device__ __forceinline__ void load_b(const DeltaArgs& A, const uint16_t* bb, const Piece& pc,
+                                         int r, int w, int c, int g) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f) {
+      const int vl = pc.v0 + 64 * (w + DT_WAVES * f) + 4 * c;
+      map_group<ALIGNED>(A, vl, cm[f]);
+      load_b_group<NE>(bb, A.N_pad, r, vl, pc.v1, g, cm[f], bq[f]);
+    }
+  }
+  __device__ __forceinline__ void mask_rank(int r, int g) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f)
+#pragma unroll
+      for (int re = 0; re < NE; ++re) {
+        const int live = r - 8 * (re * 4 + g);  // live ranks in this lane's octet
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e >= live) bq[f][re][q][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+      }
+  }
+  __device__ __forceinline__ void load_y(const Piece& pc, const int* s_tok, int w, int c, int g) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f) {
+      const int vl = pc.v0 + 64 * (w + DT_WAVES * f) + 4 * c;
+      sgmv::load_y<ALIGNED>(s_tok, pc.rows, 0, g, vl, pc.v1, cm[f], yv[f]);
     }
   }
 };
@@ -620,9 +693,15 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
 // ---------------------------------------------------------------------------------------
 // small pieces (<= 16 rows): K split across the 8 waves, expand operands prefetched
 // ---------------------------------------------------------------------------------------
-template <int MODE, int NRK, bool ALIGNED, bool XCH>
-__device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc, const int* s_tok,
-                                            float* s_part, float* s_h, int* s_mask) {
+// SPEC (fused build + delta, adapter-major, every adapter at full rank 16): pc holds the
+// adapter and the columns only; the first K step's A tile is loaded before the adapter's
+// tokens are looked up (from `id`, this thread's token id, whose load was issued first), and
+// the tokens' x, then B and y, after; the adapter's rank and scale (rank_l, scale_l) mask A
+// and B where they are first used.
+template <int MODE, int NRK, bool ALIGNED, bool XCH, bool SPEC = false>
+__device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* s_tok,
+                                            float* s_part, float* s_h, int* s_mask, int id = 0,
+                                            int rank_l = 0, float scale_l = 0.f) {
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
   constexpr bool xkernel = XCH && MODE == MODE_FUSED;
@@ -645,15 +724,39 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc,
     f32x4_t acc[NRK];
 #pragma unroll
     for (int i = 0; i < NRK; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const bool vx = c < pc.rows;
-    const uint16_t* xr =
-        static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[c] : 0) * (size_t)A.ldx;
     const uint16_t* ab = static_cast<const uint16_t*>(A.a) + (size_t)pc.lora * A.R_pad * A.K_pad;
     // K steps of this workgroup (all of K, or its split's range), then of this wave
     const int k0 = xch ? pc.split * nch / pc.nsplit : 0;
     const int k1 = xch ? (pc.split + 1) * nch / pc.nsplit : nch;
     const int c0 = k0 + w * (k1 - k0) / DT_WAVES, c1 = k0 + (w + 1) * (k1 - k0) / DT_WAVES;
-    for (int ch = c0; ch < c1; ch += NSTEP) {
+    int ch = c0;
+    if constexpr (SPEC) {
+      static_assert(MODE == MODE_FUSED && NRK == 1 && PF > 0, "adapter-major rank-16 pieces");
+      ShrinkSteps<NRK, NSTEP, ALIGNED> S;
+      S.load_a(ab, A.K_pad, A.K, ch, c1, c, g);
+      pc.rows = adapter_small_piece<DT_WAVES>(id, A.M, pc.lora, reinterpret_cast<int*>(s_part),
+                                              s_tok);
+      if (pc.rows == 0) {  // uniform: no small piece; let the loads land before leaving
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+      }
+      __syncthreads();  // s_tok; s_part is free again
+      pc.r = rank_l;
+      pc.scale = scale_l;
+      const bool vx = c < pc.rows;
+      S.load_x(static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[c] : 0) * (size_t)A.ldx,
+               vx, A.K, ch, c1, g);
+      pf.load_b(A, bb, pc, A.R_pad, w, c, g);  // B and y after x: the shrink waits on x
+      pf.load_y(pc, s_tok, w, c, g);
+      fetched = true;
+      S.mask_rank(pc.r, c);
+      S.mfma(acc);
+      ch += NSTEP;
+    }
+    const bool vx = c < pc.rows;
+    const uint16_t* xr =
+        static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[c] : 0) * (size_t)A.ldx;
+    for (; ch < c1; ch += NSTEP) {
       if constexpr (xkernel && NRK >= 3) {
         shrink_step_halves<NRK, ALIGNED>(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g, acc);
       } else {
@@ -680,6 +783,7 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, const Piece& pc,
 
   bf16x8_t P[NE][2];
   h_fragments<NE>(s_h, 0, lane, P);
+  if constexpr (SPEC) pf.mask_rank(pc.r, g);
 
   // prefetched groups
 #pragma unroll
@@ -770,9 +874,10 @@ template <int MODE, bool ALIGNED, int NRK, bool XCH>
 __device__ __forceinline__ void piece_of(const DeltaArgs& A, const Piece& pc, bool small,
                                          const int* s_tok, float* s_part, float* s_h,
                                          int* s_mask) {
-  if (small)
-    small_piece<MODE, NRK, ALIGNED, XCH>(A, pc, s_tok, s_part, s_h, s_mask);
-  else
+  if (small) {
+    Piece q = pc;
+    small_piece<MODE, NRK, ALIGNED, XCH>(A, q, const_cast<int*>(s_tok), s_part, s_h, s_mask);
+  } else
     large_piece<MODE, NRK, ALIGNED, XCH>(A, pc, s_tok, s_part, s_h, s_mask);
 }
 
@@ -831,6 +936,29 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
   if (BUILD && A.amajor && small) {
     // ---- adapter-major small piece: slot `tile` is adapter `tile`; no sort needed ----
     if (tile >= A.L) return;
+    if constexpr (MODE == MODE_FUSED && NRKM == 1) {
+      if (A.spec) {  // A first, while the ids are on their way
+        const int id0 = A.ids[tid < A.M ? tid : 0];  // unconditional loads: exact waits
+        const int rank_l = A.rank[tile];
+        const float scale_l = A.scale[tile];
+        const int id = tid < A.M ? id0 : -1;
+        pc.lora = tile;
+        pc.start = 0;
+        pc.rows = 0;
+        pc.r = A.R_pad;
+        pc.scale = 0.f;
+        const int width = (((A.v_total + P - 1) / P) + 63) & ~63;
+        pc.v0 = p * width;
+        pc.v1 = min(pc.v0 + width, A.v_total);
+        pc.tile = tile;
+        pc.split = p;
+        pc.nsplit = P;
+        if (pc.v0 >= pc.v1 && !(XCH && A.xch_small)) return;
+        small_piece<MODE, 1, ALIGNED, XCH, true>(A, pc, s_tok, s_part, s_h, &s_mask, id, rank_l,
+                                                 scale_l);
+        return;
+      }
+    }
     const int id = tid < A.M ? A.ids[tid] : -1;
     if (tid == 0) {
       s_rank[tile] = A.rank[tile];

@@ -221,6 +221,9 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
     A.w_tiles = seg->tiles;
     A.w_info = seg->info;
     A.amajor = (seg->chunk_size == 0 && pool->L <= seg->small_cap) ? 1 : 0;
+    // every adapter at the full rank of one tile: a small piece's A and B loads need
+    // neither its rank nor its tokens and are issued first
+    A.spec = (A.amajor && pool->R_pad == 16 && pool->rank_min == pool->R_pad) ? 1 : 0;
     return hip_status(launch_delta_bf16_build(aligned, A, ev, s));
   }
   if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, ev, s));
@@ -270,7 +273,7 @@ sgmv_status sgmv_pool_init(int32_t L, int32_t R_max, int32_t K, int32_t N, int32
 }
 
 sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t* rank,
-                           const float* alpha, const sgmv_pool* pool, void* stream) {
+                           const float* alpha, sgmv_pool* pool, void* stream) {
   if (!a_user || !b_user || !rank || !alpha || !pool_ok(pool)) return SGMV_EINVAL;
   const int L = pool->L;
   float* scale = static_cast<float*>(std::malloc(sizeof(float) * (size_t)L));
@@ -282,6 +285,9 @@ sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t
     }
     scale[l] = alpha[l] / (float)rank[l];
   }
+  int32_t rmin = pool->R_max;
+  for (int l = 0; l < L; ++l) rmin = rank[l] < rmin ? rank[l] : rmin;
+  pool->rank_min = rmin;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(pool->rank, rank, sizeof(int32_t) * L, hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
