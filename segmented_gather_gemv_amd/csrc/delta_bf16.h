@@ -746,11 +746,12 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
       const bool vx = c < pc.rows;
       S.load_x(static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[c] : 0) * (size_t)A.ldx,
                vx, A.K, ch, c1, g);
-      pf.load_b(A, bb, pc, A.R_pad, w, c, g);  // B and y after x: the shrink waits on x
-      pf.load_y(pc, s_tok, w, c, g);
-      fetched = true;
       S.mask_rank(pc.r, c);
       S.mfma(acc);
+      // B and y once x is in: they have the exchange to arrive, and x does not queue behind
+      pf.load_b(A, bb, pc, A.R_pad, w, c, g);
+      pf.load_y(pc, s_tok, w, c, g);
+      fetched = true;
       ch += NSTEP;
     }
     const bool vx = c < pc.rows;
