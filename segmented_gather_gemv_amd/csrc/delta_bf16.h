@@ -695,12 +695,11 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
 // ---------------------------------------------------------------------------------------
 // SPEC (fused build + delta, adapter-major, every adapter at full rank 16): pc holds the
 // adapter and the columns only; the first K step's A tile is loaded before the adapter's
-// tokens are looked up (from `id`, this thread's token id, whose load was issued first), and
-// the tokens' x, then B and y, after; the adapter's rank and scale (rank_l, scale_l) mask A
-// and B where they are first used.
+// tokens are looked up in the batch's ids, the tokens' x after, B and y once x is in; the
+// adapter's rank and scale (rank_l, scale_l) mask A and B where they are first used.
 template <int MODE, int NRK, bool ALIGNED, bool XCH, bool SPEC = false>
 __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* s_tok,
-                                            float* s_part, float* s_h, int* s_mask, int id = 0,
+                                            float* s_part, float* s_h, int* s_mask,
                                             int rank_l = 0, float scale_l = 0.f) {
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
@@ -734,8 +733,8 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
       static_assert(MODE == MODE_FUSED && NRK == 1 && PF > 0, "adapter-major rank-16 pieces");
       ShrinkSteps<NRK, NSTEP, ALIGNED> S;
       S.load_a(ab, A.K_pad, A.K, ch, c1, c, g);
-      pc.rows = adapter_small_piece<DT_WAVES>(id, A.M, pc.lora, reinterpret_cast<int*>(s_part),
-                                              s_tok);
+      pc.rows = adapter_small_piece<DT_WAVES>(wave_adapter_mask(A.ids, A.M, pc.lora), pc.lora,
+                                              reinterpret_cast<int*>(s_part), s_tok);
       if (pc.rows == 0) {  // uniform: no small piece; let the loads land before leaving
         __builtin_amdgcn_s_waitcnt(0);
         return;
@@ -938,11 +937,11 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
     // ---- adapter-major small piece: slot `tile` is adapter `tile`; no sort needed ----
     if (tile >= A.L) return;
     if constexpr (MODE == MODE_FUSED && NRKM == 1) {
-      if (A.spec) {  // A first, while the ids are on their way
-        const int id0 = A.ids[tid < A.M ? tid : 0];  // unconditional loads: exact waits
-        const int rank_l = A.rank[tile];
-        const float scale_l = A.scale[tile];
-        const int id = tid < A.M ? id0 : -1;
+      if (A.spec) {  // A first; the ids, rank and scale come through scalar loads meanwhile
+        typedef const int32_t __attribute__((address_space(4))) cint;
+        typedef const float __attribute__((address_space(4))) cfloat;
+        const int rank_l = ((const cint*)A.rank)[tile];
+        const float scale_l = ((const cfloat*)A.scale)[tile];
         pc.lora = tile;
         pc.start = 0;
         pc.rows = 0;
@@ -955,7 +954,7 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
         pc.split = p;
         pc.nsplit = P;
         if (pc.v0 >= pc.v1 && !(XCH && A.xch_small)) return;
-        small_piece<MODE, 1, ALIGNED, XCH, true>(A, pc, s_tok, s_part, s_h, &s_mask, id, rank_l,
+        small_piece<MODE, 1, ALIGNED, XCH, true>(A, pc, s_tok, s_part, s_h, &s_mask, rank_l,
                                                  scale_l);
         return;
       }
@@ -965,7 +964,8 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
       s_rank[tile] = A.rank[tile];
       s_scale[tile] = A.scale[tile];
     }
-    pc.rows = adapter_small_piece<DT_WAVES>(id, A.M, tile, reinterpret_cast<int*>(s_part), s_tok);
+    pc.rows = adapter_small_piece<DT_WAVES>(__ballot(id == tile), tile,
+                                            reinterpret_cast<int*>(s_part), s_tok);
     if (pc.rows == 0) return;  // uniform
     pc.lora = tile;
     pc.start = 0;

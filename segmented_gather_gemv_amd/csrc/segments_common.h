@@ -206,16 +206,37 @@ __device__ __forceinline__ uint64_t match_key(int key, bool valid, int L) {
   return same;
 }
 
+// Lanes of this wave's block of 64 tokens whose id is l. A full block is read with scalar
+// loads (through the constant address space; the ids are read-only for the launch), whose
+// latency does not queue behind the wave's vector loads; a partial block with one vector
+// load per lane.
+__device__ __forceinline__ uint64_t wave_adapter_mask(const int32_t* ids, int M, int l) {
+  typedef const int32_t __attribute__((address_space(4))) cint;
+  const int base = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE)) * WAVE;
+  const int n = M - base;
+  uint64_t m = 0;
+  if (n >= WAVE) {
+    const cint* cp = (const cint*)(ids + base);
+#pragma unroll
+    for (int j = 0; j < WAVE; ++j) m |= (uint64_t)(cp[j] == l) << j;
+  } else if (n > 0) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int id = ids[base + (lane < n ? lane : 0)];
+    m = __ballot(lane < n && id == l);
+  }
+  return m;
+}
+
 // The small piece of adapter l's bucket when there is no chunking: its last c % 64 tokens
 // when that is 1..16 (c: the adapter's tokens), in token order, as the device builder makes
-// it. Call from all threads of a workgroup of NW waves, thread t passing the id of token t
-// (any value for t >= M); s_wc holds NW ints. Returns the piece's rows (0: no small piece;
-// uniform) and writes its tokens to s_tok, visible after the caller's next barrier.
+// it. Call from all threads of a workgroup of NW waves, each wave passing the mask of its
+// block of 64 tokens whose id is l (ids past M never set); s_wc holds NW ints. Returns the
+// piece's rows (0: no small piece; uniform) and writes its tokens to s_tok, visible after
+// the caller's next barrier.
 template <int NW>
-__device__ int adapter_small_piece(int id, int M, int l, int* s_wc, int* s_tok) {
+__device__ int adapter_small_piece(uint64_t m, int l, int* s_wc, int* s_tok) {
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
-  const bool mine = t < M && id == l;
-  const uint64_t m = __ballot(mine);
+  const bool mine = (m >> lane) & 1u;
   if (lane == 0) s_wc[w] = __popcll(m);
   __syncthreads();
   int before = 0, c = 0;
