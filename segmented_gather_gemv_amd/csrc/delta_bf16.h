@@ -147,12 +147,15 @@ __device__ __forceinline__ void expand_mfma(const bf16x8_t (&P)[NE][2],
 template <bool ALIGNED>
 __device__ __forceinline__ void load_y(const int* s_tok, int rows, int rt, int g, int vl, int v1,
                                        const ColMap (&cm)[4], uint2 (&yv)[4]) {
+  // the four rows' tokens in one 16-byte LDS read (s_tok is 16-byte aligned)
+  const int4 tk = *reinterpret_cast<const int4*>(s_tok + rt * 16 + 4 * g);
+  const int toks[4] = {tk.x, tk.y, tk.z, tk.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = rt * 16 + 4 * g + e;
     yv[e] = make_uint2(0u, 0u);
     if (ALIGNED && row < rows && vl < v1)
-      yv[e] = *reinterpret_cast<const uint2*>(cm[0].y + (size_t)s_tok[row] * (size_t)cm[0].ldy +
+      yv[e] = *reinterpret_cast<const uint2*>(cm[0].y + (size_t)toks[e] * (size_t)cm[0].ldy +
                                               cm[0].col);
   }
 }
@@ -162,11 +165,13 @@ template <bool ALIGNED>
 __device__ __forceinline__ void store_y(const int* s_tok, int rows, int rt, int g, int vl, int v1,
                                         const ColMap (&cm)[4], const uint2 (&yv)[4],
                                         const f32x4_t (&yacc)[4]) {
+  const int4 tk = *reinterpret_cast<const int4*>(s_tok + rt * 16 + 4 * g);
+  const int toks[4] = {tk.x, tk.y, tk.z, tk.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = rt * 16 + 4 * g + e;
     if (row >= rows) continue;
-    const size_t tok = (size_t)s_tok[row];
+    const size_t tok = (size_t)toks[e];
     if (ALIGNED) {
       if (vl >= v1) continue;
       uint16_t* yp = cm[0].y + tok * (size_t)cm[0].ldy + cm[0].col;
@@ -905,7 +910,7 @@ __device__ __forceinline__ void run_piece(const DeltaArgs& A, const Piece& pc, b
 // first builds the segments of the batch itself (fused build + delta, M <= 512).
 template <int MODE, bool ALIGNED, int NRKM, bool XCH, bool BUILD>
 __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH ? 4 : 1))) void delta_bf16_kernel(DeltaArgs A) {
-  __shared__ int s_tok[SGMV_TILE_ROWS];
+  __shared__ __align__(16) int s_tok[SGMV_TILE_ROWS];
   __shared__ __align__(16) float s_h[SGMV_TILE_ROWS * HS];
   __shared__ int s_rank[RANK_TABLE_MAX];
   __shared__ float s_scale[RANK_TABLE_MAX];
