@@ -162,16 +162,20 @@ def write_traffic(args):
 
 
 def calibration_copy(args):
-    """A plain device copy of known size (the scale reference for the byte counters)."""
+    """A plain device copy of known size: the scale reference for the byte counters and, over
+    several buffer pairs whose total exceeds the last-level cache (--copy-sets), the copy
+    time of a working set that starts in HBM, for comparison with the delta kernel."""
     import torch
     n = args.copy_mib * 2 ** 20 // 2
-    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
-    b = torch.empty_like(a)
+    pairs = [(torch.ones(n, dtype=torch.bfloat16, device="cuda"),
+              torch.empty(n, dtype=torch.bfloat16, device="cuda")) for _ in range(args.copy_sets)]
     torch.cuda.synchronize()
-    for _ in range(8):  # elementwise kernel: reads a, writes b, copy_mib MiB each way
+    reps = max(8, 2 * args.copy_sets)
+    for i in range(reps):  # elementwise kernel: reads a, writes b, copy_mib MiB each way
+        a, b = pairs[i % args.copy_sets]
         torch.mul(a, 1.0, out=b)
     torch.cuda.synchronize()
-    log(f"elementwise copy of {args.copy_mib} MiB, 8 times")
+    log(f"elementwise copy of {args.copy_mib} MiB, {reps} times over {args.copy_sets} pairs")
 
 
 def cpu_baseline(w, seconds: float):
@@ -233,6 +237,8 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain device copy of --copy-mib MiB (counter scale)")
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--copy-sets", type=int, default=1,
+                    help="buffer pairs the calibration copy rotates over")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
                     help="delta FETCH, delta WRITE, copy FETCH, copy WRITE counter CSVs")
     args = ap.parse_args()

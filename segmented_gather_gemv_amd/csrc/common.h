@@ -102,9 +102,12 @@ struct LaunchEvents {
 // Piece and column split of this workgroup, from its index alone. Workgroups
 // [0, grid_large) take large pieces, the rest small ones; within a class, piece i runs on
 // XCD i % 8 (workgroup b runs on XCD b % 8) and its P column splits on consecutive slots of
-// that XCD. Returns false for a workgroup past the class capacity.
+// that XCD. Returns false for a workgroup past the class capacity. With `blocked_large`, a
+// large piece's `tile` is only its cyclic slot, to be turned into the piece by blocked_tile
+// once the piece count is known (then no capacity check is made here).
 __device__ __forceinline__ bool locate_piece(const DeltaArgs& A, bool split, bool& small,
-                                             int& tile, int& p, int& P) {
+                                             int& tile, int& p, int& P,
+                                             bool blocked_large = false) {
   int b = blockIdx.x;
   small = b >= A.grid_large;
   if (small) b -= A.grid_large;
@@ -113,7 +116,18 @@ __device__ __forceinline__ bool locate_piece(const DeltaArgs& A, bool split, boo
   const int q = slot / P;
   tile = q * 8 + (b & 7);
   p = slot - q * P;
+  if (!small && blocked_large) return true;
   return tile < (small ? A.small_cap : A.large_cap);
+}
+
+// Large pieces dealt to the XCDs in blocks: XCD x takes pieces [x * per, (x + 1) * per),
+// per = ceil(n / 8). The pieces of one adapter are consecutive, so they share an XCD's L2 for
+// A and B instead of every XCD fetching them. `c` is the cyclic slot q * 8 + x from
+// locate_piece, n the number of large pieces; returns the piece, or -1 if the slot has none.
+__device__ __forceinline__ int blocked_tile(int c, int n) {
+  const int per = (n + 7) >> 3;
+  const int q = c >> 3, t = (c & 7) * per + q;
+  return (q < per && t < n) ? t : -1;
 }
 
 // Workgroups for one class of pieces: 8 XCDs x P splits x ceil(cap / 8) pieces per XCD.

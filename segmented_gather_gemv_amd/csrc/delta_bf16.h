@@ -926,14 +926,14 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
       const int id = threadIdx.x < (unsigned)A.M ? A.ids[threadIdx.x] : 0;
       const WgBuildDst dst{A.w_sorted, A.w_indptr, A.w_seg_lora, A.w_tiles, A.w_info,
                            A.seg_cap, A.large_cap, A.small_cap};
-      wg_build(id, A.M, A.L, A.chunk, false, A.large_cap, true, dst,
+      wg_build(id, A.M, A.L, A.chunk, false, -8 /* a slot with no piece */, true, dst,
                wg_build_lds(reinterpret_cast<unsigned char*>(s_part), A.L), s_tok);
       return;
     }
   }
   bool small;
   int tile, p, P;
-  if (!locate_piece(A, split, small, tile, p, P)) return;
+  if (!locate_piece(A, split, small, tile, p, P, true)) return;
 
   const int tid = threadIdx.x;
   const bool table = A.L <= RANK_TABLE_MAX;
@@ -990,15 +990,21 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
     const WgBuildLds S = wg_build_lds(reinterpret_cast<unsigned char*>(s_part), A.L);
     const WgBuildOut bo =
         wg_build(id, A.M, A.L, A.chunk, small, tile, !A.amajor && blockIdx.x == 0, dst, S, s_tok);
-    if (tile >= (small ? bo.n_small : bo.n_large)) return;  // uniform across the workgroup
+    if (bo.tile < 0) return;  // uniform across the workgroup
+    tile = bo.tile;
     pc.lora = bo.lora;
     pc.start = bo.start;
     pc.rows = bo.rows;
     __syncthreads();  // s_tok and the table are in LDS; the build scratch (s_part) is free
   } else {
-    // ---- one round of loads: counts, the piece record, its tokens, the rank/scale table ----
-    const int32_t* rec = A.tiles + (size_t)(small ? A.large_cap + tile : tile) * SGMV_TILE_INTS;
+    // ---- one round of loads: counts, the piece record, its tokens, the rank/scale table
+    // (a large piece's record waits for the count, which places it) ----
     const int count = A.info[small ? 2 : 1];
+    if (!small) {
+      tile = blocked_tile(tile, count);
+      if (tile < 0) return;  // uniform
+    }
+    const int32_t* rec = A.tiles + (size_t)(small ? A.large_cap + tile : tile) * SGMV_TILE_INTS;
     pc.lora = rec[0];
     pc.start = rec[1];
     pc.rows = rec[2];

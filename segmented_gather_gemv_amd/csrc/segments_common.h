@@ -299,7 +299,8 @@ __device__ __forceinline__ WgBuildLds wg_build_lds(unsigned char* p, int L) {
 
 struct WgBuildOut {
   int n_large, n_small;  // 0 when an array would overflow
-  int lora, start, rows;  // this workgroup's descriptor, when tile < n_small / n_large
+  int tile;               // this workgroup's descriptor, -1 if none
+  int lora, start, rows;
 };
 
 struct WgBuildDst {  // the builder's outputs, written by the writer workgroup only
@@ -308,9 +309,10 @@ struct WgBuildDst {  // the builder's outputs, written by the writer workgroup o
 };
 
 // Call from all 512 threads; thread t passes the id of token t (any value for t >= M). For
-// descriptor `tile` of class `small` (when it exists), returns its adapter, first sorted row
-// and rows, and writes its token ids to s_tok. Ends without a barrier: the caller's next
-// barrier makes s_tok visible, and S may be written again only after it.
+// descriptor `tile` of class `small` (a large piece's `tile` is its cyclic slot, dealt in
+// blocks by blocked_tile once the count is known), returns the descriptor, its adapter, first
+// sorted row and rows, and writes its token ids to s_tok. Ends without a barrier: the
+// caller's next barrier makes s_tok visible, and S may be written again only after it.
 __device__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile, bool writer,
                                const WgBuildDst& D, const WgBuildLds& S, int* s_tok) {
   constexpr int NW = FUSED_BUILD_WAVES;
@@ -358,6 +360,7 @@ __device__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile
   block_scan<5, NW, false>(v, ex, tot, S.w);
   const int n_lora = tot[0], n_seg = tot[1], n_large = tot[2], n_small = tot[3];
   const bool overflow = n_seg > D.seg_cap || n_large > D.large_cap || n_small > D.small_cap;
+  if (!small) tile = blocked_tile(tile, overflow ? 0 : n_large);
   if (first) {
     S.base[key] = ex[0];
     S.sbase[key] = ex[3];
@@ -391,7 +394,8 @@ __device__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile
   WgBuildOut out;
   out.n_large = overflow ? 0 : n_large;
   out.n_small = overflow ? 0 : n_small;
-  const bool mine = tile < (small ? out.n_small : out.n_large);
+  const bool mine = tile >= 0 && tile < (small ? out.n_small : out.n_large);
+  out.tile = mine ? tile : -1;
   out.lora = mine ? S.rec[0] : 0;
   out.start = mine ? S.rec[1] : 0;
   out.rows = mine ? S.rec[2] : 0;
