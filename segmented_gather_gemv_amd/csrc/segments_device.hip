@@ -417,13 +417,27 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_mid_kernel(
   for (int i = tid; i < nwords; i += BUILD_THREADS) bitmap[i] = 0u;
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  for (int t = tid; t < M; t += BUILD_THREADS) {
-    int id = ids[t];
-    if (id < -1 || id >= L) {
-      s_bad = 1;
-      id = -1;
+  // the ids into LDS: each thread's loads of a round are issued together (a row of loads past
+  // M is skipped as a whole; the index clamped into [0, M)), so a round costs one memory round
+  // trip
+  constexpr int IPT = 16;
+  for (int base = 0; base < M; base += IPT * BUILD_THREADS) {
+    int v[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i)
+      v[i] = base + i * BUILD_THREADS < M ? ids[min(base + i * BUILD_THREADS + tid, M - 1)] : 0;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int t = base + i * BUILD_THREADS + tid;
+      int id = v[i];
+      if (t < M) {
+        if (id < -1 || id >= L) {
+          s_bad = 1;
+          id = -1;
+        }
+        keys[t] = (uint16_t)(id < 0 ? L : id);
+      }
     }
-    keys[t] = (uint16_t)(id < 0 ? L : id);
   }
   __syncthreads();
 
