@@ -27,6 +27,11 @@ figure divides the algorithmic bytes of one delta launch (x rows and y rows read
 for every token with an adapter, each used adapter's true-rank A and B once, 12 bytes of
 index per token) by that duration, against the 8 TB/s HBM peak.
 
+--trace (with --step two) replaces the fixed batch by seeded decode traces, one per buffer
+set, in which sequences keep their adapter and join or leave the batch; --segment-cache then
+builds through the grouping cache, and the line reports the builder time on steps with
+unchanged and with changed ids.
+
 The CPU baseline is the fp64 oracle (plain per-token NumPy loop) on the same batch, repeated
 for about 10 s on this host.
 
@@ -234,6 +239,15 @@ def main():
                     help="one: sgmv_lora_delta_ids (build inside the delta launch; bf16, "
                          "M <= 512); two: builder launch + delta launch; auto: one where it "
                          "applies")
+    ap.add_argument("--trace", action="store_true",
+                    help="ids follow a seeded decode trace (sequences join and leave; one "
+                         "trace per buffer set) instead of one fixed batch; needs --step two")
+    ap.add_argument("--trace-mean-len", type=int, default=256,
+                    help="mean sequence life in steps for --trace")
+    ap.add_argument("--trace-admit-every", type=int, default=8,
+                    help="steps between admissions of new sequences for --trace")
+    ap.add_argument("--segment-cache", action="store_true",
+                    help="build through sgmv_build_segments_cached (with --trace)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain device copy of --copy-mib MiB (counter scale)")
     ap.add_argument("--copy-mib", type=int, default=256)
@@ -275,6 +289,9 @@ def main():
         print("--step one needs a bf16 batch of 1..512 tokens", file=sys.stderr)
         sys.exit(2)
     one_launch = args.step == "one" or (args.step == "auto" and fits_one)
+    if (args.trace or args.segment_cache) and (one_launch or not args.trace):
+        print("--trace (and --segment-cache with it) needs --step two", file=sys.stderr)
+        sys.exit(2)
     elem = 2 if w.dtype == torch.bfloat16 else 4
     per_set = (w.a.numel() + w.b.numel() + w.x.numel() + w.y0.numel()) * elem
     n_sets = args.sets or max(2, min(64, -(-2 * MALL_BYTES // per_set)))
@@ -296,8 +313,20 @@ def main():
         del a_dev, b_dev
     torch.cuda.synchronize()
 
+    # --trace: buffer set j replays its own seeded decode trace, one row per use of the set
+    rows = -(-(args.warmup + args.steps) // n_sets)
+    if args.trace:
+        for j, st in enumerate(sets):
+            tr = workloads.decode_trace(rows, M=w.M, L=w.L, mean_len=args.trace_mean_len,
+                                        admit_every=args.trace_admit_every, seed=1000 + j)
+            st["trace"] = tr
+            st["trace_dev"] = tr.to(dev)
+            st["cache"] = sg.sgmv_segments_cache_alloc(w.M, dev)
+        torch.cuda.synchronize()
+
     s_handle = ctypes.c_void_p(stream.cuda_stream)
     build_fn, delta_fn = lib.sgmv_build_segments_ex, lib.sgmv_lora_delta_ex
+    cached_fn = lib.sgmv_build_segments_cached_ex
     ids_fn = lib.sgmv_lora_delta_ids_ex
     K = args.steps
     # per timed step: events the kernels' own dispatches record (start, end) -- no extra
@@ -319,12 +348,27 @@ def main():
                  st["n_sl"])
         calls.append((bargs, dargs))
 
+    def trace_row(g):
+        st = sets[g % n_sets]
+        return st, g // n_sets
+
     def step(i, timed=False):
-        bargs, dargs = calls[i % n_sets]
+        g = i + (args.warmup if timed else 0)  # use count over warm-up and timed steps
+        bargs, dargs = calls[g % n_sets] if args.trace else calls[i % n_sets]
         sample = timed and i in evs
         if one_launch:
             return ids_fn(bargs[0], *dargs, opts_d[i].ref() if sample else plain.ref(), s_handle)
-        rc = build_fn(*bargs, opts_b[i].ref() if sample else None, s_handle)
+        ob = opts_b[i].ref() if sample else None
+        if args.trace:
+            st, r = trace_row(g)
+            ids_p = ctypes.c_void_p(st["trace_dev"][r].data_ptr())
+            if args.segment_cache:
+                rc = cached_fn(ids_p, *bargs[1:], ctypes.c_void_p(st["cache"].data_ptr()), ob,
+                               s_handle)
+            else:
+                rc = build_fn(ids_p, *bargs[1:], ob, s_handle)
+        else:
+            rc = build_fn(*bargs, ob, s_handle)
         rc |= delta_fn(*dargs, opts_d[i].ref() if sample else plain.ref(), s_handle)
         return rc
 
@@ -354,6 +398,34 @@ def main():
     n_lora = int((ids_np >= 0).sum())
     alg_bytes = workloads.algorithmic_bytes(ids_np, w.rank.numpy(), w.K, w.N, elem)
     alg_flops = workloads.algorithmic_flops(ids_np, w.rank.numpy(), w.K, w.N)
+    trace_info = None
+    if args.trace:  # per-step token counts; roofline bytes averaged over the sampled steps
+        def row_ids(g):
+            st, r = trace_row(g)
+            return st["trace"][r].numpy()
+
+        def hit(g):
+            st, r = trace_row(g)
+            return r > 0 and bool((st["trace"][r] == st["trace"][r - 1]).all())
+
+        steps_g = [args.warmup + i for i in range(K)]
+        n_lora = sum(int((row_ids(g) >= 0).sum()) for g in steps_g) / K
+        samp_g = [args.warmup + i for i in sampled]
+        alg_bytes = sum(workloads.algorithmic_bytes(row_ids(g), w.rank.numpy(), w.K, w.N, elem)
+                        for g in samp_g) / len(samp_g)
+        alg_flops = sum(workloads.algorithmic_flops(row_ids(g), w.rank.numpy(), w.K, w.N)
+                        for g in samp_g) / len(samp_g)
+        hits = [hit(g) for g in samp_g]
+        bh = [b for b, h in zip(build_ms, hits) if h]
+        bm = [b for b, h in zip(build_ms, hits) if not h]
+        trace_info = {
+            "mean_len": args.trace_mean_len, "admit_every": args.trace_admit_every,
+            "segment_cache": bool(args.segment_cache),
+            "unchanged_step_fraction": sum(hit(g) for g in steps_g) / K,
+            "builder_us_unchanged_ids": sum(bh) / len(bh) * 1e3 if bh else None,
+            "builder_us_changed_ids": sum(bm) / len(bm) * 1e3 if bm else None,
+        }
+        log(f"trace: {trace_info}")
     d_avg = sum(delta_ms) / n_ev / 1e3  # seconds
     b_avg = sum(build_ms) / n_ev / 1e3
     srt = sorted(delta_ms)
@@ -403,6 +475,11 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if trace_info is not None:
+        result["config"]["trace"] = trace_info
+        result["config"]["lora_tokens_per_step"] = n_lora
+        result["config"]["step"] += (" (through the grouping cache)" if args.segment_cache
+                                     else "")
     del sets
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -188,6 +188,23 @@ sgmv_status sgmv_build_segments(const int32_t* lora_indices, int32_t M, int32_t 
                                 int32_t chunk_size, int32_t on_device, const sgmv_segments* seg,
                                 void* stream);
 
+/* Grouping cache across steps (Ascend article 4.2 and 5.3: a sequence keeps its adapter, so
+ * the grouping only changes when sequences join or leave the batch).
+ *   cache  [SGMV_CACHE_HEADER + M] int32, in the same memory as lora_indices (host for
+ *          on_device = 0, device for 1), owned by the caller; zero-fill it when it is
+ *          allocated (an all-zero cache is empty). It must not overlap lora_indices or seg.
+ * The cache holds the ids, M, L and chunk_size of the last build made into `seg` through this
+ * call with this cache. If all of them equal this call's, seg already holds the result and
+ * nothing is written (the device path still reads both id arrays, in one launch); otherwise
+ * seg is built exactly as sgmv_build_segments builds it and the cache is refreshed. Both
+ * give arrays identical to a fresh build. Anything else that writes seg (sgmv_build_segments,
+ * sgmv_lora_delta_ids) leaves the cache stale: zero cache[0] after such a write.
+ * Errors: as sgmv_build_segments, plus EINVAL for a null cache with M > 0. */
+#define SGMV_CACHE_HEADER 4
+sgmv_status sgmv_build_segments_cached(const int32_t* lora_indices, int32_t M, int32_t L,
+                                       int32_t chunk_size, int32_t on_device,
+                                       const sgmv_segments* seg, int32_t* cache, void* stream);
+
 /* One output slice: pool columns [n_begin, n_begin + n_len) land in columns [0, n_len) of
  * y, a device array [M][ldy] of the pool dtype (e.g. q, k and v of a fused projection). */
 typedef struct {
@@ -276,6 +293,10 @@ sgmv_status sgmv_build_segments_ex(const int32_t* lora_indices, int32_t M, int32
                                    int32_t chunk_size, int32_t on_device,
                                    const sgmv_segments* seg, const sgmv_launch_opts* opts,
                                    void* stream);
+sgmv_status sgmv_build_segments_cached_ex(const int32_t* lora_indices, int32_t M, int32_t L,
+                                          int32_t chunk_size, int32_t on_device,
+                                          const sgmv_segments* seg, int32_t* cache,
+                                          const sgmv_launch_opts* opts, void* stream);
 sgmv_status sgmv_shrink_ex(const void* x, int64_t ldx, int32_t M, const sgmv_pool* pool,
                            const sgmv_segments* seg, float* h, int64_t ldh,
                            const sgmv_launch_opts* opts, void* stream);

@@ -33,12 +33,14 @@ TILE_INTS = 32
 MAX_RANK = 64
 MAX_SLICES = 4
 DEVICE_BUILDER_MAX_L = 1024
+CACHE_HEADER = 4
 
 EXPORTED = [
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
     "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
-    "sgmv_lora_delta_ids_ex", "sgmv_status_string", "sgmv_version",
+    "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached", "sgmv_build_segments_cached_ex",
+    "sgmv_status_string", "sgmv_version",
 ]
 
 
@@ -111,6 +113,9 @@ def _load():
     lib.sgmv_lora_delta.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, vp]
     O = P(_LaunchOpts)
     lib.sgmv_build_segments_ex.argtypes = [vp, i32, i32, i32, i32, P(_Segments), O, vp]
+    lib.sgmv_build_segments_cached.argtypes = [vp, i32, i32, i32, i32, P(_Segments), vp, vp]
+    lib.sgmv_build_segments_cached_ex.argtypes = [vp, i32, i32, i32, i32, P(_Segments), vp, O,
+                                                  vp]
     lib.sgmv_shrink_ex.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), vp, i64, O, vp]
     lib.sgmv_expand_ex.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, O, vp]
     lib.sgmv_lora_delta_ex.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), P(_Slice), i32, O,
@@ -122,7 +127,8 @@ def _load():
     for f in ["sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
               "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
               "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
-              "sgmv_lora_delta_ids_ex"]:
+              "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached",
+              "sgmv_build_segments_cached_ex"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.sgmv_status_string.argtypes = [ctypes.c_int]
     lib.sgmv_status_string.restype = ctypes.c_char_p
@@ -331,6 +337,31 @@ def sgmv_build_segments(ids: torch.Tensor, L: int, chunk_size: int = 0, on_devic
     return seg
 
 
+def sgmv_segments_cache_alloc(M: int, device: Union[str, torch.device] = "cuda") -> torch.Tensor:
+    """An empty grouping cache for batches of M tokens: SGMV_CACHE_HEADER + M zeroed int32."""
+    return torch.zeros(CACHE_HEADER + max(int(M), 0), dtype=torch.int32, device=device)
+
+
+def sgmv_build_segments_cached(ids: torch.Tensor, seg: Segments, cache: torch.Tensor,
+                               on_device: bool = True,
+                               opts: Optional[LaunchOpts] = None) -> Segments:
+    """Build ``seg`` from ``ids`` unless the cache shows that seg already holds the build of
+    these very ids (then nothing is written). ``cache`` comes from sgmv_segments_cache_alloc
+    and is used with this seg only; on the device nothing syncs with the host."""
+    ids = ids.to(torch.int32).contiguous()
+    M = int(ids.numel())
+    dev = ids.device
+    if (dev.type == "cuda") != bool(on_device) or cache.device != dev:
+        raise ValueError("ids and cache must both be on the GPU (on_device) or on the CPU")
+    if cache.dtype != torch.int32 or not cache.is_contiguous() or cache.numel() < CACHE_HEADER + M:
+        raise ValueError("cache must be a contiguous int32 tensor of SGMV_CACHE_HEADER + M")
+    _check(_lib.sgmv_build_segments_cached_ex(_ptr(ids), M, seg.desc.L, seg.desc.chunk_size,
+                                              1 if on_device else 0, ctypes.byref(seg.desc),
+                                              _ptr(cache), _opts(opts), _stream(dev)),
+           "sgmv_build_segments_cached")
+    return seg
+
+
 # ---------------------------------------------------------------------------------------
 # shrink / expand / fused delta
 # ---------------------------------------------------------------------------------------
@@ -426,4 +457,5 @@ __all__ = [
     "LIB_PATH", "EXPORTED", "SgmvError", "Pool", "Segments", "LaunchOpts", "library",
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_alloc", "sgmv_build_segments",
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_lora_delta_ids",
+    "sgmv_segments_cache_alloc", "sgmv_build_segments_cached",
 ]

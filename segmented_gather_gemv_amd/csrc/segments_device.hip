@@ -16,13 +16,54 @@
 //    LDS, each wave walks its own contiguous range with a private row of per-key counts;
 //  * larger batches: the same counting in rounds of 1024 tokens with a running count per
 //    key, lanes of equal keys grouped by ballots.
-// Every global write index is checked against its array bound. Both kernels also clear the
-// control words of the fused call's exchange workspace, when the segments carry one.
+// Every global write index is checked against its array bound. The kernels also clear the
+// control words of the fused call's exchange workspace, when the segments carry one. Given a
+// grouping cache, a kernel first compares the batch's ids (and M, L, C) with the cached ones
+// and, if nothing changed, exits before writing anything: the segments already hold this
+// build.
 #include <climits>
 
+#include "cache.h"
 #include "segments_common.h"
 
 namespace sgmv {
+
+// ---------------------------------------------------------------------------------------
+// grouping cache (Ascend article 4.2, 5.3): a build is skipped when the ids, M, L and C equal
+// those of the last build made with the same cache
+// ---------------------------------------------------------------------------------------
+// True on every thread if the cache holds exactly this call's (M, L, C) and, for each token
+// i < M handled by this thread, `differ` says whether ids[i] differs from the cached id.
+__device__ __forceinline__ bool cache_unchanged(const int32_t* cache, int M, int L, int C,
+                                                bool differ) {
+  if (threadIdx.x == 0)
+    differ = differ || cache[0] != CACHE_TAG || cache[1] != M || cache[2] != L || cache[3] != C;
+  return !__syncthreads_or(differ);
+}
+
+__device__ __forceinline__ void cache_header(int32_t* cache, int M, int L, int C) {
+  if (threadIdx.x == 0) {
+    cache[0] = CACHE_TAG;
+    cache[1] = M;
+    cache[2] = L;
+    cache[3] = C;
+  }
+}
+
+// Strided compare of the whole batch (kernels that do not hold one token per thread).
+template <int NT>
+__device__ bool cache_hit(const int32_t* ids, int M, int L, int C, const int32_t* cache) {
+  bool differ = false;
+  for (int i = threadIdx.x; i < M; i += NT) differ |= ids[i] != cache[SGMV_CACHE_HEADER + i];
+  return cache_unchanged(cache, M, L, C, differ);
+}
+
+// Stores this build's ids and header; called once the build is known to run.
+template <int NT>
+__device__ void cache_store(const int32_t* ids, int M, int L, int C, int32_t* cache) {
+  for (int i = threadIdx.x; i < M; i += NT) cache[SGMV_CACHE_HEADER + i] = ids[i];
+  cache_header(cache, M, L, C);
+}
 
 // ---------------------------------------------------------------------------------------
 // small batches: M <= 1024
@@ -38,7 +79,7 @@ __global__ __launch_bounds__(NW * WAVE) void build_segments_small_kernel(
     const int32_t* __restrict__ ids, int M, int L, int C, int32_t* __restrict__ sorted,
     int32_t* __restrict__ indptr, int32_t* __restrict__ seg_lora, int32_t* __restrict__ tiles,
     int32_t* __restrict__ info, int seg_cap, int large_cap, int small_cap,
-    int32_t* __restrict__ xctl, int n_xctl) {
+    int32_t* __restrict__ xctl, int n_xctl, int32_t* __restrict__ cache) {
   constexpr int NT = NW * WAVE;
   extern __shared__ __align__(16) unsigned char smem[];
   const int NK = L + 1;
@@ -49,12 +90,18 @@ __global__ __launch_bounds__(NW * WAVE) void build_segments_small_kernel(
 
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
   const bool valid = t < M;
+  const int raw = valid ? ids[t] : 0;
+  if (cache != nullptr) {
+    if (cache_unchanged(cache, M, L, C, valid && cache[SGMV_CACHE_HEADER + t] != raw)) return;
+    if (valid) cache[SGMV_CACHE_HEADER + t] = raw;
+    cache_header(cache, M, L, C);
+  }
   for (int i = t; i < n_xctl; i += NT) xctl[i] = 0;
   for (int i = t; i < NK * (NW / 4); i += NT) reinterpret_cast<uint32_t*>(rc)[i] = 0;
   int key = -2;  // never equal to a real key (0..L)
   bool bad = false;
   if (valid) {
-    int id = ids[t];
+    int id = raw;
     if (id < -1 || id >= L) {
       bad = true;  // counted by the workgroup scan below
       id = -1;
@@ -148,7 +195,7 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
     const int32_t* __restrict__ ids, int M, int L, int C, int32_t* __restrict__ sorted,
     int32_t* __restrict__ indptr, int32_t* __restrict__ seg_lora, int32_t* __restrict__ tiles,
     int32_t* __restrict__ info, int seg_cap, int large_cap, int small_cap,
-    int32_t* __restrict__ xctl, int n_xctl) {
+    int32_t* __restrict__ xctl, int n_xctl, int32_t* __restrict__ cache) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int NK = L + 1;  // key L = "no adapter"
   uint8_t* rc = smem;
@@ -164,6 +211,10 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
+  if (cache != nullptr) {
+    if (cache_hit<BUILD_THREADS>(ids, M, L, C, cache)) return;
+    cache_store<BUILD_THREADS>(ids, M, L, C, cache);
+  }
   for (int i = tid; i < n_xctl; i += BUILD_THREADS) xctl[i] = 0;
   for (int i = tid; i < NK * (BUILD_WAVES / 4); i += BUILD_THREADS)
     reinterpret_cast<uint32_t*>(rc)[i] = 0;
@@ -390,7 +441,7 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_mid_kernel(
     const int32_t* __restrict__ ids, int M, int L, int C, int32_t* __restrict__ sorted,
     int32_t* __restrict__ indptr, int32_t* __restrict__ seg_lora, int32_t* __restrict__ tiles,
     int32_t* __restrict__ info, int seg_cap, int large_cap, int small_cap,
-    int32_t* __restrict__ xctl, int n_xctl) {
+    int32_t* __restrict__ xctl, int n_xctl, int32_t* __restrict__ cache) {
   extern __shared__ __align__(16) unsigned char smem[];
   const MidLds lay = mid_lds(M, L);
   const int NK = L + 1, nwords = (M + 31) / 32;
@@ -411,6 +462,10 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_mid_kernel(
   __shared__ int s_bad;
 
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  if (cache != nullptr) {
+    if (cache_hit<BUILD_THREADS>(ids, M, L, C, cache)) return;
+    cache_store<BUILD_THREADS>(ids, M, L, C, cache);
+  }
   for (int i = tid; i < n_xctl; i += BUILD_THREADS) xctl[i] = 0;
   for (int i = tid; i < BUILD_WAVES * NK; i += BUILD_THREADS) hist[i] = 0;
   for (int i = tid; i < NK; i += BUILD_THREADS) first[i] = INT_MAX;
@@ -597,14 +652,14 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_mid_kernel(
 hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_t* sorted,
                                  int32_t* indptr, int32_t* seg_lora, int32_t* tiles,
                                  int32_t* info, int seg_cap, int large_cap, int small_cap,
-                                 int32_t* xctl, int n_xctl, LaunchEvents ev,
+                                 int32_t* xctl, int n_xctl, int32_t* cache, LaunchEvents ev,
                                  hipStream_t stream) {
   if (M <= BUILD_THREADS) {
 #define SGMV_SMALL_BUILD(NW_)                                                                 \
   hipExtLaunchKernelGGL(build_segments_small_kernel<NW_>, dim3(1), dim3(NW_ * WAVE),         \
                         build_small_lds_bytes(L, NW_), stream, ev.start, ev.stop, 0, ids, M, \
                         L, C, sorted, indptr, seg_lora, tiles, info, seg_cap, large_cap,     \
-                        small_cap, xctl, n_xctl)
+                        small_cap, xctl, n_xctl, cache)
     if (M <= 4 * WAVE) SGMV_SMALL_BUILD(4);
     else if (M <= 8 * WAVE) SGMV_SMALL_BUILD(8);
     else SGMV_SMALL_BUILD(16);
@@ -613,12 +668,12 @@ hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_
     hipExtLaunchKernelGGL(build_segments_mid_kernel, dim3(1), dim3(BUILD_THREADS),
                           mid_lds(M, L).bytes, stream, ev.start, ev.stop, 0, ids, M, L, C,
                           sorted, indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap,
-                          xctl, n_xctl);
+                          xctl, n_xctl, cache);
   } else {
     hipExtLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(BUILD_THREADS),
                           build_lds_bytes(L), stream, ev.start, ev.stop, 0, ids, M, L, C, sorted,
                           indptr, seg_lora, tiles, info, seg_cap, large_cap, small_cap, xctl,
-                          n_xctl);
+                          n_xctl, cache);
   }
   return hipGetLastError();
 }

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstring>
 
+#include "cache.h"
 #include "common.h"
 #include "segments_host.h"
 
@@ -11,7 +12,7 @@ size_t build_lds_bytes(int L);
 hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_t* sorted,
                                  int32_t* indptr, int32_t* seg_lora, int32_t* tiles,
                                  int32_t* info, int seg_cap, int large_cap, int small_cap,
-                                 int32_t* xctl, int n_xctl, LaunchEvents ev,
+                                 int32_t* xctl, int n_xctl, int32_t* cache, LaunchEvents ev,
                                  hipStream_t stream);
 hipError_t launch_pool_pack(const void* a_user, const void* b_user, const sgmv_pool& p,
                             hipStream_t stream);
@@ -230,6 +231,43 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
   return hip_status(launch_delta_f32(mode, A, ev, s));
 }
 
+// Both builders; `cache` (may be null) as in sgmv_build_segments_cached.
+sgmv_status build_segments(const int32_t* lora_indices, int32_t M, int32_t L, int32_t chunk_size,
+                           int32_t on_device, const sgmv_segments* seg, int32_t* cache,
+                           const sgmv_launch_opts* opts, void* stream) {
+  if (M < 0 || L < 1 || chunk_size < 0 || (M > 0 && !lora_indices)) return SGMV_EINVAL;
+  if (!seg || seg->chunk_size != chunk_size || !seg_ok(seg, M, L)) return SGMV_EINVAL;
+  if (!opts_ok(opts)) return SGMV_EINVAL;
+  if (on_device == 0) {
+    if (cache) {
+      if (cache[0] == CACHE_TAG && cache[1] == M && cache[2] == L && cache[3] == chunk_size &&
+          (M == 0 ||
+           std::memcmp(cache + SGMV_CACHE_HEADER, lora_indices, sizeof(int32_t) * M) == 0))
+        return SGMV_OK;  // seg already holds this build (only successful ones are cached)
+      cache[0] = 0;  // a failed build leaves the cache empty
+    }
+    const int st = host_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
+                                       seg->seg_indptr, seg->seg_lora_ids, seg->tiles, seg->info,
+                                       seg->seg_cap, seg->large_cap, seg->small_cap);
+    if (cache && st == SGMV_OK) {
+      if (M > 0) std::memcpy(cache + SGMV_CACHE_HEADER, lora_indices, sizeof(int32_t) * M);
+      cache[1] = M;
+      cache[2] = L;
+      cache[3] = chunk_size;
+      cache[0] = CACHE_TAG;
+    }
+    return (sgmv_status)st;
+  }
+  if (L > SGMV_DEVICE_BUILDER_MAX_L) return SGMV_EUNSUPPORTED;
+  int32_t* xctl = static_cast<int32_t*>(seg->exchange);
+  const int n_xctl = xctl ? (seg->large_cap + seg->small_cap) * XCH_CTL_INTS : 0;
+  return hip_status(launch_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
+                                          seg->seg_indptr, seg->seg_lora_ids, seg->tiles,
+                                          seg->info, seg->seg_cap, seg->large_cap, seg->small_cap,
+                                          xctl, n_xctl, cache, events_of(opts),
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 }  // namespace sgmv
 
@@ -312,23 +350,22 @@ sgmv_status sgmv_build_segments_ex(const int32_t* lora_indices, int32_t M, int32
                                    int32_t chunk_size, int32_t on_device,
                                    const sgmv_segments* seg, const sgmv_launch_opts* opts,
                                    void* stream) {
-  if (M < 0 || L < 1 || chunk_size < 0 || (M > 0 && !lora_indices)) return SGMV_EINVAL;
-  if (!seg || seg->chunk_size != chunk_size || !seg_ok(seg, M, L)) return SGMV_EINVAL;
-  if (!opts_ok(opts)) return SGMV_EINVAL;
-  if (on_device == 0) {
-    return (sgmv_status)host_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
-                                            seg->seg_indptr, seg->seg_lora_ids, seg->tiles,
-                                            seg->info, seg->seg_cap, seg->large_cap,
-                                            seg->small_cap);
-  }
-  if (L > SGMV_DEVICE_BUILDER_MAX_L) return SGMV_EUNSUPPORTED;
-  int32_t* xctl = static_cast<int32_t*>(seg->exchange);
-  const int n_xctl = xctl ? (seg->large_cap + seg->small_cap) * XCH_CTL_INTS : 0;
-  return hip_status(launch_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
-                                          seg->seg_indptr, seg->seg_lora_ids, seg->tiles,
-                                          seg->info, seg->seg_cap, seg->large_cap, seg->small_cap,
-                                          xctl, n_xctl, events_of(opts),
-                                          static_cast<hipStream_t>(stream)));
+  return build_segments(lora_indices, M, L, chunk_size, on_device, seg, nullptr, opts, stream);
+}
+
+sgmv_status sgmv_build_segments_cached_ex(const int32_t* lora_indices, int32_t M, int32_t L,
+                                          int32_t chunk_size, int32_t on_device,
+                                          const sgmv_segments* seg, int32_t* cache,
+                                          const sgmv_launch_opts* opts, void* stream) {
+  if (!cache && M > 0) return SGMV_EINVAL;
+  return build_segments(lora_indices, M, L, chunk_size, on_device, seg, cache, opts, stream);
+}
+
+sgmv_status sgmv_build_segments_cached(const int32_t* lora_indices, int32_t M, int32_t L,
+                                       int32_t chunk_size, int32_t on_device,
+                                       const sgmv_segments* seg, int32_t* cache, void* stream) {
+  return sgmv_build_segments_cached_ex(lora_indices, M, L, chunk_size, on_device, seg, cache,
+                                       nullptr, stream);
 }
 
 sgmv_status sgmv_build_segments(const int32_t* lora_indices, int32_t M, int32_t L,

@@ -272,6 +272,31 @@ def algorithmic_flops(ids, rank, K: int, N: int) -> int:
 
 
 
+def decode_trace(steps: int, M: int = 256, L: int = 64, mean_len: int = 256,
+                 admit_every: int = 8, seed: int = SEED) -> torch.Tensor:
+    """Per-step token adapter ids [steps, M] of a decode batch with M slots, one token per
+    sequence per step. A sequence keeps its adapter (uniform on [0, L)) for its whole life,
+    whose length in steps is uniform on [1, 2 * mean_len - 1]; when it ends its slot holds -1
+    until the next admission, which fills every free slot with a new sequence every
+    `admit_every` steps. Step 0 starts with every slot occupied, each sequence with a
+    remaining life drawn like a new one's."""
+    g = torch.Generator().manual_seed(seed)
+    ids = torch.randint(0, L, (M,), generator=g, dtype=torch.int32)
+    left = torch.randint(1, 2 * mean_len, (M,), generator=g, dtype=torch.int32)
+    out = torch.empty(steps, M, dtype=torch.int32)
+    for s in range(steps):
+        if s > 0 and s % admit_every == 0:
+            free = ids < 0
+            n = int(free.sum())
+            if n:
+                ids[free] = torch.randint(0, L, (n,), generator=g, dtype=torch.int32)
+                left[free] = torch.randint(1, 2 * mean_len, (n,), generator=g, dtype=torch.int32)
+        out[s] = ids
+        left -= (ids >= 0).to(torch.int32)
+        ids[(ids >= 0) & (left <= 0)] = -1
+    return out
+
+
 BY_NAME = {"tiny": tiny, "decode": decode, "prefill": prefill, "mixed": mixed, "qkv": qkv}
 
 
