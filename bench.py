@@ -246,6 +246,8 @@ def main():
                     help="mean sequence life in steps for --trace")
     ap.add_argument("--trace-admit-every", type=int, default=8,
                     help="steps between admissions of new sequences for --trace")
+    ap.add_argument("--fold-scale", action="store_true",
+                    help="pack the pools with each adapter's scale folded into B")
     ap.add_argument("--segment-cache", action="store_true",
                     help="build through sgmv_build_segments_cached (with --trace)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -301,7 +303,8 @@ def main():
     with torch.cuda.stream(stream):
         a_dev, b_dev = w.a.to(dev), w.b.to(dev)
         for i in range(n_sets):
-            pool = sg.sgmv_pool_pack(a_dev, b_dev, w.rank.tolist(), w.alpha.tolist())
+            pool = sg.sgmv_pool_pack(a_dev, b_dev, w.rank.tolist(), w.alpha.tolist(),
+                                     fold_scale=args.fold_scale)
             x = w.x.to(dev)
             y = w.y0.to(dev)
             ids = w.ids.to(dev)
@@ -475,6 +478,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.fold_scale:
+        result["config"]["pool"] = "scale folded into B at pack time"
     if trace_info is not None:
         result["config"]["trace"] = trace_info
         result["config"]["lora_tokens_per_step"] = n_lora

@@ -90,6 +90,7 @@ typedef struct {
   int32_t dtype;    /* sgmv_dtype */
   int32_t rank_min; /* smallest r_l, set by sgmv_pool_pack (0 before): when it equals R_pad,
                        no adapter has padding and loads may start before r_l is read */
+  int32_t scale_folded; /* 1 if sgmv_pool_pack_ex folded scale_l into b (scale is then 1) */
 } sgmv_pool;
 
 /* Fill the dimensions of `pool` for L adapters of rank at most R_max, K inputs and N
@@ -110,6 +111,19 @@ sgmv_status sgmv_pool_init(int32_t L, int32_t R_max, int32_t K, int32_t N, int32
  * Errors: EINVAL (null pointers, rank out of range, non-finite alpha); EHIP. */
 sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t* rank,
                            const float* alpha, sgmv_pool* pool, void* stream);
+
+/* As sgmv_pool_pack, with flags (0 = sgmv_pool_pack):
+ *   SGMV_PACK_FOLD_SCALE  fold the scale into B at load time (Ascend article 2.1, 3.2: the
+ *     alpha/r factor may sit on either side of the expand, or be folded into B once when the
+ *     weights are loaded). Each stored B[l][n][j], j < r_l, becomes scale_l * B[l][n][j],
+ *     the product formed in fp32 (scale_l the fp32 quotient alpha_l / r_l) and rounded once
+ *     to the pool dtype (bf16: to nearest, ties to even); scale[l] is set to 1 and
+ *     pool->scale_folded to 1. For power-of-two scales (and no overflow or underflow) every
+ *     delta is bit-identical to the unfolded pool's; otherwise it differs by B's rounding.
+ * Errors: as sgmv_pool_pack, plus EINVAL for unknown flags. */
+#define SGMV_PACK_FOLD_SCALE 1
+sgmv_status sgmv_pool_pack_ex(const void* a_user, const void* b_user, const int32_t* rank,
+                              const float* alpha, int32_t flags, sgmv_pool* pool, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
  * Segments (Punica page, batching-effect and code sections; Ascend article 3.3, 4.2).

@@ -19,7 +19,8 @@ Sources, cited by page title and section:
     (alpha/r)(x A^T) B^T added to the base output), 2.1 (per-adapter rank r and alpha; a
     maximum rank), 3.3 (decode SGMV: group rows by adapter, compact descriptors: start row,
     row count, adapter index), 4.1 (row-count threshold between the vector and the matrix
-    unit), 5.2 (merged vs unmerged consistency) and 5.3 (rows without adapter are skipped).
+    unit), 3.2 (the scale on either side of the expand, or folded into B at load time),
+    5.2 (merged vs unmerged consistency) and 5.3 (rows without adapter are skipped).
 
 Readings where the pages are silent or disagree (each one is listed with its reason in the
 project's design notes):
@@ -34,6 +35,10 @@ project's design notes):
      last; chunks never cross buckets and follow bucket order.
   R6 scale_l = alpha_l / rank_l with the adapter's own rank.
   R7 the rank-r adapter uses only A[l, :r, :] and B[l, :, :r]; entries past r are ignored.
+  R8 folding the scale into B at load time (Ascend article 2.1 and 3.2 allow the factor on
+     either side of the expand, or folded into B) forms scale_l * B in fp32, with scale_l
+     the fp32 quotient alpha_l / r_l, and rounds it once to the pool's element type
+     (bf16: nearest, ties to even). The pages fix no precision for this step.
 """
 from __future__ import annotations
 
@@ -197,6 +202,39 @@ def lora_delta(x: np.ndarray, y0: np.ndarray, ids: np.ndarray, a: np.ndarray, b:
     return y
 
 
+def round_bf16(v) -> np.ndarray:
+    """Round fp32 values to bfloat16 (the upper 16 bits of an fp32 pattern), to nearest with
+    ties to even, returned as fp32. Written from the definition on the bit pattern: add half
+    of the dropped range, minus one unless the kept part is odd, then drop the low 16 bits;
+    a carry moves into the exponent (up to infinity). NaN stays a quiet NaN."""
+    bits = np.ascontiguousarray(np.asarray(v, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    keep_odd = (bits >> np.uint64(16)) & np.uint64(1)
+    rounded = ((bits + np.uint64(0x7FFF) + keep_odd) >> np.uint64(16)) << np.uint64(16)
+    is_nan = ((bits & np.uint64(0x7F800000)) == np.uint64(0x7F800000)) & \
+        ((bits & np.uint64(0x007FFFFF)) != np.uint64(0))
+    quiet = ((bits >> np.uint64(16)) << np.uint64(16)) | np.uint64(0x00400000)
+    out = np.where(is_nan, quiet, rounded).astype(np.uint32)
+    return out.view(np.float32)
+
+
+def fold_scale(b: np.ndarray, rank: np.ndarray, alpha: np.ndarray,
+               bf16: bool) -> Tuple[np.ndarray, np.ndarray]:
+    """B with each adapter's scale folded in (reading R8): for j < r_l,
+    B'[l, n, j] = round(fp32(scale_l) * fp32(B[l, n, j])) with scale_l = fp32(alpha_l) /
+    fp32(r_l) in fp32 arithmetic; round is round_bf16 for a bf16 pool and the identity for
+    an fp32 pool (the fp32 product is already rounded). Entries j >= r_l are set to 0.
+    Returns (B' as fp32 (L, N, R), alpha' = r so that every remaining scale alpha'/r is 1)."""
+    b32 = np.asarray(b, dtype=np.float32)
+    L, N, R = b32.shape
+    out = np.zeros_like(b32)
+    for l in range(L):
+        r = int(rank[l])
+        s32 = np.float32(alpha[l]) / np.float32(r)        # fp32 division (IEEE, nearest)
+        prod = b32[l, :, :r] * s32                         # fp32 products (IEEE, nearest)
+        out[l, :, :r] = round_bf16(prod) if bf16 else prod
+    return out, np.asarray(rank, dtype=np.float64).copy()
+
+
 def max_segments(M: int, L: int, chunk_size: int) -> int:
     """Upper bound on the number of segments: at most one per distinct adapter, plus one
     per extra chunk when chunking."""
@@ -208,5 +246,5 @@ def max_segments(M: int, L: int, chunk_size: int) -> int:
 
 __all__ = [
     "BadAdapterId", "validate_ids", "segments", "tiles", "shrink", "expand", "lora_delta",
-    "max_segments",
+    "max_segments", "round_bf16", "fold_scale",
 ]

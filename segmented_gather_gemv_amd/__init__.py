@@ -34,13 +34,14 @@ MAX_RANK = 64
 MAX_SLICES = 4
 DEVICE_BUILDER_MAX_L = 1024
 CACHE_HEADER = 4
+FOLD_SCALE = 1
 
 EXPORTED = [
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
     "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
     "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached", "sgmv_build_segments_cached_ex",
-    "sgmv_status_string", "sgmv_version",
+    "sgmv_pool_pack_ex", "sgmv_status_string", "sgmv_version",
 ]
 
 
@@ -55,7 +56,7 @@ class _Pool(ctypes.Structure):
                 ("scale", ctypes.c_void_p), ("L", ctypes.c_int32), ("R_max", ctypes.c_int32),
                 ("R_pad", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("K_pad", ctypes.c_int32), ("N_pad", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("rank_min", ctypes.c_int32)]
+                ("rank_min", ctypes.c_int32), ("scale_folded", ctypes.c_int32)]
 
 
 class _Segments(ctypes.Structure):
@@ -106,6 +107,7 @@ def _load():
     P = ctypes.POINTER
     lib.sgmv_pool_init.argtypes = [i32, i32, i32, i32, i32, P(_Pool), P(sz), P(sz)]
     lib.sgmv_pool_pack.argtypes = [vp, vp, vp, vp, P(_Pool), vp]
+    lib.sgmv_pool_pack_ex.argtypes = [vp, vp, vp, vp, i32, P(_Pool), vp]
     lib.sgmv_segments_init.argtypes = [i32, i32, i32, P(_Segments)]
     lib.sgmv_build_segments.argtypes = [vp, i32, i32, i32, i32, P(_Segments), vp]
     lib.sgmv_shrink.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), vp, i64, vp]
@@ -128,7 +130,7 @@ def _load():
               "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
               "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
               "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached",
-              "sgmv_build_segments_cached_ex"]:
+              "sgmv_build_segments_cached_ex", "sgmv_pool_pack_ex"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.sgmv_status_string.argtypes = [ctypes.c_int]
     lib.sgmv_status_string.restype = ctypes.c_char_p
@@ -217,9 +219,10 @@ def sgmv_pool_init(L: int, R_max: int, K: int, N: int, dtype: torch.dtype,
 
 
 def sgmv_pool_pack(a: torch.Tensor, b: torch.Tensor, rank: Sequence[int],
-                   alpha: Sequence[float]) -> Pool:
+                   alpha: Sequence[float], fold_scale: bool = False) -> Pool:
     """Pack user-layout adapters A (L, R, K) and B (L, N, R) (device tensors of the pool
-    dtype) with per-adapter rank and alpha into a new pool."""
+    dtype) with per-adapter rank and alpha into a new pool. ``fold_scale`` stores
+    alpha/r * B (formed in fp32, rounded once to the pool dtype) and unit scales."""
     if a.dim() != 3 or b.dim() != 3:
         raise ValueError("a must be (L, R, K) and b (L, N, R)")
     L, R, K = a.shape
@@ -235,8 +238,9 @@ def sgmv_pool_pack(a: torch.Tensor, b: torch.Tensor, rank: Sequence[int],
     alpha_h = torch.as_tensor(alpha, dtype=torch.float32).cpu().contiguous()
     if rank_h.numel() != L or alpha_h.numel() != L:
         raise ValueError("rank and alpha need one entry per adapter")
-    _check(_lib.sgmv_pool_pack(_ptr(a), _ptr(b), _ptr(rank_h), _ptr(alpha_h),
-                               ctypes.byref(pool.desc), _stream(a.device)), "sgmv_pool_pack")
+    _check(_lib.sgmv_pool_pack_ex(_ptr(a), _ptr(b), _ptr(rank_h), _ptr(alpha_h),
+                                  FOLD_SCALE if fold_scale else 0, ctypes.byref(pool.desc),
+                                  _stream(a.device)), "sgmv_pool_pack")
     return pool
 
 

@@ -15,7 +15,7 @@ hipError_t launch_build_segments(const int32_t* ids, int M, int L, int C, int32_
                                  int32_t* xctl, int n_xctl, int32_t* cache, LaunchEvents ev,
                                  hipStream_t stream);
 hipError_t launch_pool_pack(const void* a_user, const void* b_user, const sgmv_pool& p,
-                            hipStream_t stream);
+                            bool fold_scale, hipStream_t stream);
 hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, LaunchEvents ev,
                              hipStream_t stream);
 hipError_t launch_delta_f32(int mode, DeltaArgs A, LaunchEvents ev, hipStream_t stream);
@@ -310,9 +310,11 @@ sgmv_status sgmv_pool_init(int32_t L, int32_t R_max, int32_t K, int32_t N, int32
   return SGMV_OK;
 }
 
-sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t* rank,
-                           const float* alpha, sgmv_pool* pool, void* stream) {
+sgmv_status sgmv_pool_pack_ex(const void* a_user, const void* b_user, const int32_t* rank,
+                              const float* alpha, int32_t flags, sgmv_pool* pool, void* stream) {
   if (!a_user || !b_user || !rank || !alpha || !pool_ok(pool)) return SGMV_EINVAL;
+  if ((flags & ~SGMV_PACK_FOLD_SCALE) != 0) return SGMV_EINVAL;
+  const bool fold = (flags & SGMV_PACK_FOLD_SCALE) != 0;
   const int L = pool->L;
   float* scale = static_cast<float*>(std::malloc(sizeof(float) * (size_t)L));
   if (!scale) return SGMV_EINVAL;
@@ -330,10 +332,22 @@ sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t
   hipError_t e = hipMemcpyAsync(pool->rank, rank, sizeof(int32_t) * L, hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(pool->scale, scale, sizeof(float) * L, hipMemcpyHostToDevice, s);
+  // folding: B is packed with the true scales, then the stored scales become 1
+  if (e == hipSuccess) e = launch_pool_pack(a_user, b_user, *pool, fold, s);
+  if (e == hipSuccess && fold) {
+    for (int l = 0; l < L; ++l) scale[l] = 1.f;
+    e = hipMemcpyAsync(pool->scale, scale, sizeof(float) * L, hipMemcpyHostToDevice, s);
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(s);  // host staging buffers end here
   std::free(scale);
   if (e != hipSuccess) return SGMV_EHIP;
-  return hip_status(launch_pool_pack(a_user, b_user, *pool, s));
+  pool->scale_folded = fold ? 1 : 0;
+  return SGMV_OK;
+}
+
+sgmv_status sgmv_pool_pack(const void* a_user, const void* b_user, const int32_t* rank,
+                           const float* alpha, sgmv_pool* pool, void* stream) {
+  return sgmv_pool_pack_ex(a_user, b_user, rank, alpha, 0, pool, stream);
 }
 
 sgmv_status sgmv_segments_init(int32_t M, int32_t L, int32_t chunk_size, sgmv_segments* seg) {

@@ -11,6 +11,9 @@
   * closed forms: all tokens without adapter leave y bit-identical, power-of-two scales act
     exactly, an adapter of rank r stored in a wider pool equals the same adapter in a pool
     of rank r, permuting tokens permutes rows;
+  * bf16 rounding of the scale fold: hand-worked bit patterns, agreement with torch's
+    float32 -> bfloat16 conversion, exactness for power-of-two scales, the half-unit error
+    bound on the folded B and on the folded delta;
   * planted mistakes: plausible bugs injected into copies of the oracle are each caught by
     at least one of the checks above.
 """
@@ -462,3 +465,167 @@ def test_planted_delta_mistakes_are_caught(kind):
     # and the unmutated variant passes them all
     ok = _delta_variant("none")
     assert check_merged(ok) and check_single_adapter(ok) and check_brute(ok) and check_rank_pool(ok)
+
+
+# ---------------------------------------------------------------------------------------
+# scale folded into B (reading R8): bf16 rounding and the fold
+# ---------------------------------------------------------------------------------------
+# (fp32 bit pattern, bf16 result as an fp32 pattern), worked out by hand from the definition
+# of round-to-nearest-even on the low 16 bits
+ROUND_CASES = [
+    (0x3F800000, 0x3F800000),  # 1.0
+    (0x3F808000, 0x3F800000),  # 1 + 2^-8: halfway, kept part even -> down
+    (0x3F818000, 0x3F820000),  # 1 + 2^-7 + 2^-8: halfway, kept part odd -> up
+    (0x3F808001, 0x3F810000),  # just above halfway -> up
+    (0x3F807FFF, 0x3F800000),  # just below halfway -> down
+    (0xBF808000, 0xBF800000),  # negative halfway, even -> toward zero here
+    (0xBF818000, 0xBF820000),  # negative halfway, odd -> away from zero
+    (0x3FFFFFFF, 0x40000000),  # carry into the exponent
+    (0x7F7FFFFF, 0x7F800000),  # largest finite fp32 rounds to infinity
+    (0x7F800000, 0x7F800000),  # infinity
+    (0x00008000, 0x00000000),  # subnormal halfway, even
+    (0x00018000, 0x00020000),  # subnormal halfway, odd
+    (0x80000000, 0x80000000),  # -0
+]
+
+
+def _bits(v):
+    return np.asarray(v, dtype=np.float32).view(np.uint32)
+
+
+def check_round_cases(round_fn):
+    src = np.asarray([c[0] for c in ROUND_CASES], dtype=np.uint32).view(np.float32)
+    want = np.asarray([c[1] for c in ROUND_CASES], dtype=np.uint32)
+    got = _bits(round_fn(src))
+    nan = round_fn(np.asarray([0x7FC00001, 0xFF800001], dtype=np.uint32).view(np.float32))
+    return bool(np.array_equal(got, want)) and bool(np.isnan(nan).all())
+
+
+def test_round_bf16_hand_values():
+    assert check_round_cases(oracle.round_bf16)
+
+
+def test_round_bf16_matches_torch_cast():
+    """torch's CPU float32 -> bfloat16 conversion (a library routine) on 2^20 random fp32 bit
+    patterns, NaNs aside (their payloads may differ)."""
+    import torch
+    pat = np.random.default_rng(5).integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64)
+    v = pat.astype(np.uint32).view(np.float32)
+    keep = ~np.isnan(v)
+    ref = torch.from_numpy(v.copy()).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(_bits(oracle.round_bf16(v))[keep], _bits(ref)[keep])
+
+
+def _bf16_problem(rng, M, K, N, L, R, ranks):
+    x, y0, ids, A, B, rank, _ = rand_problem(rng, M, K, N, L, R, ranks=ranks)
+    # bf16-representable operands, as a bf16 pool holds them
+    A = oracle.round_bf16(A.astype(np.float32)).astype(np.float64)
+    B = oracle.round_bf16(B.astype(np.float32)).astype(np.float64)
+    x = oracle.round_bf16(x.astype(np.float32)).astype(np.float64)
+    return x, y0, ids, A, B, rank
+
+
+def check_fold_power_of_two(fold_fn):
+    """Power-of-two scales: the folded B is scale * B exactly, and the folded delta equals
+    the unfolded one bit for bit."""
+    rng = np.random.default_rng(21)
+    ranks = [4, 2, 3, 1]
+    x, y0, ids, A, B, rank = _bf16_problem(rng, 12, 16, 20, 4, 4, ranks)
+    alpha = np.asarray([8.0, 1.0, 0.75, 0.25]) * np.asarray(ranks)   # scales 8, 1, 0.75, 0.25
+    alpha[2] = 0.5 * ranks[2]                                          # keep powers of two
+    for bf16 in (True, False):
+        Bf, alpha1 = fold_fn(B, rank, alpha, bf16)
+        for l, r in enumerate(ranks):
+            if not np.array_equal(Bf[l, :, :r], B[l, :, :r] * (alpha[l] / r)):
+                return False
+        if not np.array_equal(oracle.lora_delta(x, y0, ids, A, Bf, rank, alpha1),
+                              oracle.lora_delta(x, y0, ids, A, B, rank, alpha)):
+            return False
+    return True
+
+
+def test_fold_power_of_two_is_exact():
+    assert check_fold_power_of_two(oracle.fold_scale)
+
+
+def check_fold_error_bound(fold_fn):
+    """Other scales: every folded entry is a bf16 value within half a bf16 unit (2^-8
+    relative) of the fp32 product, and each folded delta element is within that bound (plus
+    the fp32 product and quotient roundings, 2^-23) of the exact one, term by term."""
+    rng = np.random.default_rng(22)
+    ranks = [5, 3, 7]
+    x, y0, ids, A, B, rank = _bf16_problem(rng, 30, 24, 40, 3, 8, ranks)
+    alpha = np.asarray([3.0, 10.0, 0.3])
+    Bf, alpha1 = fold_fn(B, rank, alpha, True)
+    for l, r in enumerate(ranks):
+        prod = B[l, :, :r].astype(np.float32) * (np.float32(alpha[l]) / np.float32(r))
+        f = Bf[l, :, :r].astype(np.float32)
+        if np.any(_bits(f) & 0xFFFF):
+            return False
+        if np.any(np.abs(f.astype(np.float64) - prod) > 2.0 ** -8 * np.abs(prod.astype(np.float64))):
+            return False
+    zero = np.zeros_like(y0)
+    yf = oracle.lora_delta(x, zero, ids, A, Bf, rank, alpha1)
+    yu = oracle.lora_delta(x, zero, ids, A, B, rank, alpha)
+    for t in range(x.shape[0]):
+        l = int(ids[t])
+        if l < 0:
+            if np.any(yf[t] != 0):
+                return False
+            continue
+        r = ranks[l]
+        h = A[l, :r, :] @ x[t]
+        bound = (2.0 ** -8 + 2.0 ** -23) * (np.abs(B[l, :, :r] * (alpha[l] / r)) @ np.abs(h))
+        if np.any(np.abs(yf[t] - yu[t]) > bound + 1e-12 * np.max(np.abs(yu[t]))):
+            return False
+    # a scale that is not a power of two does change some entries
+    return not np.array_equal(Bf[0, :, :5], B[0, :, :5] * (alpha[0] / 5))
+
+
+def test_fold_error_bound():
+    assert check_fold_error_bound(oracle.fold_scale)
+
+
+def _round_variant(kind):
+    def fn(v):
+        bits = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+        if kind == "truncate":
+            out = (bits >> 16) << 16
+        elif kind == "ties_away":
+            out = ((bits + 0x8000) >> 16) << 16
+        else:  # "ties_up_only_even_bit_ignored": always adds half minus one
+            out = ((bits + 0x7FFF) >> 16) << 16
+        return out.astype(np.uint32).view(np.float32)
+    return fn
+
+
+def _fold_variant(kind):
+    def fn(b, rank, alpha, bf16):
+        b32 = np.asarray(b, dtype=np.float32)
+        out = np.zeros_like(b32)
+        R = b32.shape[2]
+        for l in range(b32.shape[0]):
+            r = int(rank[l])
+            s = np.float32(alpha[l]) / np.float32(R if kind == "scale_by_max_rank" else r)
+            if kind == "no_scale":
+                s = np.float32(1.0)
+            prod = b32[l, :, :r] * s
+            if bf16:
+                prod = _round_variant("truncate")(prod) if kind == "truncate" else \
+                    oracle.round_bf16(prod)
+            out[l, :, :r] = prod
+        return out, np.asarray(rank, dtype=np.float64).copy()
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["truncate", "ties_away", "ties_up_only_even_bit_ignored"])
+def test_planted_rounding_mistakes_are_caught(kind):
+    assert not check_round_cases(_round_variant(kind))
+
+
+@pytest.mark.parametrize("kind", ["no_scale", "scale_by_max_rank", "truncate"])
+def test_planted_fold_mistakes_are_caught(kind):
+    fn = _fold_variant(kind)
+    assert not (check_fold_power_of_two(fn) and check_fold_error_bound(fn))
+    ok = _fold_variant("none")
+    assert check_fold_power_of_two(ok) and check_fold_error_bound(ok)
