@@ -216,6 +216,91 @@ def cpu_baseline(w, seconds: float):
                       f"{os.cpu_count()} visible host cores"}
 
 
+def merge_bench(args):
+    """Merged weight (sgmv_merge_adapter) on the decode shapes: W 4096 x 4096 bf16, rank 16.
+    Times the merge kernel (dispatch events, W and W' rotating over sets larger than the
+    last-level cache), the base GEMM x W^T of the decode batch (torch.matmul, the vendor GEMM
+    library) and the unmerged delta of a batch whose 256 tokens all use one adapter, and
+    reports the merge as HBM bandwidth against the peak plus the number of steps after which
+    merging pays for itself (Ascend article 4.4)."""
+    import torch
+    import segmented_gather_gemv_amd as sg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    ev = HipEvents()
+    w = workloads.get("decode")
+    N, K = w.N, w.K
+    e = 2
+    n_sets = max(2, -(-2 * MALL_BYTES // (2 * N * K * e)))
+    g = torch.Generator().manual_seed(7)
+    with torch.cuda.stream(stream):
+        pool = sg.sgmv_pool_pack(w.a.to(dev), w.b.to(dev), w.rank.tolist(), w.alpha.tolist())
+        Ws = [(torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+              for _ in range(n_sets)]
+        Wo = [torch.empty_like(Ws[0]) for _ in range(n_sets)]
+        x = w.x.to(dev)
+        ids = torch.zeros(w.M, dtype=torch.int32, device=dev)  # one adapter for the batch
+        ys = [w.y0.to(dev) for _ in range(n_sets)]
+        seg = sg.sgmv_segments_alloc(w.M, w.L, 0, dev)
+    torch.cuda.synchronize()
+    log(f"merge bench: W {N}x{K} bf16 x {n_sets} sets, rank {int(w.rank[0])}")
+
+    def timed(fn, reps):
+        pairs = [ev.create(2) for _ in range(reps)]
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                fn(i, None)
+            torch.cuda.synchronize()
+            for i in range(reps):
+                fn(i, sg.LaunchOpts(pairs[i][0], pairs[i][1]))
+        torch.cuda.synchronize()
+        ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+        for p_ in pairs:
+            ev.destroy(p_)
+        return sum(ms) / len(ms) * 1e3  # us
+
+    reps = max(16, min(args.steps, 200))
+    merge_us = timed(lambda i, o: sg.sgmv_merge_adapter(Ws[i % n_sets], pool, 0,
+                                                       out=Wo[i % n_sets], opts=o), reps)
+    delta_us = timed(lambda i, o: sg.sgmv_lora_delta_ids(ids, x, pool, seg, ys[i % n_sets],
+                                                         opts=o), reps)
+    # base GEMM y = x W^T through torch (events around each call on the stream)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            torch.matmul(x, Ws[i % n_sets].t())
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for i in range(reps):
+            evs[i][0].record(stream)
+            torch.matmul(x, Ws[i % n_sets].t())
+            evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    gemm_us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    r = int(w.rank[0])
+    alg = 2 * N * K * e + r * (N + K) * e
+    gbps = alg / (merge_us * 1e-6) / 1e9
+    log(f"merge {merge_us:.2f} us ({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS * 100:.1f}% of peak) | "
+        f"base GEMM {gemm_us:.2f} us | one-adapter delta {delta_us:.2f} us | break-even "
+        f"{merge_us / delta_us:.1f} steps")
+    print(json.dumps({
+        "metric": "merged-weight build (sgmv_merge_adapter) HBM GB/s, W 4096x4096 bf16 r=16",
+        "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": merge_us / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "merge adapter 0 of the decode pool into a random base weight",
+                   "N": N, "K": K, "rank": r, "buffer_sets": n_sets,
+                   "merge_kernel_us": merge_us, "base_gemm_us_bs256": gemm_us,
+                   "unmerged_delta_us_one_adapter_bs256": delta_us,
+                   "break_even_steps": merge_us / delta_us,
+                   "algorithmic_bytes_per_launch": alg},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +335,8 @@ def main():
                     help="pack the pools with each adapter's scale folded into B")
     ap.add_argument("--segment-cache", action="store_true",
                     help="build through sgmv_build_segments_cached (with --trace)")
+    ap.add_argument("--merge", action="store_true",
+                    help="time the merged-weight kernel against the base GEMM + delta")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain device copy of --copy-mib MiB (counter scale)")
     ap.add_argument("--copy-mib", type=int, default=256)
@@ -265,6 +352,9 @@ def main():
         return
     if args.calibration_copy:
         calibration_copy(args)
+        return
+    if args.merge:
+        merge_bench(args)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

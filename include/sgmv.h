@@ -326,6 +326,27 @@ sgmv_status sgmv_lora_delta_ids_ex(const int32_t* lora_indices, const void* x, i
                                    const sgmv_slice* out, int32_t n_slices,
                                    const sgmv_launch_opts* opts, void* stream);
 
+/* ------------------------------------------------------------------------------------ *
+ * Merged weight of one adapter (Ascend article 1.1 and 4.4: for a batch that holds only one
+ * or two long-lived adapters, merging each into a copy of the base weight and running the
+ * plain GEMM can beat the unmerged delta; Punica page, SGMV section: merged and unmerged
+ * forms give the same product).
+ *   w       device [N][ldw] of the pool dtype: the base weight of y = x W^T (row n = output n,
+ *           column k = input k), N = pool->N, K = pool->K, ldw >= K
+ *   w_out   device [N][ldo], ldo >= K; may be w itself (in place), must not overlap it
+ *           otherwise
+ *   adapter l in [0, pool->L)
+ * w_out[n][k] = w[n][k] + scale_l * sum_{j < r_l} B[l][n][j] * A[l][j][k], the product summed
+ * in fp32 (exact bf16 products) and the result rounded once to the pool dtype (bf16: to
+ * nearest even). Ranks at or past r_l are never read. To go back to the unmerged weight keep
+ * w (merge out of place): in bf16, merging -scale does not undo a merge exactly.
+ * Errors: EINVAL (null pointers, ld < K, adapter out of range, an invalid pool); EHIP. */
+sgmv_status sgmv_merge_adapter(const void* w, int64_t ldw, void* w_out, int64_t ldo,
+                               const sgmv_pool* pool, int32_t adapter, void* stream);
+sgmv_status sgmv_merge_adapter_ex(const void* w, int64_t ldw, void* w_out, int64_t ldo,
+                                  const sgmv_pool* pool, int32_t adapter,
+                                  const sgmv_launch_opts* opts, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* sgmv_status_string(sgmv_status s);
 

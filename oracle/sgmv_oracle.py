@@ -235,6 +235,17 @@ def fold_scale(b: np.ndarray, rank: np.ndarray, alpha: np.ndarray,
     return out, np.asarray(rank, dtype=np.float64).copy()
 
 
+def merge_weight(w: np.ndarray, a: np.ndarray, b: np.ndarray, rank: np.ndarray,
+                 alpha: np.ndarray, l: int) -> np.ndarray:
+    """Adapter l merged into a base weight (Ascend article 1.1 and 4.4; Punica page, SGMV
+    section): W' = W + (alpha_l / r_l) * B[l, :, :r_l] @ A[l, :r_l, :] in fp64, where W (N, K)
+    is the base weight of y = x W^T, so that x W'^T = x W^T + the adapter's delta."""
+    r = int(rank[l])
+    w64 = np.asarray(w, dtype=np.float64)
+    return w64 + (float(alpha[l]) / r) * (np.asarray(b[l, :, :r], np.float64)
+                                          @ np.asarray(a[l, :r, :], np.float64))
+
+
 def max_segments(M: int, L: int, chunk_size: int) -> int:
     """Upper bound on the number of segments: at most one per distinct adapter, plus one
     per extra chunk when chunking."""
@@ -246,5 +257,5 @@ def max_segments(M: int, L: int, chunk_size: int) -> int:
 
 __all__ = [
     "BadAdapterId", "validate_ids", "segments", "tiles", "shrink", "expand", "lora_delta",
-    "max_segments", "round_bf16", "fold_scale",
+    "max_segments", "round_bf16", "fold_scale", "merge_weight",
 ]

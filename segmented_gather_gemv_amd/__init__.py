@@ -41,7 +41,8 @@ EXPORTED = [
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
     "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
     "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached", "sgmv_build_segments_cached_ex",
-    "sgmv_pool_pack_ex", "sgmv_status_string", "sgmv_version",
+    "sgmv_pool_pack_ex", "sgmv_merge_adapter", "sgmv_merge_adapter_ex", "sgmv_status_string",
+    "sgmv_version",
 ]
 
 
@@ -108,6 +109,7 @@ def _load():
     lib.sgmv_pool_init.argtypes = [i32, i32, i32, i32, i32, P(_Pool), P(sz), P(sz)]
     lib.sgmv_pool_pack.argtypes = [vp, vp, vp, vp, P(_Pool), vp]
     lib.sgmv_pool_pack_ex.argtypes = [vp, vp, vp, vp, i32, P(_Pool), vp]
+    lib.sgmv_merge_adapter.argtypes = [vp, i64, vp, i64, P(_Pool), i32, vp]
     lib.sgmv_segments_init.argtypes = [i32, i32, i32, P(_Segments)]
     lib.sgmv_build_segments.argtypes = [vp, i32, i32, i32, i32, P(_Segments), vp]
     lib.sgmv_shrink.argtypes = [vp, i64, i32, P(_Pool), P(_Segments), vp, i64, vp]
@@ -126,11 +128,13 @@ def _load():
                                         i32, vp]
     lib.sgmv_lora_delta_ids_ex.argtypes = [vp, vp, i64, i32, P(_Pool), P(_Segments), P(_Slice),
                                            i32, O, vp]
+    lib.sgmv_merge_adapter_ex.argtypes = [vp, i64, vp, i64, P(_Pool), i32, O, vp]
     for f in ["sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
               "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
               "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
               "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached",
-              "sgmv_build_segments_cached_ex", "sgmv_pool_pack_ex"]:
+              "sgmv_build_segments_cached_ex", "sgmv_pool_pack_ex", "sgmv_merge_adapter",
+              "sgmv_merge_adapter_ex"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.sgmv_status_string.argtypes = [ctypes.c_int]
     lib.sgmv_status_string.restype = ctypes.c_char_p
@@ -457,9 +461,28 @@ def sgmv_lora_delta_ids(ids: torch.Tensor, x: torch.Tensor, pool: Pool, seg: Seg
                                        _opts(opts), _stream(x.device)), "sgmv_lora_delta_ids")
 
 
+def sgmv_merge_adapter(w: torch.Tensor, pool: Pool, adapter: int,
+                       out: Optional[torch.Tensor] = None,
+                       opts: Optional[LaunchOpts] = None) -> torch.Tensor:
+    """W' = W + scale_l B_l A_l for the base weight w (N, K) of y = x W^T, into ``out`` (a new
+    tensor by default; ``out=w`` merges in place)."""
+    if w.dim() != 2 or tuple(w.shape) != (pool.N, pool.K):
+        raise ValueError(f"w must be (N, K) = ({pool.N}, {pool.K})")
+    if w.dtype != pool.dtype or w.device != pool.a.device or w.stride(1) != 1:
+        raise ValueError("w must be a row-contiguous tensor of the pool's dtype and device")
+    if out is None:
+        out = torch.empty_like(w, memory_format=torch.contiguous_format)
+    if tuple(out.shape) != tuple(w.shape) or out.dtype != w.dtype or out.stride(1) != 1:
+        raise ValueError("out must match w")
+    _check(_lib.sgmv_merge_adapter_ex(_ptr(w), w.stride(0), _ptr(out), out.stride(0),
+                                      ctypes.byref(pool.desc), int(adapter), _opts(opts),
+                                      _stream(w.device)), "sgmv_merge_adapter")
+    return out
+
+
 __all__ = [
     "LIB_PATH", "EXPORTED", "SgmvError", "Pool", "Segments", "LaunchOpts", "library",
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_alloc", "sgmv_build_segments",
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_lora_delta_ids",
-    "sgmv_segments_cache_alloc", "sgmv_build_segments_cached",
+    "sgmv_segments_cache_alloc", "sgmv_build_segments_cached", "sgmv_merge_adapter",
 ]

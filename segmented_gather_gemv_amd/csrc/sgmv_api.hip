@@ -21,6 +21,8 @@ hipError_t launch_delta_bf16(int mode, bool aligned, DeltaArgs A, LaunchEvents e
 hipError_t launch_delta_f32(int mode, DeltaArgs A, LaunchEvents ev, hipStream_t stream);
 hipError_t launch_delta_bf16_build(bool aligned, DeltaArgs A, LaunchEvents ev,
                                    hipStream_t stream);
+hipError_t launch_merge(const void* w, int64_t ldw, void* w_out, int64_t ldo, const sgmv_pool& p,
+                        int l, LaunchEvents ev, hipStream_t stream);
 
 namespace {
 
@@ -450,6 +452,20 @@ sgmv_status sgmv_lora_delta_ids_ex(const int32_t* lora_indices, const void* x, i
                                                 seg, &ob, stream);
   if (st != SGMV_OK) return st;
   return sgmv_lora_delta_ex(x, ldx, M, pool, seg, out, n_slices, &od, stream);
+}
+
+sgmv_status sgmv_merge_adapter_ex(const void* w, int64_t ldw, void* w_out, int64_t ldo,
+                                  const sgmv_pool* pool, int32_t adapter,
+                                  const sgmv_launch_opts* opts, void* stream) {
+  if (!w || !w_out || !pool_ok(pool) || !opts_ok(opts)) return SGMV_EINVAL;
+  if (adapter < 0 || adapter >= pool->L || ldw < pool->K || ldo < pool->K) return SGMV_EINVAL;
+  return hip_status(launch_merge(w, ldw, w_out, ldo, *pool, adapter, events_of(opts),
+                                 static_cast<hipStream_t>(stream)));
+}
+
+sgmv_status sgmv_merge_adapter(const void* w, int64_t ldw, void* w_out, int64_t ldo,
+                               const sgmv_pool* pool, int32_t adapter, void* stream) {
+  return sgmv_merge_adapter_ex(w, ldw, w_out, ldo, pool, adapter, nullptr, stream);
 }
 
 sgmv_status sgmv_lora_delta_ids(const int32_t* lora_indices, const void* x, int64_t ldx,

@@ -629,3 +629,80 @@ def test_planted_fold_mistakes_are_caught(kind):
     assert not (check_fold_power_of_two(fn) and check_fold_error_bound(fn))
     ok = _fold_variant("none")
     assert check_fold_power_of_two(ok) and check_fold_error_bound(ok)
+
+
+# ---------------------------------------------------------------------------------------
+# merged weight (Ascend article 1.1 and 4.4; Punica page, SGMV section)
+# ---------------------------------------------------------------------------------------
+def check_merge_equivalence(merge_fn):
+    """x W'^T equals the base product plus the unmerged delta of the (independently pinned)
+    per-token oracle, for every token of the merged adapter."""
+    rng = np.random.default_rng(31)
+    M, K, N, L, R = 9, 14, 11, 3, 6
+    x, _, _, A, B, rank, alpha = rand_problem(rng, M, K, N, L, R, ranks=[6, 2, 5])
+    W = rng.standard_normal((N, K))
+    for l in range(L):
+        ids = np.full(M, l, dtype=np.int32)
+        base = x @ W.T
+        ref = oracle.lora_delta(x, base, ids, A, B, rank, alpha)
+        got = x @ merge_fn(W, A, B, rank, alpha, l).T
+        if rel_err(got, ref) > 1e-12:
+            return False
+    return True
+
+
+def check_merge_brute(merge_fn):
+    """Pure-Python loops on a tiny case, with entries past each rank set to NaN (never read)."""
+    rng = np.random.default_rng(32)
+    N, K, L, R = 5, 7, 2, 4
+    A = rng.standard_normal((L, R, K))
+    B = rng.standard_normal((L, N, R))
+    rank = np.asarray([3, 1], dtype=np.int32)
+    alpha = np.asarray([1.5, 4.0])
+    A[0, 3:, :] = np.nan
+    B[0, :, 3:] = np.nan
+    A[1, 1:, :] = np.nan
+    B[1, :, 1:] = np.nan
+    W = rng.standard_normal((N, K))
+    for l in range(L):
+        got = merge_fn(W, A, B, rank, alpha, l)
+        r = int(rank[l])
+        for n in range(N):
+            for k in range(K):
+                v = float(W[n, k]) + (float(alpha[l]) / r) * sum(
+                    float(B[l, n, j]) * float(A[l, j, k]) for j in range(r))
+                if not abs(got[n, k] - v) <= 1e-12 * max(1.0, abs(v)):
+                    return False
+    return True
+
+
+def test_merge_equals_unmerged_delta():
+    assert check_merge_equivalence(oracle.merge_weight)
+
+
+def test_merge_bruteforce_tiny():
+    assert check_merge_brute(oracle.merge_weight)
+
+
+def _merge_variant(kind):
+    def fn(w, a, b, rank, alpha, l):
+        R = a.shape[1]
+        r = int(rank[l])
+        s = float(alpha[l]) / (R if kind == "scale_by_max_rank" else r)
+        if kind == "no_scale":
+            s = 1.0
+        if kind == "all_ranks":
+            r = R
+        d = np.asarray(b[l, :, :r], np.float64) @ np.asarray(a[l, :r, :], np.float64)
+        if kind == "wrong_sign":
+            d = -d
+        return np.asarray(w, np.float64) + s * d
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["scale_by_max_rank", "no_scale", "all_ranks", "wrong_sign"])
+def test_planted_merge_mistakes_are_caught(kind):
+    fn = _merge_variant(kind)
+    assert not (check_merge_equivalence(fn) and check_merge_brute(fn))
+    ok = _merge_variant("none")
+    assert check_merge_equivalence(ok) and check_merge_brute(ok)
