@@ -120,6 +120,50 @@ __device__ void write_bucket(int lora, int cnt, int C, int start, int seg0, int 
   }
 }
 
+// The same entries as write_bucket, written by the bucket's own token threads (one token per
+// thread): the first token of each chunk writes that segment's start and adapter, the first
+// token of each piece writes the piece's record. A long bucket's hundreds of stores are then
+// spread over many waves instead of queueing behind one lane's store limit. `rank` is the
+// token's rank in its bucket of `cnt` rows; start, seg0, lt and st are the bucket's first
+// sorted row, segment, large and small descriptor.
+__device__ __forceinline__ void bucket_entries(int lora, int rank, int cnt, int C, int start,
+                                               int seg0, int lt, int st, int32_t* indptr,
+                                               int32_t* seg_lora, int32_t* tiles, int seg_cap,
+                                               int large_cap, int small_cap) {
+  const int i = C > 0 ? rank / C : 0;  // chunk (segment) inside the bucket
+  const int in_seg = C > 0 ? rank - i * C : rank;
+  if (in_seg % SGMV_TILE_ROWS != 0) return;
+  const int len = C > 0 ? min(C, cnt - i * C) : cnt;
+  const int s0 = start + (C > 0 ? i * C : 0);
+  const int seg = seg0 + i;
+  if (in_seg == 0 && seg < seg_cap) {
+    indptr[seg] = s0;
+    seg_lora[seg] = lora;
+  }
+  const int rows = min(SGMV_TILE_ROWS, len - in_seg);
+  const bool small = rows <= SGMV_SMALL_ROWS;
+  // every chunk before this one is full: nl_full large pieces and ns_full (0 or 1) small
+  // ones each; inside a chunk only the last piece can be small
+  int nl_full = 0, ns_full = 0;
+  if (C > 0) piece_tiles(C, nl_full, ns_full);
+  const int idx = small ? st + i * ns_full : lt + i * nl_full + in_seg / SGMV_TILE_ROWS;
+  if (small ? idx >= small_cap : idx >= large_cap) return;
+  int4* d = reinterpret_cast<int4*>(tiles + (size_t)(small ? large_cap + idx : idx) *
+                                                SGMV_TILE_INTS);
+  d[0] = make_int4(lora, s0 + in_seg, rows, seg);
+  d[1] = d[2] = d[3] = make_int4(0, 0, 0, 0);
+  const int first_free = small ? rows : 0;  // token slots past the piece's rows
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (4 * q >= first_free) {
+      d[4 + q] = make_int4(-1, -1, -1, -1);
+    } else if (4 * q + 4 > first_free) {
+      int32_t* e = reinterpret_cast<int32_t*>(d + 4 + q);
+      for (int k = first_free - 4 * q; k < 4; ++k) e[k] = -1;
+    }
+  }
+}
+
 // The token with in-bucket rank `rank` of a bucket of `cnt` rows whose first small
 // descriptor is `sbase`: if it lands in a small descriptor, store its id in that record.
 __device__ __forceinline__ void token_slot(int t, int rank, int cnt, int C, int sbase,
@@ -272,13 +316,15 @@ struct WgBuildLds {
   uint8_t* rc;  // [L + 1][8] per-(key, wave) counts
   int* base;    // [L + 1] first sorted row of each bucket (L: the tail)
   int* sbase;   // [L + 1] first small descriptor of each bucket
+  int* seg0;    // [L + 1] first segment of each bucket
+  int* lbase;   // [L + 1] first large descriptor of each bucket
   int* w;       // [5 * 8] workgroup scan scratch
   int* rec;     // [4] this workgroup's descriptor: adapter, first row, rows, segment
 };
 
 inline size_t wg_build_lds_bytes(int L) {
   const size_t nk = (size_t)L + 1;
-  return align16(nk * FUSED_BUILD_WAVES) + 2 * align16(nk * sizeof(int)) +
+  return align16(nk * FUSED_BUILD_WAVES) + 4 * align16(nk * sizeof(int)) +
          align16(5 * FUSED_BUILD_WAVES * sizeof(int)) + 16;
 }
 
@@ -290,6 +336,10 @@ __device__ __forceinline__ WgBuildLds wg_build_lds(unsigned char* p, int L) {
   s.base = reinterpret_cast<int*>(p);
   p += align16(nk * sizeof(int));
   s.sbase = reinterpret_cast<int*>(p);
+  p += align16(nk * sizeof(int));
+  s.seg0 = reinterpret_cast<int*>(p);
+  p += align16(nk * sizeof(int));
+  s.lbase = reinterpret_cast<int*>(p);
   p += align16(nk * sizeof(int));
   s.w = reinterpret_cast<int*>(p);
   p += align16(5 * FUSED_BUILD_WAVES * sizeof(int));
@@ -364,6 +414,8 @@ __device__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile
   if (first) {
     S.base[key] = ex[0];
     S.sbase[key] = ex[3];
+    S.seg0[key] = ex[1];
+    S.lbase[key] = ex[2];
     if (!overflow) {
       // this workgroup's descriptor, if it belongs to this bucket
       const int first_d = small ? ex[3] : ex[2], nd = small ? v[3] : v[2];
@@ -375,9 +427,6 @@ __device__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile
         S.rec[2] = pd.rows;
         S.rec[3] = pd.seg;
       }
-      if (writer)
-        write_bucket(key, cnt, C, ex[0], ex[1], ex[2], ex[3], D.indptr, D.seg_lora, D.tiles,
-                     D.seg_cap, D.large_cap, D.small_cap);
     }
   }
   if (t == 0) {
@@ -404,8 +453,12 @@ __device__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile
     if (key < L && pos >= out.start && pos < out.start + out.rows) s_tok[pos - out.start] = t;
     if (writer) {
       if (pos < M) D.sorted[pos] = t;
-      if (key < L && !overflow)
+      if (key < L && !overflow) {
         token_slot(t, rank, cnt, C, S.sbase[key], D.tiles, D.large_cap, D.small_cap);
+        bucket_entries(key, rank, cnt, C, S.base[key], S.seg0[key], S.lbase[key],
+                       S.sbase[key], D.indptr, D.seg_lora, D.tiles, D.seg_cap, D.large_cap,
+                       D.small_cap);
+      }
     }
   }
   return out;

@@ -11,7 +11,8 @@
 //  * small batches (M <= 1024, one token per thread, 4, 8 or 16 waves): each wave ranks its
 //    64 keys in registers (one ballot per lane), a per-(key, wave) byte table in LDS adds the
 //    counts of lower waves, and one workgroup scan over the tokens of (first-appearance flag,
-//    bucket size, segments, large and small descriptors) places every bucket;
+//    bucket size, segments, large and small descriptors) places every bucket; each token's
+//    thread writes its sorted position and, if it starts a chunk or a piece, that entry;
 //  * mid-size batches (up to 32768 tokens, tables within 64 KB of LDS): ids loaded once into
 //    LDS, each wave walks its own contiguous range with a private row of per-key counts;
 //  * larger batches: the same counting in rounds of 1024 tokens with a running count per
@@ -70,7 +71,7 @@ __device__ void cache_store(const int32_t* ids, int M, int L, int C, int32_t* ca
 // ---------------------------------------------------------------------------------------
 size_t build_small_lds_bytes(int L, int nw) {
   const size_t nk = (size_t)L + 1;
-  return align16(nk * nw) + 2 * align16(nk * sizeof(int));
+  return align16(nk * nw) + 4 * align16(nk * sizeof(int));
 }
 
 // One token per thread, NW waves (the fewest that cover M).
@@ -85,7 +86,10 @@ __global__ __launch_bounds__(NW * WAVE) void build_segments_small_kernel(
   const int NK = L + 1;
   uint8_t* rc = smem;                                                     // [NK][NW]
   int* s_base = reinterpret_cast<int*>(smem + align16((size_t)NK * NW));  // [NK]
-  int* s_sbase = s_base + align16((size_t)NK * sizeof(int)) / sizeof(int);  // [NK]
+  const size_t kstride = align16((size_t)NK * sizeof(int)) / sizeof(int);
+  int* s_sbase = s_base + kstride;  // [NK] first small descriptor of each bucket
+  int* s_seg0 = s_sbase + kstride;  // [NK] first segment
+  int* s_lbase = s_seg0 + kstride;  // [NK] first large descriptor
   __shared__ __align__(16) int s_w[6 * NW];
 
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
@@ -141,9 +145,8 @@ __global__ __launch_bounds__(NW * WAVE) void build_segments_small_kernel(
   if (first) {
     s_base[key] = ex[1];
     s_sbase[key] = ex[4];
-    if (!overflow)
-      write_bucket(key, cnt, C, ex[1], ex[2], ex[3], ex[4], indptr, seg_lora, tiles, seg_cap,
-                   large_cap, small_cap);
+    s_seg0[key] = ex[2];
+    s_lbase[key] = ex[3];
   }
   if (t == 0) {
     if (!overflow) indptr[n_seg] = n_lora;
@@ -157,8 +160,52 @@ __global__ __launch_bounds__(NW * WAVE) void build_segments_small_kernel(
   if (valid) {
     const int pos = s_base[key] + rank;
     if (pos < M) sorted[pos] = t;
-    if (key < L && !overflow)
+    if (key < L && !overflow) {
       token_slot(t, rank, cnt, C, s_sbase[key], tiles, large_cap, small_cap);
+      bucket_entries(key, rank, cnt, C, s_base[key], s_seg0[key], s_lbase[key], s_sbase[key],
+                     indptr, seg_lora, tiles, seg_cap, large_cap, small_cap);
+    }
+  }
+}
+
+// Segment entries and piece records of every bucket, written by the whole workgroup: one
+// thread per 16-byte quad of a record (a wave writes eight whole records) and one per segment,
+// each finding its bucket by a binary search over the buckets' first record or segment.
+// Per bucket b (in bucket order): bstart first sorted row (bstart[n_buckets] = the total),
+// pstart first segment, lstart / sbase first large / small record, ord its adapter.
+__device__ void write_entries_coop(int n_large, int n_small, int n_seg, int n_buckets,
+                                   const int* bstart, const int* pstart, const int* lstart,
+                                   const int* sbase, const int* ord, int C, int32_t* indptr,
+                                   int32_t* seg_lora, int32_t* tiles, int large_cap) {
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < (n_large + n_small) * 8; idx += BUILD_THREADS) {
+    const int rec = idx >> 3, q = idx & 7;
+    const bool small = rec >= n_large;
+    const int r = small ? rec - n_large : rec;
+    const int b = last_at_most(small ? sbase : lstart, n_buckets, r);
+    const int cnt_b = bstart[b + 1] - bstart[b];
+    const PieceDesc pd = small ? small_piece_desc(r - sbase[b], C, cnt_b, bstart[b], pstart[b])
+                               : large_piece_desc(r - lstart[b], C, cnt_b, bstart[b], pstart[b]);
+    int4* d = reinterpret_cast<int4*>(tiles + (size_t)(small ? large_cap + r : r) *
+                                                  SGMV_TILE_INTS) + q;
+    if (q == 0) {
+      *d = make_int4(ord[b], pd.start, pd.rows, pd.seg);
+    } else if (q < 4) {
+      *d = make_int4(0, 0, 0, 0);
+    } else {  // token slots past the piece's rows; the others belong to the tokens' threads
+      const int first_free = small ? pd.rows : 0, s0 = 4 * (q - 4);
+      if (s0 >= first_free) {
+        *d = make_int4(-1, -1, -1, -1);
+      } else if (s0 + 4 > first_free) {
+        int32_t* e = reinterpret_cast<int32_t*>(d);
+        for (int i = first_free - s0; i < 4; ++i) e[i] = -1;
+      }
+    }
+  }
+  for (int sg = tid; sg < n_seg; sg += BUILD_THREADS) {
+    const int b = last_at_most(pstart, n_buckets, sg);
+    indptr[sg] = bstart[b] + (C > 0 ? (sg - pstart[b]) * C : 0);
+    seg_lora[sg] = ord[b];
   }
 }
 
@@ -201,7 +248,7 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
   uint8_t* rc = smem;
   int* run = reinterpret_cast<int*>(smem + align16((size_t)NK * BUILD_WAVES));
   const size_t stride = align16((size_t)(NK + 1) * sizeof(int)) / sizeof(int);
-  int* first = run + stride;      // first token of each adapter, then its first large piece
+  int* first = run + stride;      // first token per adapter, then first large piece per bucket
   int* bidx = first + stride;     // bucket of each adapter
   int* ord = bidx + stride;       // adapter of each bucket
   int* bstart = ord + stride;     // first sorted row of each bucket
@@ -294,7 +341,7 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
     if (b < n_buckets) {
       bstart[b] = n_lora + ex[0];
       pstart[b] = n_seg + ex[1];
-      first[ord[b]] = n_large + ex[2];  // first[] is free after the bucket order
+      first[b] = n_large + ex[2];  // first[] is free after the bucket order: large starts
       sbase[b] = n_small + ex[3];
     }
     n_lora += tot[0];
@@ -308,13 +355,9 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_kernel(
   }
   const bool overflow = n_seg > seg_cap || n_large > large_cap || n_small > small_cap;
   __syncthreads();
-  if (!overflow) {
-    for (int b = tid; b < n_buckets; b += BUILD_THREADS) {
-      const int lora = ord[b];
-      write_bucket(lora, bstart[b + 1] - bstart[b], C, bstart[b], pstart[b], first[lora],
-                   sbase[b], indptr, seg_lora, tiles, seg_cap, large_cap, small_cap);
-    }
-  }
+  if (!overflow)
+    write_entries_coop(n_large, n_small, n_seg, n_buckets, bstart, pstart, first, sbase, ord, C,
+                       indptr, seg_lora, tiles, large_cap);
   if (tid == 0) {
     if (!overflow) indptr[n_seg] = n_lora;
     info[0] = overflow ? 0 : n_seg;
@@ -588,38 +631,9 @@ __global__ __launch_bounds__(BUILD_THREADS) void build_segments_mid_kernel(
   }
   const bool overflow = n_seg > seg_cap || n_large > large_cap || n_small > small_cap;
   __syncthreads();
-  if (!overflow) {
-    // records, one thread per 16-byte quad, so that a wave writes eight whole records
-    for (int idx = tid; idx < (n_large + n_small) * 8; idx += BUILD_THREADS) {
-      const int rec = idx >> 3, q = idx & 7;
-      const bool small = rec >= n_large;
-      const int r = small ? rec - n_large : rec;
-      const int b = last_at_most(small ? sbase : lstart, n_buckets, r);
-      const int cnt_b = bstart[b + 1] - bstart[b];
-      const PieceDesc pd = small ? small_piece_desc(r - sbase[b], C, cnt_b, bstart[b], pstart[b])
-                                 : large_piece_desc(r - lstart[b], C, cnt_b, bstart[b], pstart[b]);
-      int4* d = reinterpret_cast<int4*>(tiles + (size_t)(small ? large_cap + r : r) *
-                                                    SGMV_TILE_INTS) + q;
-      if (q == 0) {
-        *d = make_int4(ord[b], pd.start, pd.rows, pd.seg);
-      } else if (q < 4) {
-        *d = make_int4(0, 0, 0, 0);
-      } else {  // token slots past the piece's rows; the others belong to the tokens' threads
-        const int first_free = small ? pd.rows : 0, s0 = 4 * (q - 4);
-        if (s0 >= first_free) {
-          *d = make_int4(-1, -1, -1, -1);
-        } else if (s0 + 4 > first_free) {
-          int32_t* e = reinterpret_cast<int32_t*>(d);
-          for (int i = first_free - s0; i < 4; ++i) e[i] = -1;
-        }
-      }
-    }
-    for (int sg = tid; sg < n_seg; sg += BUILD_THREADS) {
-      const int b = last_at_most(pstart, n_buckets, sg);
-      indptr[sg] = bstart[b] + (C > 0 ? (sg - pstart[b]) * C : 0);
-      seg_lora[sg] = ord[b];
-    }
-  }
+  if (!overflow)
+    write_entries_coop(n_large, n_small, n_seg, n_buckets, bstart, pstart, lstart, sbase, ord, C,
+                       indptr, seg_lora, tiles, large_cap);
   if (tid == 0) {
     if (!overflow) indptr[n_seg] = n_lora;
     info[0] = overflow ? 0 : n_seg;
