@@ -301,6 +301,85 @@ def merge_bench(args):
         "cpu_baseline": None}), flush=True)
 
 
+def chunk_sweep(args):
+    """Chunk size against batch shape (the chunk-size rule of sgmv_chunk_size_for_batch):
+    step time (segment build + fused delta, dispatch events) for batches of M tokens spread
+    uniformly over n adapters of the decode pool (d = 4096, rank 16), at several chunk sizes,
+    with two launches and, where it applies, as one sgmv_lora_delta_ids launch."""
+    import numpy as np
+    import torch
+    import segmented_gather_gemv_amd as sg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    ev = HipEvents()
+    lib = sg.library()
+    specs = [(256, 1), (256, 4), (256, 16), (256, 64), (512, 1), (512, 8), (512, 64),
+             (1024, 1), (1024, 8), (1024, 64), (2048, 1), (2048, 16), (4096, 1), (4096, 16),
+             (8192, 1), (8192, 12), (8192, 64)]
+    chunks = [0, 16, 32, 64, 128]
+    if args.sweep_ranks != "16":  # a shorter grid per rank
+        specs = [(256, 1), (256, 16), (512, 8), (1024, 1), (1024, 16), (2048, 16), (4096, 16),
+                 (8192, 12)]
+        chunks = [0, 16, 32]
+    reps, sets = 40, 4
+    rows = []
+    for R, (M, n_ad) in [(int(r), sp) for r in args.sweep_ranks.split(",") for sp in specs]:
+        w = workloads.custom(M=M, K=4096, N=4096, L=64, R=R, name="sweep", seed=M + n_ad)
+        rng = np.random.default_rng(M * 100 + n_ad)
+        ad = rng.choice(64, size=n_ad, replace=False)
+        w.ids = torch.from_numpy(ad[rng.integers(0, n_ad, M)].astype(np.int32))
+        with torch.cuda.stream(stream):
+            pool = sg.sgmv_pool_pack(w.a.to(dev), w.b.to(dev), w.rank.tolist(), w.alpha.tolist())
+            xs = [w.x.to(dev) for _ in range(sets)]
+            ys = [w.y0.to(dev) for _ in range(sets)]
+            ids = w.ids.to(dev)
+        torch.cuda.synchronize()
+        for C in chunks:
+            segs = [sg.sgmv_segments_alloc(M, 64, C, dev) for _ in range(sets)]
+            modes = ["two"] + (["one"] if M <= 512 else [])
+            for mode in modes:
+                pairs = [ev.create(4) for _ in range(reps)]
+                with torch.cuda.stream(stream):
+                    for i in range(-5, reps):
+                        e = pairs[i] if i >= 0 else None
+                        st = i % sets
+                        if mode == "one":
+                            o = sg.LaunchOpts(e[0], e[1]) if e else None
+                            sg.sgmv_lora_delta_ids(ids, xs[st], pool, segs[st], ys[st], opts=o)
+                        else:
+                            sg.sgmv_build_segments(ids, 64, C, out=segs[st],
+                                                   opts=sg.LaunchOpts(e[0], e[1]) if e else None)
+                            sg.sgmv_lora_delta(xs[st], pool, segs[st], ys[st],
+                                               opts=sg.LaunchOpts(e[2], e[3]) if e else None)
+                torch.cuda.synchronize()
+                b = float(np.mean([ev.elapsed_ms(p_[0], p_[1]) for p_ in pairs])) * 1e3
+                d = 0.0 if mode == "one" else \
+                    float(np.mean([ev.elapsed_ms(p_[2], p_[3]) for p_ in pairs])) * 1e3
+                for p_ in pairs:
+                    ev.destroy(p_)
+                row = {"M": M, "adapters": n_ad, "rank": R, "chunk": C, "launches": mode,
+                       "build_us": round(b, 2) if mode == "two" else None,
+                       "delta_us": round(d, 2) if mode == "two" else round(b, 2),
+                       "total_us": round(b + d, 2)}
+                rows.append(row)
+                log(json.dumps(row))
+            del segs
+    best = {}
+    for r in rows:
+        k = (r["rank"], r["M"], r["adapters"])
+        if k not in best or r["total_us"] < best[k]["total_us"]:
+            best[k] = r
+    print(json.dumps({"metric": "build + delta step time by chunk size (sweep)",
+                      "value": None, "unit": "us", "n_gpus": 1, "data": "synthetic",
+                      "config": {"workload": "M tokens uniform over n adapters of a 64-adapter "
+                                             "pool, d=4096, every adapter at rank r",
+                                 "ranks": args.sweep_ranks},
+                      "rows": rows,
+                      "best": [best[k] for k in sorted(best)]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,10 +410,17 @@ def main():
                     help="mean sequence life in steps for --trace")
     ap.add_argument("--trace-admit-every", type=int, default=8,
                     help="steps between admissions of new sequences for --trace")
+    ap.add_argument("--chunk-size", type=int, default=-1,
+                    help="override the workload's chunk size (-1: the workload's; -2: "
+                         "sgmv_chunk_size_for_batch)")
     ap.add_argument("--fold-scale", action="store_true",
                     help="pack the pools with each adapter's scale folded into B")
     ap.add_argument("--segment-cache", action="store_true",
                     help="build through sgmv_build_segments_cached (with --trace)")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="step time by chunk size over batch sizes and adapter counts")
+    ap.add_argument("--sweep-ranks", default="16",
+                    help="comma-separated adapter ranks for --chunk-sweep")
     ap.add_argument("--merge", action="store_true",
                     help="time the merged-weight kernel against the base GEMM + delta")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -356,6 +442,9 @@ def main():
     if args.merge:
         merge_bench(args)
         return
+    if args.chunk_sweep:
+        chunk_sweep(args)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -375,10 +464,16 @@ def main():
     ev = HipEvents()
 
     w = workloads.get(args.workload)
-    log(f"workload: {w.note}")
-    fits_one = w.dtype == torch.bfloat16 and 1 <= w.M <= 512
+    if args.chunk_size == -2:
+        n_ad = int(len(set(w.ids[w.ids >= 0].tolist())))
+        w.chunk_size = sg.sgmv_chunk_size_for_batch(w.M, n_ad)
+    elif args.chunk_size >= 0:
+        w.chunk_size = args.chunk_size
+    log(f"workload: {w.note} (chunk size {w.chunk_size})")
+    # the single launch takes bf16 batches of 1..512 tokens whose ranks fit one 16-rank tile
+    fits_one = w.dtype == torch.bfloat16 and 1 <= w.M <= 512 and w.a.shape[1] <= 16
     if args.step == "one" and not fits_one:
-        print("--step one needs a bf16 batch of 1..512 tokens", file=sys.stderr)
+        print("--step one needs a bf16 batch of 1..512 tokens with ranks <= 16", file=sys.stderr)
         sys.exit(2)
     one_launch = args.step == "one" or (args.step == "auto" and fits_one)
     if (args.trace or args.segment_cache) and (one_launch or not args.trace):
@@ -523,7 +618,9 @@ def main():
     b_avg = sum(build_ms) / n_ev / 1e3
     srt = sorted(delta_ms)
     achieved = alg_bytes / d_avg / 1e9
-    traffic = load_traffic(args.workload, one_launch)
+    # counters were taken on the workload's own batch and chunk size
+    traffic = (load_traffic(args.workload, one_launch)
+               if args.chunk_size == -1 and not args.trace else None)
     kname = "build + delta kernel" if one_launch else "delta kernel"
     log(f"step {wall / K * 1e6:.2f} us | {kname} avg {d_avg * 1e6:.2f} us "
         f"(p10 {srt[n_ev // 10] * 1e3:.2f}, p50 {srt[n_ev // 2] * 1e3:.2f}, "
@@ -547,6 +644,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.note,
+            "chunk_size": w.chunk_size,
             "tokens_per_step": w.M,
             "lora_tokens_per_step": n_lora,
             "buffer_sets": n_sets,

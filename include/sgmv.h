@@ -219,6 +219,20 @@ sgmv_status sgmv_build_segments_cached(const int32_t* lora_indices, int32_t M, i
                                        int32_t chunk_size, int32_t on_device,
                                        const sgmv_segments* seg, int32_t* cache, void* stream);
 
+/* Chunk size for a batch (Punica page, code section: the reordered tokens are cut into
+ * fixed-size chunks, each one segment; the page leaves the rule that picks the size open).
+ *   M           tokens in the batch
+ *   n_adapters  distinct adapters among them if the caller knows it (a scheduler that
+ *               collects each step's adapter set does), else 0
+ * Returns the chunk size to pass to sgmv_segments_init / sgmv_build_segments, measured on
+ * MI355X over 256..8192 tokens, 1..64 adapters and ranks 16..64 (d = 4096): 0 (no chunks)
+ * when 1 <= M <= 512 and M <= 8 * n_adapters, where buckets are already small pieces and the
+ * single launch of sgmv_lora_delta_ids groups them itself; 16 for any other M <= 1024 (a few
+ * adapters' rows then spread over many more workgroups than 64-row pieces give); 0 above,
+ * where sequence-ordered prefill batches measured fastest without chunks. M <= 0 gives 0.
+ * Never fails. */
+int32_t sgmv_chunk_size_for_batch(int32_t M, int32_t n_adapters);
+
 /* One output slice: pool columns [n_begin, n_begin + n_len) land in columns [0, n_len) of
  * y, a device array [M][ldy] of the pool dtype (e.g. q, k and v of a fused projection). */
 typedef struct {
@@ -263,14 +277,14 @@ sgmv_status sgmv_lora_delta(const void* x, int64_t ldx, int32_t M, const sgmv_po
  * followed by sgmv_lora_delta(x, ldx, M, pool, seg, out, n_slices, stream).
  *   lora_indices  [M] int32 DEVICE array; a bad id counts as -1 and sets info[3] to
  *                 SGMV_EBADID, as in the device builder.
- * For a bf16 pool with 1 <= M <= SGMV_FUSED_BUILD_MAX_M and pool->L <=
- * SGMV_DEVICE_BUILDER_MAX_L this is ONE launch: every workgroup groups the batch's tokens
- * itself in LDS, and one of them also writes the arrays of `seg`, which no other workgroup
- * of the launch reads. Without chunking and with pool->L <= seg->small_cap, a small piece's
- * exchange control word and partial tiles are those of slot large_cap + its adapter id
- * rather than of its descriptor. That launch leaves the exchange control words of seg->exchange as it
- * finds them (every completed fused call leaves them consistent). Otherwise it issues the two
- * launches. Never synchronises with the host.
+ * For a bf16 pool with R_pad == 16 (every rank <= 16), 1 <= M <= SGMV_FUSED_BUILD_MAX_M and
+ * pool->L <= SGMV_DEVICE_BUILDER_MAX_L this is ONE launch: every workgroup groups the batch's
+ * tokens itself in LDS, and one of them also writes the arrays of `seg`, which no other
+ * workgroup of the launch reads. Without chunking and with pool->L <= seg->small_cap, a small
+ * piece's exchange control word and partial tiles are those of slot large_cap + its adapter
+ * id rather than of its descriptor; the launch leaves the control words consistent, as every
+ * completed fused call does. Otherwise (wider ranks, where two launches measured faster,
+ * larger batches, fp32) it issues the two launches. Never synchronises with the host.
  * Errors: EINVAL; EUNSUPPORTED; EHIP. */
 sgmv_status sgmv_lora_delta_ids(const int32_t* lora_indices, const void* x, int64_t ldx,
                                 int32_t M, const sgmv_pool* pool, const sgmv_segments* seg,

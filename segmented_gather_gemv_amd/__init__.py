@@ -42,7 +42,7 @@ EXPORTED = [
     "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
     "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached", "sgmv_build_segments_cached_ex",
     "sgmv_pool_pack_ex", "sgmv_merge_adapter", "sgmv_merge_adapter_ex", "sgmv_status_string",
-    "sgmv_version",
+    "sgmv_version", "sgmv_chunk_size_for_batch",
 ]
 
 
@@ -139,6 +139,8 @@ def _load():
     lib.sgmv_status_string.argtypes = [ctypes.c_int]
     lib.sgmv_status_string.restype = ctypes.c_char_p
     lib.sgmv_version.restype = ctypes.c_int32
+    lib.sgmv_chunk_size_for_batch.argtypes = [i32, i32]
+    lib.sgmv_chunk_size_for_batch.restype = ctypes.c_int32
     return lib
 
 
@@ -345,6 +347,12 @@ def sgmv_build_segments(ids: torch.Tensor, L: int, chunk_size: int = 0, on_devic
     return seg
 
 
+def sgmv_chunk_size_for_batch(M: int, n_adapters: int = 0) -> int:
+    """The library's chunk size for a batch of M tokens over n_adapters distinct adapters
+    (0 = unknown), measured: see include/sgmv.h."""
+    return int(_lib.sgmv_chunk_size_for_batch(int(M), int(n_adapters)))
+
+
 def sgmv_segments_cache_alloc(M: int, device: Union[str, torch.device] = "cuda") -> torch.Tensor:
     """An empty grouping cache for batches of M tokens: SGMV_CACHE_HEADER + M zeroed int32."""
     return torch.zeros(CACHE_HEADER + max(int(M), 0), dtype=torch.int32, device=device)
@@ -485,4 +493,5 @@ __all__ = [
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_alloc", "sgmv_build_segments",
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_lora_delta_ids",
     "sgmv_segments_cache_alloc", "sgmv_build_segments_cached", "sgmv_merge_adapter",
+    "sgmv_chunk_size_for_batch",
 ]

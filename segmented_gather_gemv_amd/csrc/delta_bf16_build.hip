@@ -1,5 +1,6 @@
 // Fused build + delta: instantiations of the bf16 delta kernel whose workgroups first build
-// the batch's segments themselves (M <= 512), so a decode step needs a single launch.
+// the batch's segments themselves (M <= 512, ranks within one 16-rank tile), so a decode step
+// needs a single launch.
 #include "delta_bf16.h"
 
 namespace sgmv {
@@ -16,15 +17,10 @@ hipError_t launch_delta_bf16_build(bool aligned, DeltaArgs A, LaunchEvents ev,
 #define SGMV_LAUNCH(AL_, NR_, X_)                                                              \
   hipExtLaunchKernelGGL((delta_bf16_kernel<MODE_FUSED, AL_, NR_, X_, true>), g, b, lds, stream, \
                         ev.start, ev.stop, 0, A)
+  if (nrkm != 1) return hipErrorInvalidValue;  // the caller takes two launches instead
   if (aligned) {
-    if (nrkm == 1) {
-      if (x) SGMV_LAUNCH(true, 1, true); else SGMV_LAUNCH(true, 1, false);
-    } else if (nrkm == 2) {
-      if (x) SGMV_LAUNCH(true, 2, true); else SGMV_LAUNCH(true, 2, false);
-    } else {
-      if (x) SGMV_LAUNCH(true, 4, true); else SGMV_LAUNCH(true, 4, false);
-    }
-  } else {
+    if (x) SGMV_LAUNCH(true, 1, true); else SGMV_LAUNCH(true, 1, false);
+  } else {  // the generic instance (any rank tile count) also serves unaligned rank-16 pools
     if (x) SGMV_LAUNCH(false, 4, true); else SGMV_LAUNCH(false, 4, false);
   }
 #undef SGMV_LAUNCH

@@ -291,6 +291,12 @@ const char* sgmv_status_string(sgmv_status s) {
 
 int32_t sgmv_version(void) { return 100; }
 
+int32_t sgmv_chunk_size_for_batch(int32_t M, int32_t n_adapters) {
+  if (M <= 0) return 0;
+  if (M <= SGMV_FUSED_BUILD_MAX_M && n_adapters > 0 && M <= 8 * n_adapters) return 0;
+  return M <= 1024 ? 16 : 0;
+}
+
 sgmv_status sgmv_pool_init(int32_t L, int32_t R_max, int32_t K, int32_t N, int32_t dtype,
                            sgmv_pool* pool, size_t* a_bytes, size_t* b_bytes) {
   if (!pool || !a_bytes || !b_bytes) return SGMV_EINVAL;
@@ -433,8 +439,11 @@ sgmv_status sgmv_lora_delta_ids_ex(const int32_t* lora_indices, const void* x, i
                                    const sgmv_launch_opts* opts, void* stream) {
   if (M < 0 || (M > 0 && !lora_indices) || !pool_ok(pool) || !opts_ok(opts)) return SGMV_EINVAL;
   if (!seg_ok(seg, M, pool->L)) return SGMV_EINVAL;
+  // one launch where it measured faster than two: small bf16 batches whose ranks fit one
+  // 16-rank tile (with wider ranks every workgroup's in-kernel grouping cost more than the
+  // builder launch it saves)
   if (pool->dtype == SGMV_BF16 && M >= 1 && M <= SGMV_FUSED_BUILD_MAX_M &&
-      pool->L <= SGMV_DEVICE_BUILDER_MAX_L)
+      pool->L <= SGMV_DEVICE_BUILDER_MAX_L && pool->R_pad == 16)
     return run_delta(MODE_FUSED, x, ldx, nullptr, nullptr, 0, M, pool, seg, out, n_slices, opts,
                      stream, lora_indices);
   // two launches: validate the delta's arguments first so that a bad call changes nothing

@@ -330,3 +330,20 @@ def test_delta_ids_argument_errors():
         other = sg.sgmv_segments_alloc(M + 1, 4, 0, "cpu")
         assert call(ids, x, other.desc) == sg.SGMV_EINVAL          # segments for another M
         assert call(ids, x, seg.desc, o=sg.LaunchOpts(exchange=3).ref()) == sg.SGMV_EINVAL
+
+
+def test_chunk_size_rule():
+    """sgmv_chunk_size_for_batch: no chunks for small batches whose adapters are many enough
+    that buckets are already small pieces, 16-row chunks up to 1024 tokens, none above."""
+    f = sg.sgmv_chunk_size_for_batch
+    assert f(0, 0) == 0 and f(-3, 5) == 0
+    assert f(256, 64) == 0 and f(512, 64) == 0 and f(512, 100) == 0
+    assert f(256, 16) == 16 and f(256, 1) == 16 and f(256, 0) == 16   # unknown: chunks
+    assert f(513, 1000) == 16 and f(1024, 1) == 16
+    assert f(1025, 0) == 0 and f(8192, 12) == 0 and f(1 << 20, 3) == 0
+    # the answer is a valid chunk size for the segment calls
+    for M, n in [(1, 1), (300, 2), (5000, 40)]:
+        C = f(M, n)
+        assert C >= 0
+        seg = sg.sgmv_segments_alloc(M, 64, C, "cpu")
+        assert seg.desc.chunk_size == C
