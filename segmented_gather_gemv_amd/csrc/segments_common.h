@@ -81,51 +81,14 @@ __device__ __forceinline__ void piece_tiles(int len, int& nl, int& ns) {
   ns = (rem > 0 && rem <= SGMV_SMALL_ROWS) ? 1 : 0;
 }
 
-// Writes the descriptors of one bucket (adapter `lora`, `cnt` rows from sorted row `start`,
-// chunk size C) and its segments. Token slots of small descriptors are left to the tokens'
-// own threads (token_slot); every other token slot gets -1.
-__device__ void write_bucket(int lora, int cnt, int C, int start, int seg0, int lt, int st,
-                             int32_t* indptr, int32_t* seg_lora, int32_t* tiles, int seg_cap,
-                             int large_cap, int small_cap) {
-  const int np = C > 0 ? (cnt + C - 1) / C : 1;
-  for (int i = 0; i < np; ++i) {
-    const int seg = seg0 + i;
-    const int s0 = start + (C > 0 ? i * C : 0);
-    const int len = C > 0 ? min(C, cnt - i * C) : cnt;
-    if (seg < seg_cap) {
-      indptr[seg] = s0;
-      seg_lora[seg] = lora;
-    }
-    for (int r0 = 0; r0 < len; r0 += SGMV_TILE_ROWS) {
-      const int rows = min(SGMV_TILE_ROWS, len - r0);
-      const bool small = rows <= SGMV_SMALL_ROWS;
-      const int idx = small ? st++ : lt++;
-      if (small ? idx >= small_cap : idx >= large_cap) continue;
-      int4* d = reinterpret_cast<int4*>(tiles + (size_t)(small ? large_cap + idx : idx) *
-                                                    SGMV_TILE_INTS);
-      d[0] = make_int4(lora, s0 + r0, rows, seg);
-      d[1] = d[2] = d[3] = make_int4(0, 0, 0, 0);
-      // token slots past the piece's rows; the others belong to the tokens' own threads
-      const int first_free = small ? rows : 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (4 * q >= first_free) {
-          d[4 + q] = make_int4(-1, -1, -1, -1);
-        } else if (4 * q + 4 > first_free) {
-          int32_t* e = reinterpret_cast<int32_t*>(d + 4 + q);
-          for (int i = first_free - 4 * q; i < 4; ++i) e[i] = -1;
-        }
-      }
-    }
-  }
-}
-
-// The same entries as write_bucket, written by the bucket's own token threads (one token per
+// The segment entries and piece records of one bucket (adapter `lora`, `cnt` rows from sorted
+// row `start`, chunk size C), written by the bucket's own token threads (one token per
 // thread): the first token of each chunk writes that segment's start and adapter, the first
-// token of each piece writes the piece's record. A long bucket's hundreds of stores are then
-// spread over many waves instead of queueing behind one lane's store limit. `rank` is the
-// token's rank in its bucket of `cnt` rows; start, seg0, lt and st are the bucket's first
-// sorted row, segment, large and small descriptor.
+// token of each piece writes the piece's record, with -1 in the token slots that the piece's
+// tokens do not fill (those write their own ids, token_slot). A long bucket's hundreds of
+// stores are spread over many waves instead of queueing behind one lane's store limit. `rank`
+// is the token's rank in its bucket; seg0, lt and st are the bucket's first segment, large
+// and small descriptor.
 __device__ __forceinline__ void bucket_entries(int lora, int rank, int cnt, int C, int start,
                                                int seg0, int lt, int st, int32_t* indptr,
                                                int32_t* seg_lora, int32_t* tiles, int seg_cap,
