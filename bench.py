@@ -652,6 +652,11 @@ def main():
                      if one_launch else "device segment build launch + fused delta launch"),
             "timed_launches_sampled": n_ev,
             "delta_kernel_us": d_avg * 1e6,
+            "delta_kernel_us_p10_p50_p90": [srt[n_ev // 10] * 1e3, srt[n_ev // 2] * 1e3,
+                                            srt[9 * n_ev // 10] * 1e3],
+            "device": (f"{torch.cuda.get_device_name(dev)} "
+                       f"({torch.cuda.get_device_properties(dev).gcnArchName})"),
+            "hip_runtime": torch.version.hip,
             "builder_kernel_us": None if one_launch else b_avg * 1e6,
             "algorithmic_bytes_per_launch": alg_bytes,
             "algorithmic_flops_per_launch": alg_flops,
