@@ -7,6 +7,8 @@ against the fp64 oracle (bf16: rel-L2 <= 5e-3 and max-abs <= 1e-2 * max|ref|; fp
 1e-4), the unfused shrink + expand against the oracle, and, for bf16 batches, the
 build-and-delta call against the two calls (segment arrays and y bit for bit).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,7 +18,7 @@ from test_gpu_parity import DEV, check_no_adapter_rows, compare, np32, oracle_y,
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = int(os.environ.get("SGMV_RANDOM_CASES", "40"))  # more for a deeper sweep
 
 
 @pytest.fixture(scope="module")
