@@ -46,6 +46,8 @@ CASES = {
     "unaligned_k": (dict(M=4, K=999, N=77, L=2, R=16, ranks=[3, 16]), 0.5),
     "f32": (dict(M=4, K=300, N=130, L=3, R=8, ranks=[1, 8], dtype=torch.float32, w_std=0.1),
             0.5),
+    "tiny": (dict(M=2, K=7, N=5, L=2, R=2, ranks=[1, 2]), 0.5),
+    "tiny_f32": (dict(M=2, K=3, N=9, L=1, R=3, dtype=torch.float32, w_std=0.1), 0.5),
 }
 
 
