@@ -4,8 +4,9 @@ slices, each drawn from its own seed.
 
 Every case runs the device builder against the host builder (bit for bit), the fused delta
 against the fp64 oracle (bf16: rel-L2 <= 5e-3 and max-abs <= 1e-2 * max|ref|; fp32: rel-L2 <=
-1e-4), the unfused shrink + expand against the oracle, and, for bf16 batches, the
-build-and-delta call against the two calls (segment arrays and y bit for bit).
+1e-4) on the drawn base output and on a zero base (the delta alone), the unfused shrink +
+expand against the oracle, and, for bf16 batches, the build-and-delta call against the two
+calls (segment arrays and y bit for bit).
 """
 import os
 
@@ -90,6 +91,9 @@ def test_random_configuration(sg, seed):
     y = _apply(sg, w, x, y0, lambda v: sg.sgmv_lora_delta(x, pool, dev, v))
     compare(np32(y), ref, w.dtype, what=what)
     check_no_adapter_rows(w, y, w.y0)
+    # zero-base twin: the delta alone, which a large base output would hide
+    yz = _apply(sg, w, x, torch.zeros_like(y0), lambda v: sg.sgmv_lora_delta(x, pool, dev, v))
+    compare(np32(yz), oracle_y(w, np.zeros_like(np32(w.y0))), w.dtype, what=what + " zero base")
     # unfused shrink + expand against the oracle
     h = sg.sgmv_shrink(x, pool, dev)
     y2 = _apply(sg, w, x, y0, lambda v: sg.sgmv_expand(h, pool, dev, v))
