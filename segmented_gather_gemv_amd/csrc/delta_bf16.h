@@ -738,7 +738,7 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
       static_assert(MODE == MODE_FUSED && NRK == 1 && PF > 0, "adapter-major rank-16 pieces");
       ShrinkSteps<NRK, NSTEP, ALIGNED> S;
       S.load_a(ab, A.K_pad, A.K, ch, c1, c, g);
-      pc.rows = adapter_small_piece<DT_WAVES>(wave_adapter_mask(A.ids, A.M, pc.lora), pc.lora,
+      pc.rows = adapter_small_piece<DT_WAVES>(wave_adapter_mask(A.ids, A.M, pc.lora),
                                               reinterpret_cast<int*>(s_part), s_tok);
       if (pc.rows == 0) {  // uniform: no small piece; let the loads land before leaving
         __builtin_amdgcn_s_waitcnt(0);
@@ -827,7 +827,7 @@ __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc,
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
   const ShrinkGeom G = shrink_geom(false, pc.rows);
-  const int nrt = G.nrt, ntp = G.ntp, ks = G.ks;  // 2..4 row tiles
+  const int nrt = G.nrt;  // 2..4 row tiles
   constexpr bool xkernel = XCH && MODE == MODE_FUSED;
   const bool xch = xkernel && A.xch_large;
   if (MODE != MODE_EXPAND) {
@@ -908,8 +908,11 @@ __device__ __forceinline__ void run_piece(const DeltaArgs& A, const Piece& pc, b
 // Pieces of rank tiles up to NRKM (ranks up to 16 NRKM); XCH: pieces of fused calls split
 // their shrink over K with the other column splits of the piece; BUILD: every workgroup
 // first builds the segments of the batch itself (fused build + delta, M <= 512).
+// Aligned exchange variants are held to 128 registers so that two workgroups share a CU; the
+// generic unaligned instance needs more and is left unconstrained.
 template <int MODE, bool ALIGNED, int NRKM, bool XCH, bool BUILD>
-__global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH ? 4 : 1))) void delta_bf16_kernel(DeltaArgs A) {
+__global__ __launch_bounds__(DT_THREADS)
+__attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_kernel(DeltaArgs A) {
   __shared__ __align__(16) int s_tok[SGMV_TILE_ROWS];
   __shared__ __align__(16) float s_h[SGMV_TILE_ROWS * HS];
   __shared__ int s_rank[RANK_TABLE_MAX];
@@ -969,7 +972,7 @@ __global__ __launch_bounds__(DT_THREADS) __attribute__((amdgpu_waves_per_eu(XCH 
       s_rank[tile] = A.rank[tile];
       s_scale[tile] = A.scale[tile];
     }
-    pc.rows = adapter_small_piece<DT_WAVES>(__ballot(id == tile), tile,
+    pc.rows = adapter_small_piece<DT_WAVES>(__ballot(id == tile),
                                             reinterpret_cast<int*>(s_part), s_tok);
     if (pc.rows == 0) return;  // uniform
     pc.lora = tile;

@@ -234,14 +234,14 @@ __device__ __forceinline__ uint64_t wave_adapter_mask(const int32_t* ids, int M,
   return m;
 }
 
-// The small piece of adapter l's bucket when there is no chunking: its last c % 64 tokens
+// The small piece of an adapter's bucket when there is no chunking: its last c % 64 tokens
 // when that is 1..16 (c: the adapter's tokens), in token order, as the device builder makes
 // it. Call from all threads of a workgroup of NW waves, each wave passing the mask of its
-// block of 64 tokens whose id is l (ids past M never set); s_wc holds NW ints. Returns the
-// piece's rows (0: no small piece; uniform) and writes its tokens to s_tok, visible after
-// the caller's next barrier.
+// block of 64 tokens whose id is the adapter's (ids past M never set); s_wc holds NW ints.
+// Returns the piece's rows (0: no small piece; uniform) and writes its tokens to s_tok,
+// visible after the caller's next barrier.
 template <int NW>
-__device__ int adapter_small_piece(uint64_t m, int l, int* s_wc, int* s_tok) {
+__device__ int adapter_small_piece(uint64_t m, int* s_wc, int* s_tok) {
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
   const bool mine = (m >> lane) & 1u;
   if (lane == 0) s_wc[w] = __popcll(m);
