@@ -209,11 +209,25 @@ def cpu_baseline(w, seconds: float):
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:
             break
+    one_thread = ""
+    try:  # the same loop held to one BLAS thread, briefly
+        import threadpoolctl
+        with threadpoolctl.threadpool_limits(1):
+            r1, t1 = 0, time.perf_counter()
+            while True:
+                oracle.lora_delta(x, y0, ids, a, b, rank, alpha)
+                r1 += 1
+                e1 = time.perf_counter() - t1
+                if e1 >= min(3.0, seconds) or r1 >= 1000:
+                    break
+        one_thread = f"; with one BLAS thread {n_tok * r1 / e1:.0f} tokens/s ({r1} times)"
+    except Exception:
+        pass
     return {"value": n_tok * reps / el, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{w.note}: the full batch ({n_tok} tokens with an adapter) through the "
                       f"fp64 per-token oracle, {reps} times in {el:.1f} s on "
-                      f"{os.cpu_count()} visible host cores"}
+                      f"{os.cpu_count()} visible host cores{one_thread}"}
 
 
 def merge_bench(args):
