@@ -347,3 +347,35 @@ def test_chunk_size_rule():
         assert C >= 0
         seg = sg.sgmv_segments_alloc(M, 64, C, "cpu")
         assert seg.desc.chunk_size == C
+
+
+def test_merge_and_pack_argument_errors():
+    """sgmv_merge_adapter and sgmv_pool_pack_ex reject bad arguments before any launch."""
+    lib = sg.library()
+    pool = _fake_pool(L=4, R=16, K=128, N=256)
+    w, wo = ctypes.c_void_p(0x6000), ctypes.c_void_p(0x7000)
+    merge = lambda *a: lib.sgmv_merge_adapter(*a)
+    assert merge(None, 128, wo, 128, ctypes.byref(pool), 0, None) == sg.SGMV_EINVAL
+    assert merge(w, 128, None, 128, ctypes.byref(pool), 0, None) == sg.SGMV_EINVAL
+    assert merge(w, 127, wo, 128, ctypes.byref(pool), 0, None) == sg.SGMV_EINVAL  # ldw < K
+    assert merge(w, 128, wo, 100, ctypes.byref(pool), 0, None) == sg.SGMV_EINVAL  # ldo < K
+    assert merge(w, 128, wo, 128, ctypes.byref(pool), -1, None) == sg.SGMV_EINVAL
+    assert merge(w, 128, wo, 128, ctypes.byref(pool), 4, None) == sg.SGMV_EINVAL   # L = 4
+    bad = _fake_pool()
+    bad.b = 0
+    assert merge(w, 128, wo, 128, ctypes.byref(bad), 0, None) == sg.SGMV_EINVAL
+    bad_opts = sg.LaunchOpts(n_split_small=-3)
+    assert lib.sgmv_merge_adapter_ex(w, 128, wo, 128, ctypes.byref(pool), 0, bad_opts.ref(),
+                                     None) == sg.SGMV_EINVAL
+    # unknown pack flags (checked with the pool before any copy)
+    rank = torch.full((4,), 16, dtype=torch.int32)
+    alpha = torch.full((4,), 32.0)
+    assert lib.sgmv_pool_pack_ex(w, wo, ctypes.c_void_p(rank.data_ptr()),
+                                 ctypes.c_void_p(alpha.data_ptr()), 2, ctypes.byref(pool),
+                                 None) == sg.SGMV_EINVAL
+    # the Python binding checks shapes and dtypes of w
+    p = sg.Pool.__new__(sg.Pool)
+    p.desc = pool
+    p.a = torch.zeros(1, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sg.sgmv_merge_adapter(torch.zeros(3, 3, dtype=torch.bfloat16), p, 0)
