@@ -15,17 +15,24 @@ copies of every buffer (pool, x, y, ids, segment arrays) whose total size is abo
 256 MB last-level cache, so each step reads its operands from HBM rather than from that
 cache.
 
-Timing: W untimed warm-up steps, then K steps between two device synchronisations
-(ms_per_step, value = tokens with an adapter per second). Inside the same timed region every
-eighth step's kernel launches (the single build + delta kernel, or the builder and the
-delta kernel) record a pair of HIP events as part of their own dispatch on the launch stream
-(start and end of the kernel, no extra stream packets); their averages give the per-launch
-durations used for the roofline, which takes the kernel that does the delta (including the
-build it does itself in the single-launch step).
-Events on every launch would slow the host's launch path and lengthen the step. The roofline
-figure divides the algorithmic bytes of one delta launch (x rows and y rows read and written
-for every token with an adapter, each used adapter's true-rank A and B once, 12 bytes of
-index per token) by that duration, against the 8 TB/s HBM peak.
+Timing: W untimed warm-up steps, then K plain steps between two device synchronisations
+(ms_per_step, value = tokens with an adapter per second), with two HIP events recorded on the
+launch stream around them. The roofline takes the kernel that does the delta (including the
+build it does itself in the single-launch step): its average launch duration is the timed
+region's event time over K for the single launch (one kernel per step; the figure includes
+the gaps between launches), and for two launches the event time of K launches of that kernel
+alone, run after the timed region on the same rotating buffer sets. The roofline figure
+divides the algorithmic bytes of one delta launch (x rows and y rows read and written for
+every token with an adapter, each used adapter's true-rank A and B once, 12 bytes of index
+per token) by that duration, against the 8 TB/s HBM peak. The builder's figure for two
+launches is the timed step less the delta alone: a few microseconds of kernel, which the host
+cannot launch alone as fast as the GPU runs it. The line also gives the host's time to issue
+each region's launches; a warning goes to stderr if it comes near the region's own time.
+A further K steps, outside the timed region, give the spread of launch durations: every
+eighth launch records a pair of events in its own dispatch (start and end of the kernel, no
+extra stream packets). Such launches can run longer than plain ones (the single launch by
+about 1.7 us), so these samples give the p10/p50/p90 only, except with --trace, whose
+per-step batches change and whose builder and delta averages come from them.
 
 --trace (with --step two) replaces the fixed batch by seeded decode traces, one per buffer
 set, in which sequences keep their adapter and join or leave the batch; --segment-cache then
@@ -85,6 +92,9 @@ class HipEvents:
             evs.append(e)
         return evs
 
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
         assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
@@ -93,6 +103,28 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.lib.hipEventDestroy(e)
+
+
+def region_us(ev, stream, fn, n):
+    """Mean microseconds per call of fn(i), i < n, from two HIP events recorded on `stream` (a
+    torch stream, made current for the calls) around all n calls: the kernels and the gaps
+    between them, with no event inside any launch. Also returns the host's time per call to
+    issue them (no wait inside the loop): when that is close to the first figure, the host's
+    launch rate, not the GPU, set it."""
+    import torch
+    h = ctypes.c_void_p(stream.cuda_stream)
+    e = ev.create(2)
+    with torch.cuda.stream(stream):
+        ev.record(e[0], h)
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        t1 = time.perf_counter()
+        ev.record(e[1], h)
+    torch.cuda.synchronize()
+    t = ev.elapsed_ms(e[0], e[1]) / n * 1e3
+    ev.destroy(e)
+    return t, (t1 - t0) / n * 1e6
 
 
 def kernel_source_sha() -> str:
@@ -232,9 +264,10 @@ def cpu_baseline(w, seconds: float):
 
 def merge_bench(args):
     """Merged weight (sgmv_merge_adapter) on the decode shapes: W 4096 x 4096 bf16, rank 16.
-    Times the merge kernel (dispatch events, W and W' rotating over sets larger than the
-    last-level cache), the base GEMM x W^T of the decode batch (torch.matmul, the vendor GEMM
-    library) and the unmerged delta of a batch whose 256 tokens all use one adapter, and
+    Times the merge kernel (W and W' rotating over sets larger than the last-level cache), the
+    base GEMM x W^T of the decode batch (torch.matmul, the vendor GEMM library) and the unmerged
+    delta of a batch whose 256 tokens all use one adapter, each from stream events around a run
+    of its launches, and
     reports the merge as HBM bandwidth against the peak plus the number of steps after which
     merging pays for itself (Ascend article 4.4)."""
     import torch
@@ -261,38 +294,21 @@ def merge_bench(args):
     torch.cuda.synchronize()
     log(f"merge bench: W {N}x{K} bf16 x {n_sets} sets, rank {int(w.rank[0])}")
 
-    def timed(fn, reps):
-        pairs = [ev.create(2) for _ in range(reps)]
+    def timed(fn, reps):  # us per call
         with torch.cuda.stream(stream):
             for i in range(args.warmup):
-                fn(i, None)
-            torch.cuda.synchronize()
-            for i in range(reps):
-                fn(i, sg.LaunchOpts(pairs[i][0], pairs[i][1]))
+                fn(i)
         torch.cuda.synchronize()
-        ms = [ev.elapsed_ms(a, b) for a, b in pairs]
-        for p_ in pairs:
-            ev.destroy(p_)
-        return sum(ms) / len(ms) * 1e3  # us
+        t, host = region_us(ev, stream, fn, reps)
+        if host > 0.9 * t:
+            log(f"warning: host issue {host:.2f} us per call against {t:.2f} us: launch-bound")
+        return t
 
     reps = max(16, min(args.steps, 200))
-    merge_us = timed(lambda i, o: sg.sgmv_merge_adapter(Ws[i % n_sets], pool, 0,
-                                                       out=Wo[i % n_sets], opts=o), reps)
-    delta_us = timed(lambda i, o: sg.sgmv_lora_delta_ids(ids, x, pool, seg, ys[i % n_sets],
-                                                         opts=o), reps)
-    # base GEMM y = x W^T through torch (events around each call on the stream)
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            torch.matmul(x, Ws[i % n_sets].t())
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for i in range(reps):
-            evs[i][0].record(stream)
-            torch.matmul(x, Ws[i % n_sets].t())
-            evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    gemm_us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    merge_us = timed(lambda i: sg.sgmv_merge_adapter(Ws[i % n_sets], pool, 0,
+                                                    out=Wo[i % n_sets]), reps)
+    delta_us = timed(lambda i: sg.sgmv_lora_delta_ids(ids, x, pool, seg, ys[i % n_sets]), reps)
+    gemm_us = timed(lambda i: torch.matmul(x, Ws[i % n_sets].t()), reps)  # base y = x W^T
     r = int(w.rank[0])
     alg = 2 * N * K * e + r * (N + K) * e
     gbps = alg / (merge_us * 1e-6) / 1e9
@@ -317,9 +333,11 @@ def merge_bench(args):
 
 def chunk_sweep(args):
     """Chunk size against batch shape (the chunk-size rule of sgmv_chunk_size_for_batch):
-    step time (segment build + fused delta, dispatch events) for batches of M tokens spread
-    uniformly over n adapters of the decode pool (d = 4096, rank 16), at several chunk sizes,
-    with two launches and, where it applies, as one sgmv_lora_delta_ids launch."""
+    step time (segment build + fused delta) for batches of M tokens spread uniformly over n
+    adapters of the decode pool (d = 4096, rank 16), at several chunk sizes, with two launches
+    and, where it applies, as one sgmv_lora_delta_ids launch. Every figure comes from stream
+    events around a run of launches: whole steps for the total, each kernel alone for the
+    builder and delta columns."""
     import numpy as np
     import torch
     import segmented_gather_gemv_amd as sg
@@ -338,6 +356,9 @@ def chunk_sweep(args):
                  (8192, 12)]
         chunks = [0, 16, 32]
     reps, sets = 40, 4
+    s_handle = ctypes.c_void_p(stream.cuda_stream)
+    dflt_opts = sg.LaunchOpts()
+    dflt = dflt_opts.ref()
     rows = []
     for R, (M, n_ad) in [(int(r), sp) for r in args.sweep_ranks.split(",") for sp in specs]:
         w = workloads.custom(M=M, K=4096, N=4096, L=64, R=R, name="sweep", seed=M + n_ad)
@@ -352,31 +373,43 @@ def chunk_sweep(args):
         torch.cuda.synchronize()
         for C in chunks:
             segs = [sg.sgmv_segments_alloc(M, 64, C, dev) for _ in range(sets)]
+            calls = []  # ctypes arguments made once: the loops below only launch
+            for st in range(sets):
+                sl, n_sl = sg._slices([(ys[st], 0)], pool, M)
+                calls.append(((ctypes.c_void_p(ids.data_ptr()), M, 64, C, 1,
+                               ctypes.byref(segs[st].desc)),
+                              (ctypes.c_void_p(xs[st].data_ptr()), xs[st].stride(0), M,
+                               ctypes.byref(pool.desc), ctypes.byref(segs[st].desc), sl, n_sl)))
             modes = ["two"] + (["one"] if M <= 512 else [])
             for mode in modes:
-                pairs = [ev.create(4) for _ in range(reps)]
-                with torch.cuda.stream(stream):
-                    for i in range(-5, reps):
-                        e = pairs[i] if i >= 0 else None
-                        st = i % sets
-                        if mode == "one":
-                            o = sg.LaunchOpts(e[0], e[1]) if e else None
-                            sg.sgmv_lora_delta_ids(ids, xs[st], pool, segs[st], ys[st], opts=o)
-                        else:
-                            sg.sgmv_build_segments(ids, 64, C, out=segs[st],
-                                                   opts=sg.LaunchOpts(e[0], e[1]) if e else None)
-                            sg.sgmv_lora_delta(xs[st], pool, segs[st], ys[st],
-                                               opts=sg.LaunchOpts(e[2], e[3]) if e else None)
+                rcs = []
+
+                def build(i):
+                    rcs.append(lib.sgmv_build_segments_ex(*calls[i % sets][0], None, s_handle))
+
+                def delta(i):
+                    bargs, dargs = calls[i % sets]
+                    if mode == "one":
+                        rcs.append(lib.sgmv_lora_delta_ids_ex(bargs[0], *dargs, dflt, s_handle))
+                    else:
+                        rcs.append(lib.sgmv_lora_delta_ex(*dargs, dflt, s_handle))
+
+                def full(i):
+                    if mode == "two":
+                        build(i)
+                    delta(i)
+
+                for i in range(5):
+                    full(i)
                 torch.cuda.synchronize()
-                b = float(np.mean([ev.elapsed_ms(p_[0], p_[1]) for p_ in pairs])) * 1e3
-                d = 0.0 if mode == "one" else \
-                    float(np.mean([ev.elapsed_ms(p_[2], p_[3]) for p_ in pairs])) * 1e3
-                for p_ in pairs:
-                    ev.destroy(p_)
+                t, th = region_us(ev, stream, full, reps)
+                b, bh = region_us(ev, stream, build, reps) if mode == "two" else (None, 0.0)
+                d, dh = region_us(ev, stream, delta, reps) if mode == "two" else (t, th)
+                assert not any(rcs), f"library call failed with status {max(rcs)}"
                 row = {"M": M, "adapters": n_ad, "rank": R, "chunk": C, "launches": mode,
-                       "build_us": round(b, 2) if mode == "two" else None,
-                       "delta_us": round(d, 2) if mode == "two" else round(b, 2),
-                       "total_us": round(b + d, 2)}
+                       "build_us": round(b, 2) if b is not None else None,
+                       "delta_us": round(d, 2), "total_us": round(t, 2),
+                       "host_issue_us": [round(th, 2), round(bh, 2), round(dh, 2)]}
                 rows.append(row)
                 log(json.dumps(row))
             del segs
@@ -406,7 +439,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=8,
-                    help="timed steps between launches that carry timing events")
+                    help="steps between the sampled launches that carry dispatch events")
     ap.add_argument("--split-small", type=int, default=0,
                     help="column splits per small piece (0: library choice)")
     ap.add_argument("--split-large", type=int, default=0,
@@ -516,7 +549,8 @@ def main():
     torch.cuda.synchronize()
 
     # --trace: buffer set j replays its own seeded decode trace, one row per use of the set
-    rows = -(-(args.warmup + args.steps) // n_sets)
+    # (rows for the warm-up, the timed region and the sampled region)
+    rows = -(-(args.warmup + 2 * args.steps) // n_sets)
     if args.trace:
         for j, st in enumerate(sets):
             tr = workloads.decode_trace(rows, M=w.M, L=w.L, mean_len=args.trace_mean_len,
@@ -531,16 +565,16 @@ def main():
     cached_fn = lib.sgmv_build_segments_cached_ex
     ids_fn = lib.sgmv_lora_delta_ids_ex
     K = args.steps
-    # per timed step: events the kernels' own dispatches record (start, end) -- no extra
-    # packets in the stream
+    # launches that record a pair of events in their own dispatch (start, end of the kernel);
+    # they run in a region of their own, after the timed one
     every = max(1, args.event_every)
-    sampled = list(range(0, K, every))
-    evs = {i: ev.create(4) for i in sampled}
+    n_samp = len(range(0, K, every))
+    evs = [ev.create(4) for _ in range(n_samp)]
     plain = sg.LaunchOpts(n_split_small=args.split_small, n_split_large=args.split_large,
                           exchange=args.exchange)
-    opts_b = {i: sg.LaunchOpts(e[0], e[1]) for i, e in evs.items()}
-    opts_d = {i: sg.LaunchOpts(e[2], e[3], args.split_small, args.split_large, args.exchange)
-              for i, e in evs.items()}
+    opts_b = [sg.LaunchOpts(e[0], e[1]) for e in evs]
+    opts_d = [sg.LaunchOpts(e[2], e[3], args.split_small, args.split_large, args.exchange)
+              for e in evs]
     calls = []
     for st in sets:
         bargs = (ctypes.c_void_p(st["ids"].data_ptr()), w.M, w.L, w.chunk_size, 1,
@@ -554,25 +588,37 @@ def main():
         st = sets[g % n_sets]
         return st, g // n_sets
 
-    def step(i, timed=False):
-        g = i + (args.warmup if timed else 0)  # use count over warm-up and timed steps
-        bargs, dargs = calls[g % n_sets] if args.trace else calls[i % n_sets]
-        sample = timed and i in evs
+    def step(g, sample=None, part="both"):
+        """The launches of use g of buffer set g % n_sets (trace row g // n_sets); `sample`
+        picks a pair of dispatch events per launch; part: "both", "build" or "delta"."""
+        bargs, dargs = calls[g % n_sets]
+        od = opts_d[sample].ref() if sample is not None else plain.ref()
         if one_launch:
-            return ids_fn(bargs[0], *dargs, opts_d[i].ref() if sample else plain.ref(), s_handle)
-        ob = opts_b[i].ref() if sample else None
-        if args.trace:
-            st, r = trace_row(g)
-            ids_p = ctypes.c_void_p(st["trace_dev"][r].data_ptr())
-            if args.segment_cache:
-                rc = cached_fn(ids_p, *bargs[1:], ctypes.c_void_p(st["cache"].data_ptr()), ob,
-                               s_handle)
+            return ids_fn(bargs[0], *dargs, od, s_handle)
+        rc = 0
+        if part != "delta":
+            ob = opts_b[sample].ref() if sample is not None else None
+            if args.trace:
+                st, r = trace_row(g)
+                ids_p = ctypes.c_void_p(st["trace_dev"][r].data_ptr())
+                if args.segment_cache:
+                    rc = cached_fn(ids_p, *bargs[1:], ctypes.c_void_p(st["cache"].data_ptr()),
+                                   ob, s_handle)
+                else:
+                    rc = build_fn(ids_p, *bargs[1:], ob, s_handle)
             else:
-                rc = build_fn(ids_p, *bargs[1:], ob, s_handle)
-        else:
-            rc = build_fn(*bargs, ob, s_handle)
-        rc |= delta_fn(*dargs, opts_d[i].ref() if sample else plain.ref(), s_handle)
+                rc = build_fn(*bargs, ob, s_handle)
+        if part != "build":
+            rc |= delta_fn(*dargs, od, s_handle)
         return rc
+
+    def region(g0, n, part="both"):
+        """Seconds per step over n plain steps from use g0 (stream events around them), and the
+        host's issue time per step."""
+        rcs = []
+        t, host = region_us(ev, stream, lambda j: rcs.append(step(g0 + j, part=part)), n)
+        assert not any(rcs), f"library call failed with status {max(rcs)}"
+        return t / 1e6, host / 1e6
 
     rc = 0
     for i in range(args.warmup):
@@ -582,18 +628,64 @@ def main():
     for st in sets:
         assert int(st["seg"].info[3].item()) == sg.SGMV_OK
 
+    # the timed region: K plain steps, host clock and stream events around them
+    reg = ev.create(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev.record(reg[0], s_handle)
     for i in range(K):
-        rc |= step(i, timed=True)
+        rc |= step(args.warmup + i)
+    t_issue = time.perf_counter()
+    ev.record(reg[1], s_handle)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     assert rc == 0, f"library call failed with status {rc}"
-    build_ms = [0.0 if one_launch else ev.elapsed_ms(e[0], e[1]) for e in evs.values()]
-    delta_ms = [ev.elapsed_ms(e[2], e[3]) for e in evs.values()]
-    for e in evs.values():
+    region_s = ev.elapsed_ms(reg[0], reg[1]) / K / 1e3
+    ev.destroy(reg)
+
+    # the sampled region: K more steps, every `every`-th with dispatch events (per-launch
+    # durations; each such launch runs longer than a plain one)
+    g_samp = args.warmup + K
+    samp_g = []
+    for i in range(K):
+        j = i // every if i % every == 0 else None
+        if j is not None:
+            samp_g.append(g_samp + i)
+        rc |= step(g_samp + i, sample=j)
+    torch.cuda.synchronize()
+    assert rc == 0, f"library call failed with status {rc}"
+    build_ms = [0.0 if one_launch else ev.elapsed_ms(e[0], e[1]) for e in evs]
+    delta_ms = [ev.elapsed_ms(e[2], e[3]) for e in evs]
+    for e in evs:
         ev.destroy(e)
     n_ev = len(delta_ms)
+
+    # the delta kernel's average from plain launches: the timed region itself for the single
+    # launch, K launches of the delta alone for two (the segments of every set are built). The
+    # builder is too short to time alone (the host issues its launches no faster than the GPU
+    # runs them), so its figure is its share of the step: the step less the delta alone. The
+    # trace's batches change per step, so there the sampled launches give both.
+    host_us = {"timed_step": (t_issue - t0) / K * 1e6}
+    b_avg = 0.0
+    if one_launch:
+        timing = {"delta": "stream events around the timed steps (one launch per step)"}
+        d_avg = region_s
+    elif args.trace:
+        timing = {"delta": "dispatch events of the sampled launches",
+                  "builder": "dispatch events of the sampled launches"}
+        d_avg = sum(delta_ms) / n_ev / 1e3
+        b_avg = sum(build_ms) / n_ev / 1e3
+    else:
+        timing = {"delta": "stream events around K launches of the delta kernel alone",
+                  "builder": "the timed step less the delta alone (builder launch and gap)"}
+        d_avg, h = region(g_samp + K, K, part="delta")
+        host_us["delta_alone"] = h * 1e6
+        b_avg = max(region_s - d_avg, 0.0)
+    for k, v in host_us.items():
+        ref = region_s if k == "timed_step" else d_avg
+        if v > 0.9 * ref * 1e6:
+            log(f"warning: host issue {v:.2f} us per launch in the {k} region against "
+                f"{ref * 1e6:.2f} us: launch-bound")
 
     wall = t1 - t0
     ids_np = w.ids.numpy()
@@ -612,7 +704,6 @@ def main():
 
         steps_g = [args.warmup + i for i in range(K)]
         n_lora = sum(int((row_ids(g) >= 0).sum()) for g in steps_g) / K
-        samp_g = [args.warmup + i for i in sampled]
         alg_bytes = sum(workloads.algorithmic_bytes(row_ids(g), w.rank.numpy(), w.K, w.N, elem)
                         for g in samp_g) / len(samp_g)
         alg_flops = sum(workloads.algorithmic_flops(row_ids(g), w.rank.numpy(), w.K, w.N)
@@ -628,8 +719,6 @@ def main():
             "builder_us_changed_ids": sum(bm) / len(bm) * 1e3 if bm else None,
         }
         log(f"trace: {trace_info}")
-    d_avg = sum(delta_ms) / n_ev / 1e3  # seconds
-    b_avg = sum(build_ms) / n_ev / 1e3
     srt = sorted(delta_ms)
     achieved = alg_bytes / d_avg / 1e9
     # counters were taken on the workload's own batch and chunk size
@@ -638,8 +727,8 @@ def main():
     kname = "build + delta kernel" if one_launch else "delta kernel"
     log(f"step {wall / K * 1e6:.2f} us | {kname} avg {d_avg * 1e6:.2f} us "
         f"(p10 {srt[n_ev // 10] * 1e3:.2f}, p50 {srt[n_ev // 2] * 1e3:.2f}, "
-        f"p90 {srt[9 * n_ev // 10] * 1e3:.2f}, {n_ev} sampled launches) "
-        f"| builder avg {'(inside)' if one_launch else f'{b_avg * 1e6:.2f} us'} "
+        f"p90 {srt[9 * n_ev // 10] * 1e3:.2f} over {n_ev} sampled launches) "
+        f"| builder {'(inside)' if one_launch else f'{b_avg * 1e6:.2f} us'} "
         f"| {achieved:.0f} GB/s algorithmic "
         f"({achieved / HBM_PEAK_GBPS * 100:.1f}% of peak) | {alg_flops / d_avg / 1e12:.2f} TFLOP/s")
 
@@ -664,10 +753,12 @@ def main():
             "buffer_sets": n_sets,
             "step": ("segment build + fused delta in one launch (sgmv_lora_delta_ids)"
                      if one_launch else "device segment build launch + fused delta launch"),
-            "timed_launches_sampled": n_ev,
+            "kernel_timing": timing,
+            "host_issue_us": host_us,
             "delta_kernel_us": d_avg * 1e6,
-            "delta_kernel_us_p10_p50_p90": [srt[n_ev // 10] * 1e3, srt[n_ev // 2] * 1e3,
-                                            srt[9 * n_ev // 10] * 1e3],
+            "sampled_launches": n_ev,
+            "sampled_delta_kernel_us_p10_p50_p90": [srt[n_ev // 10] * 1e3, srt[n_ev // 2] * 1e3,
+                                                    srt[9 * n_ev // 10] * 1e3],
             "device": (f"{torch.cuda.get_device_name(dev)} "
                        f"({torch.cuda.get_device_properties(dev).gcnArchName})"),
             "hip_runtime": torch.version.hip,
