@@ -450,6 +450,9 @@ def main():
                     help="one: sgmv_lora_delta_ids (build inside the delta launch; bf16, "
                          "M <= 512); two: builder launch + delta launch; auto: one where it "
                          "applies")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed steps in one HIP graph and time its replay, as a "
+                         "serving loop replays its decode step (not with --trace)")
     ap.add_argument("--trace", action="store_true",
                     help="ids follow a seeded decode trace (sequences join and leave; one "
                          "trace per buffer set) instead of one fixed batch; needs --step two")
@@ -525,6 +528,9 @@ def main():
     one_launch = args.step == "one" or (args.step == "auto" and fits_one)
     if (args.trace or args.segment_cache) and (one_launch or not args.trace):
         print("--trace (and --segment-cache with it) needs --step two", file=sys.stderr)
+        sys.exit(2)
+    if args.graph and args.trace:
+        print("--graph replays fixed batches; it does not take --trace", file=sys.stderr)
         sys.exit(2)
     elem = 2 if w.dtype == torch.bfloat16 else 4
     per_set = (w.a.numel() + w.b.numel() + w.x.numel() + w.y0.numel()) * elem
@@ -628,13 +634,28 @@ def main():
     for st in sets:
         assert int(st["seg"].info[3].item()) == sg.SGMV_OK
 
-    # the timed region: K plain steps, host clock and stream events around them
+    # the timed region: K plain steps, host clock and stream events around them; with --graph
+    # the same K steps captured once in a HIP graph, run once untimed, then replayed
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(K):
+                rc |= step(args.warmup + i)
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        assert rc == 0, f"library call failed with status {rc}"
     reg = ev.create(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev.record(reg[0], s_handle)
-    for i in range(K):
-        rc |= step(args.warmup + i)
+    if graph is not None:
+        with torch.cuda.stream(stream):
+            graph.replay()
+    else:
+        for i in range(K):
+            rc |= step(args.warmup + i)
     t_issue = time.perf_counter()
     ev.record(reg[1], s_handle)
     torch.cuda.synchronize()
@@ -668,7 +689,8 @@ def main():
     host_us = {"timed_step": (t_issue - t0) / K * 1e6}
     b_avg = 0.0
     if one_launch:
-        timing = {"delta": "stream events around the timed steps (one launch per step)"}
+        timing = {"delta": "stream events around the timed steps (one launch per step)"
+                           + (", replayed from one HIP graph" if graph is not None else "")}
         d_avg = region_s
     elif args.trace:
         timing = {"delta": "dispatch events of the sampled launches",
@@ -752,7 +774,8 @@ def main():
             "lora_tokens_per_step": n_lora,
             "buffer_sets": n_sets,
             "step": ("segment build + fused delta in one launch (sgmv_lora_delta_ids)"
-                     if one_launch else "device segment build launch + fused delta launch"),
+                     if one_launch else "device segment build launch + fused delta launch")
+                    + (", K steps replayed from one HIP graph" if graph is not None else ""),
             "kernel_timing": timing,
             "host_issue_us": host_us,
             "delta_kernel_us": d_avg * 1e6,
