@@ -153,6 +153,38 @@ def test_build_and_delta_with_exchange(sg, name, P):
     compare(np32(yb), oracle_y(w, np32(w.y0)), w.dtype, what=f"{name} P={P}")
 
 
+# The single launch's adapter-major pieces when every adapter has rank 16 (A loaded before the
+# tokens are known) with the K-split exchange at several split counts. Ragged K (steps not a
+# multiple of the eight K slices: some slices empty), ragged N (column splits with empty
+# column groups), adapters whose tokens make no small piece or a small piece next to large
+# ones.
+ROLE_CASES = {
+    "decode_like": dict(M=256, K=4096, N=4096, L=64, R=16),
+    "few_tokens": dict(M=40, K=1024, N=1024, L=8, R=16, no_lora_frac=0.1),
+    "many_per_adapter": dict(M=300, K=2048, N=2048, L=5, R=16),
+    "ragged": dict(M=100, K=1152, N=640, L=10, R=16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROLE_CASES))
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_single_launch_rank16_exchange(sg, name, P):
+    """Bit-exact against two launches, also with every partner's partial computed locally."""
+    w = workloads.custom(name=name, seed=20 + P, **ROLE_CASES[name])
+    pool, x, y0, ids = upload(w, sg)
+    opts = sg.LaunchOpts(n_split_small=P, n_split_large=min(P, 4), exchange=1)
+    sep, ya, one, yb = _both(sg, w, pool, x, y0, ids, opts)
+    _same_segments(sep, one)
+    assert torch.equal(ya, yb)
+    local = sg.LaunchOpts(n_split_small=P, n_split_large=min(P, 4), exchange=1, exchange_wait=-1)
+    yc = _delta(sg, w, x, y0, lambda y, o: sg.sgmv_lora_delta_ids(ids, x, pool, one, y, opts=o),
+                local)
+    assert torch.equal(ya, yc)
+    _check_control_any_slot(sg, one, 2)
+    compare(np32(yb), oracle_y(w, np32(w.y0)), w.dtype, what=f"{name} P={P}")
+    check_no_adapter_rows(w, yb, w.y0)
+
+
 def test_build_and_delta_decode_full_size(sg):
     """The decode workload (one token per sequence, ids uniform over the pool)."""
     w = workloads.get("decode")
