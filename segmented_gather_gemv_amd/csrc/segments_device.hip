@@ -59,7 +59,7 @@ __device__ bool cache_hit(const int32_t* ids, int M, int L, int C, const int32_t
   return cache_unchanged(cache, M, L, C, differ);
 }
 
-// Stores this build's ids and header; called once the build is known to run.
+// Stores the ids and header of this call's segment build; called once it is known to run.
 template <int NT>
 __device__ void cache_store(const int32_t* ids, int M, int L, int C, int32_t* cache) {
   for (int i = threadIdx.x; i < M; i += NT) cache[SGMV_CACHE_HEADER + i] = ids[i];

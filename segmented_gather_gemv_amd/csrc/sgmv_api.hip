@@ -245,7 +245,7 @@ sgmv_status build_segments(const int32_t* lora_indices, int32_t M, int32_t L, in
       if (cache[0] == CACHE_TAG && cache[1] == M && cache[2] == L && cache[3] == chunk_size &&
           (M == 0 ||
            std::memcmp(cache + SGMV_CACHE_HEADER, lora_indices, sizeof(int32_t) * M) == 0))
-        return SGMV_OK;  // seg already holds this build (only successful ones are cached)
+        return SGMV_OK;  // seg already holds these segments (only successful builds are cached)
       cache[0] = 0;  // a failed build leaves the cache empty
     }
     const int st = host_build_segments(lora_indices, M, L, chunk_size, seg->sorted_token_ids,
