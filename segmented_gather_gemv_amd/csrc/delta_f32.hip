@@ -1,8 +1,8 @@
 // fp32 multi-LoRA delta on the vector ALU.
 //
 // Same work descriptors, column splits and workgroup mapping as the bf16 matrix-core path,
-// with plain fp32 fused multiply-adds: the shrink gives each thread one (row, rank) pair and
-// a serial dot product over K (Ascend article 3.2, first stage); the expand gives each
+// with plain fp32 fused multiply-adds: the shrink gives each wave one (row, rank) pair at a
+// time, its lanes splitting K (Ascend article 3.2, first stage); the expand gives each
 // thread one output column, streams that column's rank octets of B and updates every row of
 // the piece (second stage). Used for fp32 pools, whose products the bf16 matrix cores
 // cannot take; not tuned for speed.
@@ -46,17 +46,24 @@ __global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
       s_h[row * F_HS + j] = v;
     }
   } else {
+    // one wave per live (row, rank) pair: lane l takes k = l, l + 64, ... (coalesced,
+    // independent loads), then a butterfly sum over the lanes in a fixed order
     const float mult = MODE == MODE_SHRINK ? 1.f : scale;
     const float* ab = static_cast<const float*>(A.a) + (size_t)wi.lora * A.R_pad * A.K_pad;
-    for (int idx = tid; idx < SGMV_TILE_ROWS * 64; idx += F_THREADS) {
-      const int row = idx >> 6, j = idx & 63;
+    for (int idx = tid; idx < SGMV_TILE_ROWS * 64; idx += F_THREADS)
+      s_h[(idx >> 6) * F_HS + (idx & 63)] = 0.f;
+    __syncthreads();
+    const int lane = tid & (WAVE - 1), wv = tid / WAVE;
+    const int rr = r > 0 ? r : 1;
+    for (int q = wv; q < wi.rows * r; q += F_THREADS / WAVE) {
+      const int row = q / rr, j = q - row * rr;
+      const float* xr = static_cast<const float*>(A.x) + (size_t)s_tok[row] * (size_t)A.ldx;
+      const float* ar = ab + (size_t)j * A.K_pad;
       float s = 0.f;
-      if (row < wi.rows && j < r) {
-        const float* xr = static_cast<const float*>(A.x) + (size_t)s_tok[row] * (size_t)A.ldx;
-        const float* ar = ab + (size_t)j * A.K_pad;
-        for (int k = 0; k < A.K; ++k) s = fmaf(xr[k], ar[k], s);
-      }
-      s_h[row * F_HS + j] = s * mult;
+      for (int k = lane; k < A.K; k += WAVE) s = fmaf(xr[k], ar[k], s);
+#pragma unroll
+      for (int off = WAVE / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0) s_h[row * F_HS + j] = s * mult;
     }
   }
   __syncthreads();
