@@ -1,11 +1,11 @@
 // fp32 multi-LoRA delta on the vector ALU.
 //
 // Same work descriptors, column splits and workgroup mapping as the bf16 matrix-core path,
-// with plain fp32 fused multiply-adds: the shrink gives each wave one (row, rank) pair at a
-// time, its lanes splitting K (Ascend article 3.2, first stage); the expand gives each
-// thread one output column, streams that column's rank octets of B and updates every row of
-// the piece (second stage). Used for fp32 pools, whose products the bf16 matrix cores
-// cannot take; not tuned for speed.
+// with plain fp32 fused multiply-adds: the shrink gives each group of 16 lanes one (row,
+// rank) pair at a time, its lanes splitting K (Ascend article 3.2, first stage); the expand
+// gives each thread one output column, streams that column's rank octets of B and updates
+// every row of the piece (second stage). Used for fp32 pools, whose products the bf16
+// matrix cores cannot take; not tuned for speed.
 #include "common.h"
 
 namespace sgmv {
@@ -46,24 +46,30 @@ __global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
       s_h[row * F_HS + j] = v;
     }
   } else {
-    // one wave per live (row, rank) pair: lane l takes k = l, l + 64, ... (coalesced,
-    // independent loads), then a butterfly sum over the lanes in a fixed order
+    // four live (row, rank) pairs per wave at a time, 16 lanes each: lane l of a group takes
+    // k = l, l + 16, ... (coalesced, independent loads), then a butterfly sum over the group's
+    // lanes in a fixed order
+    constexpr int GL = 16, GPW = WAVE / GL;
     const float mult = MODE == MODE_SHRINK ? 1.f : scale;
     const float* ab = static_cast<const float*>(A.a) + (size_t)wi.lora * A.R_pad * A.K_pad;
     for (int idx = tid; idx < SGMV_TILE_ROWS * 64; idx += F_THREADS)
       s_h[(idx >> 6) * F_HS + (idx & 63)] = 0.f;
     __syncthreads();
-    const int lane = tid & (WAVE - 1), wv = tid / WAVE;
-    const int rr = r > 0 ? r : 1;
-    for (int q = wv; q < wi.rows * r; q += F_THREADS / WAVE) {
-      const int row = q / rr, j = q - row * rr;
-      const float* xr = static_cast<const float*>(A.x) + (size_t)s_tok[row] * (size_t)A.ldx;
-      const float* ar = ab + (size_t)j * A.K_pad;
+    const int lane = tid & (WAVE - 1), wv = tid / WAVE, sub = lane / GL, gl = lane % GL;
+    const int rr = r > 0 ? r : 1, npair = wi.rows * r;
+    for (int q0 = wv * GPW; q0 < npair; q0 += (F_THREADS / WAVE) * GPW) {  // wave-uniform
+      const int q = q0 + sub;
+      const bool live = q < npair;
+      const int row = live ? q / rr : 0, j = live ? q - row * rr : 0;
       float s = 0.f;
-      for (int k = lane; k < A.K; k += WAVE) s = fmaf(xr[k], ar[k], s);
+      if (live) {
+        const float* xr = static_cast<const float*>(A.x) + (size_t)s_tok[row] * (size_t)A.ldx;
+        const float* ar = ab + (size_t)j * A.K_pad;
+        for (int k = gl; k < A.K; k += GL) s = fmaf(xr[k], ar[k], s);
+      }
 #pragma unroll
-      for (int off = WAVE / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-      if (lane == 0) s_h[row * F_HS + j] = s * mult;
+      for (int off = GL / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (live && gl == 0) s_h[row * F_HS + j] = s * mult;
     }
   }
   __syncthreads();
