@@ -105,12 +105,17 @@ __global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
 #pragma unroll
       for (int row = 0; row < SGMV_TILE_ROWS; ++row) acc[row] = fmaf(s_h[row * F_HS + j], bj, acc[row]);
     }
+    // the old y of 16 rows at a time, all loaded before any is stored
 #pragma unroll
-    for (int row = 0; row < SGMV_TILE_ROWS; ++row) {
-      if (row < wi.rows) {
-        float* yp = yb + (size_t)s_tok[row] * (size_t)ldy + col;
-        *yp = *yp + acc[row];
-      }
+    for (int r0 = 0; r0 < SGMV_TILE_ROWS; r0 += 16) {
+      if (r0 >= wi.rows) break;
+      float yo[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        yo[i] = r0 + i < wi.rows ? yb[(size_t)s_tok[r0 + i] * (size_t)ldy + col] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (r0 + i < wi.rows) yb[(size_t)s_tok[r0 + i] * (size_t)ldy + col] = yo[i] + acc[r0 + i];
     }
   }
 }
