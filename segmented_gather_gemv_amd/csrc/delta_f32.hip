@@ -13,6 +13,48 @@ namespace sgmv {
 constexpr int F_THREADS = 256;
 constexpr int F_HS = 65;  // LDS row stride of the h tile
 
+// Expand of one piece over columns [v0, v1), one column per thread: y[tokens, col] += the
+// first NR rows of the h tile (rows past `rows` are zero) times that column's ranks of B.
+template <int NR>
+__device__ __forceinline__ void expand_columns(const DeltaArgs& A, const float* bb,
+                                               const float* s_h, const int* s_tok, int rows,
+                                               int r, int v0, int v1) {
+  for (int v = v0 + (int)threadIdx.x; v < v1; v += F_THREADS) {
+    float* yb = static_cast<float*>(A.slices[0].y);
+    int64_t ldy = A.slices[0].ldy;
+    int col = v, n = A.slices[0].n_begin + v;
+#pragma unroll
+    for (int i = 1; i < SGMV_MAX_SLICES; ++i) {
+      if (i < A.n_slices && v >= A.slices[i].v_begin) {
+        yb = static_cast<float*>(A.slices[i].y);
+        ldy = A.slices[i].ldy;
+        col = v - A.slices[i].v_begin;
+        n = A.slices[i].n_begin + col;
+      }
+    }
+    float acc[NR];
+#pragma unroll
+    for (int row = 0; row < NR; ++row) acc[row] = 0.f;
+    for (int j = 0; j < r; ++j) {
+      const float bj = bb[((size_t)(j >> 3) * A.N_pad + n) * 8 + (j & 7)];
+#pragma unroll
+      for (int row = 0; row < NR; ++row) acc[row] = fmaf(s_h[row * F_HS + j], bj, acc[row]);
+    }
+    // the old y of 16 rows at a time, all loaded before any is stored
+#pragma unroll
+    for (int r0 = 0; r0 < NR; r0 += 16) {
+      if (r0 >= rows) break;
+      float yo[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        yo[i] = r0 + i < rows ? yb[(size_t)s_tok[r0 + i] * (size_t)ldy + col] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (r0 + i < rows) yb[(size_t)s_tok[r0 + i] * (size_t)ldy + col] = yo[i] + acc[r0 + i];
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
   __shared__ int s_tok[SGMV_TILE_ROWS];
@@ -84,40 +126,10 @@ __global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
   }
 
   const float* bb = static_cast<const float*>(A.b) + (size_t)wi.lora * (A.R_pad / 8) * A.N_pad * 8;
-  for (int v = wi.v0 + tid; v < wi.v1; v += F_THREADS) {
-    float* yb = static_cast<float*>(A.slices[0].y);
-    int64_t ldy = A.slices[0].ldy;
-    int col = v, n = A.slices[0].n_begin + v;
-#pragma unroll
-    for (int i = 1; i < SGMV_MAX_SLICES; ++i) {
-      if (i < A.n_slices && v >= A.slices[i].v_begin) {
-        yb = static_cast<float*>(A.slices[i].y);
-        ldy = A.slices[i].ldy;
-        col = v - A.slices[i].v_begin;
-        n = A.slices[i].n_begin + col;
-      }
-    }
-    float acc[SGMV_TILE_ROWS];
-#pragma unroll
-    for (int row = 0; row < SGMV_TILE_ROWS; ++row) acc[row] = 0.f;
-    for (int j = 0; j < r; ++j) {
-      const float bj = bb[((size_t)(j >> 3) * A.N_pad + n) * 8 + (j & 7)];
-#pragma unroll
-      for (int row = 0; row < SGMV_TILE_ROWS; ++row) acc[row] = fmaf(s_h[row * F_HS + j], bj, acc[row]);
-    }
-    // the old y of 16 rows at a time, all loaded before any is stored
-#pragma unroll
-    for (int r0 = 0; r0 < SGMV_TILE_ROWS; r0 += 16) {
-      if (r0 >= wi.rows) break;
-      float yo[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        yo[i] = r0 + i < wi.rows ? yb[(size_t)s_tok[r0 + i] * (size_t)ldy + col] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (r0 + i < wi.rows) yb[(size_t)s_tok[r0 + i] * (size_t)ldy + col] = yo[i] + acc[r0 + i];
-    }
-  }
+  if (wi.rows <= 16)  // uniform: small pieces accumulate only the rows they have
+    expand_columns<16>(A, bb, s_h, s_tok, wi.rows, r, wi.v0, wi.v1);
+  else
+    expand_columns<SGMV_TILE_ROWS>(A, bb, s_h, s_tok, wi.rows, r, wi.v0, wi.v1);
 }
 
 hipError_t launch_delta_f32(int mode, DeltaArgs A, LaunchEvents ev, hipStream_t stream) {
