@@ -126,8 +126,10 @@ __global__ __launch_bounds__(F_THREADS) void delta_f32_kernel(DeltaArgs A) {
   }
 
   const float* bb = static_cast<const float*>(A.b) + (size_t)wi.lora * (A.R_pad / 8) * A.N_pad * 8;
-  if (wi.rows <= 16)  // uniform: small pieces accumulate only the rows they have
+  if (wi.rows <= 16)  // uniform: a piece accumulates only the rows it can have
     expand_columns<16>(A, bb, s_h, s_tok, wi.rows, r, wi.v0, wi.v1);
+  else if (wi.rows <= 32)
+    expand_columns<32>(A, bb, s_h, s_tok, wi.rows, r, wi.v0, wi.v1);
   else
     expand_columns<SGMV_TILE_ROWS>(A, bb, s_h, s_tok, wi.rows, r, wi.v0, wi.v1);
 }
