@@ -17,9 +17,9 @@ Sources, cited by page title and section:
     segment; rows resolved through sorted token ids).
   * Ascend article: vLLM-Ascend LoRA operator article, sections 1.1 (delta
     (alpha/r)(x A^T) B^T added to the base output), 2.1 (per-adapter rank r and alpha; a
-    maximum rank), 3.3 (decode SGMV: group rows by adapter, compact descriptors: start row,
-    row count, adapter index), 4.1 (row-count threshold between the vector and the matrix
-    unit), 3.2 (the scale on either side of the expand, or folded into B at load time),
+    maximum rank), 3.3 (decode SGMV: group rows by adapter), 3.2 (the scale on either side
+    of the expand, or folded into B at load time), 4.4 (a merged weight for batches with
+    one or two adapters),
     5.2 (merged vs unmerged consistency) and 5.3 (rows without adapter are skipped).
 
 Readings where the pages are silent or disagree (each one is listed with its reason in the
@@ -110,27 +110,6 @@ def segments(ids: Sequence[int], L: int, chunk_size: int = 0) -> Dict[str, np.nd
         "seg_lora_ids": np.asarray(seg_lora, dtype=np.int32),
         "num_segments": len(seg_lora),
     }
-
-
-def tiles(seg_indptr: np.ndarray, seg_lora_ids: np.ndarray, tile_rows: int = 64,
-          small_max: int = 16) -> Tuple[np.ndarray, np.ndarray]:
-    """Compact work descriptors (Ascend article 3.3: start row, row count, adapter index),
-    one per piece of at most ``tile_rows`` rows of a segment, pieces in segment order.
-    Pieces of at most ``small_max`` rows form the small list, the rest the large list
-    (Ascend article 4.1: dispatch by row count). Each row is
-    (adapter, start in sorted order, rows, segment index)."""
-    large, small = [], []
-    S = len(seg_lora_ids)
-    for s in range(S):
-        a, b = int(seg_indptr[s]), int(seg_indptr[s + 1])
-        start = a
-        while start < b:
-            rows = min(tile_rows, b - start)
-            rec = (int(seg_lora_ids[s]), start, rows, s)
-            (small if rows <= small_max else large).append(rec)
-            start += rows
-    as_arr = lambda v: np.asarray(v, dtype=np.int32).reshape(-1, 4)
-    return as_arr(large), as_arr(small)
 
 
 # ----------------------------------------------------------------------------------------
@@ -246,16 +225,7 @@ def merge_weight(w: np.ndarray, a: np.ndarray, b: np.ndarray, rank: np.ndarray,
                                           @ np.asarray(a[l, :r, :], np.float64))
 
 
-def max_segments(M: int, L: int, chunk_size: int) -> int:
-    """Upper bound on the number of segments: at most one per distinct adapter, plus one
-    per extra chunk when chunking."""
-    base = min(M, L)
-    if chunk_size > 0:
-        return min(M, base + M // chunk_size)
-    return base
-
-
 __all__ = [
-    "BadAdapterId", "validate_ids", "segments", "tiles", "shrink", "expand", "lora_delta",
-    "max_segments", "round_bf16", "fold_scale", "merge_weight",
+    "BadAdapterId", "validate_ids", "segments", "shrink", "expand", "lora_delta",
+    "round_bf16", "fold_scale", "merge_weight",
 ]

@@ -70,20 +70,69 @@ def assert_same_as_oracle(ids, L, C):
 
 
 def check_records(got, ref):
-    """Descriptor records: header fields equal the oracle's pieces, [4..16) zero, token slots
-    of a small piece hold its sorted token ids then -1, those of a large piece all -1."""
-    lg, sm = oracle.tiles(ref["seg_indptr"], ref["seg_lora_ids"], sg.TILE_ROWS, sg.SMALL_ROWS)
+    """Descriptor records against the oracle's segments, by the invariants include/sgmv.h
+    states for them (the piece split is the library's, with the library's constants): every
+    segment is cut, from its first sorted row, into pieces of SGMV_TILE_ROWS rows, the last
+    one shorter; each record names its segment's adapter, its first row and its rows, in
+    segment order within its class; a piece is small exactly when it has at most
+    SGMV_SMALL_ROWS rows; together the pieces cover every sorted row of a segment once;
+    [4..16) are zero; the token slots of a small piece hold its sorted token ids then -1,
+    those of a large piece all -1."""
     st = np.asarray(ref["sorted_token_ids"])
-    for recs, want, small in ((got["large_tiles"], lg, False), (got["small_tiles"], sm, True)):
+    ip = np.asarray(ref["seg_indptr"])
+    sl = np.asarray(ref["seg_lora_ids"])
+    S = int(ref["num_segments"])
+    n_rows = int(ip[S]) if S else 0
+    covered = np.zeros(n_rows, dtype=np.int64)
+    pieces = {}
+    for recs, small in ((got["large_tiles"], False), (got["small_tiles"], True)):
         recs = recs.numpy().reshape(-1, sg.TILE_INTS)
-        assert np.array_equal(recs[:, :4], want)
-        assert np.all(recs[:, 4:16] == 0)
+        if len(recs):
+            assert np.all(np.diff(recs[:, 1]) > 0), "records follow segment order"
         for rec in recs:
-            start, rows = int(rec[1]), int(rec[2])
+            lora, start, rows, s = (int(v) for v in rec[:4])
+            assert 0 <= s < S
+            assert lora == int(sl[s])
+            assert 1 <= rows <= sg.TILE_ROWS
+            assert (rows <= sg.SMALL_ROWS) == small
+            assert int(ip[s]) <= start and start + rows <= int(ip[s + 1])
+            assert (start - int(ip[s])) % sg.TILE_ROWS == 0, "pieces start every TILE_ROWS"
+            covered[start:start + rows] += 1
+            pieces.setdefault(s, []).append((start, rows))
+            assert np.all(rec[4:16] == 0)
             toks = np.full(16, -1)
             if small:
                 toks[:rows] = st[start:start + rows]
             assert np.array_equal(rec[16:], toks)
+    assert np.all(covered == 1), "every sorted row of a segment in exactly one piece"
+    for s in range(S):  # all pieces of a segment but its last are full
+        ps = sorted(pieces[s])
+        assert all(r == sg.TILE_ROWS for _, r in ps[:-1])
+
+
+def test_record_checker_catches_corrupted_records():
+    """check_records itself: each plausible corruption of a correct build is rejected."""
+    ids = np.concatenate([np.full(150, 3), np.arange(40) % 5, np.full(20, 1), [-1, -1]])
+    ref = oracle.segments(ids, 6, 0)
+    good = host_build(ids, 6, 0)
+    check_records(good, ref)
+
+    def corrupt(cls, row, col, delta):
+        bad = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in good.items()}
+        recs = bad[cls].view(-1, sg.TILE_INTS)
+        recs[row, col] += delta
+        return bad
+
+    n_small = good["small_tiles"].numel() // sg.TILE_INTS
+    assert n_small >= 2 and good["large_tiles"].numel() // sg.TILE_INTS >= 2
+    for cls, row, col, delta in [("large_tiles", 0, 0, 1),    # wrong adapter
+                                 ("large_tiles", 1, 1, -1),   # overlapping pieces
+                                 ("large_tiles", 0, 2, -1),   # a row left out
+                                 ("small_tiles", 0, 3, 1),    # wrong segment
+                                 ("small_tiles", 1, 16, 1),   # wrong token in a slot
+                                 ("small_tiles", 0, 5, 7)]:   # reserved word not zero
+        with pytest.raises(AssertionError):
+            check_records(corrupt(cls, row, col, delta), ref)
 
 
 def test_host_builder_worked_example():
@@ -136,6 +185,8 @@ def test_host_builder_empty_and_all_negative():
 
 
 def test_capacities_bound_the_outputs():
+    """The capacities sgmv_segments_init reports bound what the oracle's segments need: one
+    entry per segment, and per piece of SGMV_TILE_ROWS rows in its class."""
     rng = np.random.default_rng(1)
     for _ in range(50):
         M = int(rng.integers(0, 3000))
@@ -144,10 +195,14 @@ def test_capacities_bound_the_outputs():
         seg = sg.sgmv_segments_alloc(M, L, C, "cpu")
         d = seg.desc
         ids = rng.integers(-1, L, size=M)
+        if M:
+            ids[: M // 3] = rng.integers(0, L)  # long buckets: many large pieces
         ref = oracle.segments(ids, L, C)
-        lg, sm = oracle.tiles(ref["seg_indptr"], ref["seg_lora_ids"])
+        lens = np.diff(ref["seg_indptr"])
+        n_large = int(sum(c // sg.TILE_ROWS + (c % sg.TILE_ROWS > sg.SMALL_ROWS) for c in lens))
+        n_small = int(sum(0 < c % sg.TILE_ROWS <= sg.SMALL_ROWS for c in lens))
         assert ref["num_segments"] <= d.seg_cap
-        assert len(lg) <= d.large_cap and len(sm) <= d.small_cap
+        assert n_large <= d.large_cap and n_small <= d.small_cap
 
 
 # ---------------------------------------------------------------------------------------

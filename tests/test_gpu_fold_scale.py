@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from test_gpu_parity import DEV, check_no_adapter_rows, compare, np32, sample_rows
+from test_gpu_parity import DEV, check_no_adapter_rows, compare, np32
 
 pytestmark = pytest.mark.gpu
 
@@ -156,7 +156,6 @@ def test_power_of_two_fold_is_bit_identical(sg, name):
     b = _all_paths(sg, w, _pack(sg, w, True), x, y0, ids)
     for k in a:
         assert torch.equal(a[k], b[k]), k
-    rows = sample_rows(w, 32)
     ref = oracle.lora_delta(np32(w.x), np32(w.y0), w.ids.numpy(), np32(w.a), np32(w.b),
-                            w.rank.numpy(), w.alpha.numpy(), rows=rows)
-    compare(np32(b["fused"]), ref, w.dtype, rows=rows, what=name)
+                            w.rank.numpy(), w.alpha.numpy())
+    compare(np32(b["fused"]), ref, w.dtype, what=name)

@@ -12,7 +12,7 @@ import torch
 
 import workloads
 from test_gpu_parity import (DEV, _check_control, _xch_control, check_no_adapter_rows, compare,
-                             np32, oracle_y, sample_rows, upload)
+                             np32, oracle_y, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -192,8 +192,12 @@ def test_build_and_delta_decode_full_size(sg):
     sep, ya, one, yb = _both(sg, w, pool, x, y0, ids, None)
     _same_segments(sep, one)
     assert torch.equal(ya, yb)
-    rows = sample_rows(w, 64)
-    compare(np32(yb), oracle_y(w, np32(w.y0), rows=rows), w.dtype, rows=rows, what="decode")
+    compare(np32(yb), oracle_y(w, np32(w.y0)), w.dtype, what="decode")
+    check_no_adapter_rows(w, yb, w.y0)
+    # the delta alone (zero base) through the single launch
+    z = torch.zeros_like(y0)
+    yz = _delta(sg, w, x, z, lambda v, o: sg.sgmv_lora_delta_ids(ids, x, pool, one, v), None)
+    compare(np32(yz), oracle_y(w, np.zeros((w.M, w.N))), w.dtype, what="decode zero base")
 
 
 def test_build_and_delta_reuse_per_step(sg):

@@ -238,6 +238,14 @@ SMALL_CASES = {
     "f32_odd": dict(M=40, K=100, N=37, L=3, R=3, dtype=torch.float32, w_std=0.1),
     "f32_mixed_rank": dict(M=90, K=64, N=70, L=6, R=64, ranks=[1, 5, 16, 64],
                            dtype=torch.float32, w_std=0.1, seq_lens=[70, 20]),
+    # fp32 pieces at the expand's row-count branches: 16, 17, 32, 33, 64 rows, a 64 + 16
+    # segment, one row
+    "f32_piece_edges": dict(M=243, K=160, N=200, L=7, R=16, dtype=torch.float32, w_std=0.1,
+                            seq_lens=[16, 17, 32, 33, 64, 80, 1],
+                            seq_adapters=[3, 0, 6, 1, 5, 2, 4]),
+    "f32_piece_edges_c16": dict(M=243, K=160, N=200, L=7, R=16, dtype=torch.float32,
+                                w_std=0.1, seq_lens=[16, 17, 32, 33, 64, 80, 1],
+                                seq_adapters=[3, 0, 6, 1, 5, 2, 4], chunk=16),
 }
 
 
@@ -382,7 +390,7 @@ def test_slices_in_any_order(sg):
 
 
 # ---------------------------------------------------------------------------------------
-# full-size workloads, checked on sampled tokens
+# full-size workloads, every row against the oracle
 # ---------------------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed", "qkv"])
 @pytest.mark.parametrize("zero_base", [False, True])
@@ -390,30 +398,37 @@ def test_fused_full_size(sg, name, zero_base):
     w = workloads.get(name)
     if zero_base:
         w.y0 = torch.zeros_like(w.y0)
+    print(f"fused full size {name} zero_base={zero_base}", flush=True)
     y_gpu, seg = run_fused(w, sg)
     assert int(seg.info[3].item()) == sg.SGMV_OK
-    rows = sample_rows(w, 128)
-    ref = oracle_y(w, np32(w.y0), rows=rows)
-    compare(np32(y_gpu), ref, w.dtype, rows=rows, what=name)
+    ref = oracle_y(w, np32(w.y0))
+    compare(np32(y_gpu), ref, w.dtype, what=name)
     check_no_adapter_rows(w, y_gpu, w.y0)
 
 
-@pytest.mark.parametrize("name", ["decode", "mixed"])
-def test_unfused_full_size(sg, name):
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "mixed", "qkv"])
+@pytest.mark.parametrize("zero_base", [False, True])
+def test_unfused_full_size(sg, name, zero_base):
     w = workloads.get(name)
+    if zero_base:
+        w.y0 = torch.zeros_like(w.y0)
+    print(f"unfused full size {name} zero_base={zero_base}", flush=True)
     pool, x, y, ids = upload(w, sg)
     seg = sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True)
     h = sg.sgmv_shrink(x, pool, seg)
-    sg.sgmv_expand(h, pool, seg, y)
+    outs = slice_views(w, y)
+    sg.sgmv_expand(h, pool, seg, outs if len(outs) > 1 else outs[0][0])
     torch.cuda.synchronize()
-    rows = sample_rows(w, 96)
-    h_ref = oracle.shrink(np32(w.x), w.ids.numpy(), np32(w.a), w.rank.numpy(), rows=rows)
-    hr = h_ref[rows]
-    hg = h.cpu().numpy()[rows]
-    lora = w.ids.numpy()[rows] >= 0
-    assert np.linalg.norm(hg[lora] - hr[lora]) / np.linalg.norm(hr[lora]) <= 1e-4
-    ref = oracle_y(w, np32(w.y0), rows=rows)
-    compare(np32(y), ref, w.dtype, rows=rows, what=name + " unfused")
+    for t, n0 in outs:
+        y[:, n0:n0 + t.shape[1]] = t
+    h_ref = oracle.shrink(np32(w.x), w.ids.numpy(), np32(w.a), w.rank.numpy())
+    lora = w.ids.numpy() >= 0
+    hg = h.cpu().numpy()[lora]
+    hr = h_ref[lora]
+    assert np.linalg.norm(hg - hr) / np.linalg.norm(hr) <= 1e-4
+    ref = oracle_y(w, np32(w.y0))
+    compare(np32(y), ref, w.dtype, what=name + " unfused")
+    check_no_adapter_rows(w, y, w.y0)
 
 
 # ---------------------------------------------------------------------------------------
@@ -507,24 +522,27 @@ def test_exchange_workspace_optional(sg):
 
 
 def test_exchange_full_decode_forced_local(sg):
-    """The decode workload with every missing partial computed locally, on sampled rows,
-    bit-identical to the default call."""
+    """The decode workload with every missing partial computed locally, bit-identical to the
+    default call, every row against the oracle."""
     w = workloads.get("decode")
     pool, x, y0, ids = upload(w, sg)
     seg = sg.sgmv_build_segments(ids, w.L, 0, on_device=True)
     a = _fused_opts(sg, w, seg, pool, x, y0)
     b = _fused_opts(sg, w, seg, pool, x, y0, exchange_wait=-1)
     assert torch.equal(a, b)
-    rows = sample_rows(w, 64)
-    compare(np32(a), oracle_y(w, np32(w.y0), rows=rows), w.dtype, rows=rows, what="decode")
+    compare(np32(a), oracle_y(w, np32(w.y0)), w.dtype, what="decode")
 
 
 @pytest.mark.parametrize("name", ["prefill", "mixed", "qkv"])
-def test_exchange_full_size_forced_local(sg, name):
+@pytest.mark.parametrize("zero_base", [False, True])
+def test_exchange_full_size_forced_local(sg, name, zero_base):
     """Full-size workloads with large pieces: the default call (large and small pieces split
     their shrink over K) is bit-identical to the call that computes every partner's partial
-    locally, and matches the oracle on sampled rows."""
+    locally, and every row matches the oracle."""
     w = workloads.get(name)
+    if zero_base:
+        w.y0 = torch.zeros_like(w.y0)
+    print(f"exchange forced local {name} zero_base={zero_base}", flush=True)
     pool, x, y0, ids = upload(w, sg)
     seg = sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True)
     def call(**kw):
@@ -540,5 +558,5 @@ def test_exchange_full_size_forced_local(sg, name):
     a = call()
     b = call(exchange_wait=-1)
     assert torch.equal(a, b)
-    rows = sample_rows(w, 64)
-    compare(np32(a), oracle_y(w, np32(w.y0), rows=rows), w.dtype, rows=rows, what=name)
+    compare(np32(a), oracle_y(w, np32(w.y0)), w.dtype, what=name)
+    check_no_adapter_rows(w, a, w.y0)

@@ -3,7 +3,7 @@
   * the worked segment example printed on the Punica page (golden fixture);
   * exhaustive comparison of the segment builder with a second, differently written
     definition (a stable sort by first-appearance key) over every short id string;
-  * structural invariants of segments and tiles;
+  * structural invariants of segments;
   * merged vs unmerged equivalence x(W + s A^T B^T) = xW + s (x A^T) B^T through a dense
     K x N matrix (Punica page, SGMV section; Ascend article 1.1 and 5.2);
   * the single-adapter special case as two plain matmuls over the whole batch;
@@ -184,35 +184,6 @@ def test_bad_ids_raise(bad):
         oracle.lora_delta(np.zeros((len(bad), 2)), np.zeros((len(bad), 2)), np.asarray(bad),
                           np.zeros((4, 1, 2)), np.zeros((4, 2, 1)), np.ones(4, np.int32),
                           np.ones(4))
-
-
-def test_segments_bound():
-    rng = np.random.default_rng(5)
-    for C in (0, 1, 3, 64):
-        for _ in range(20):
-            M = int(rng.integers(0, 300))
-            L = int(rng.integers(1, 50))
-            ids = rng.integers(-1, L, size=M)
-            out = oracle.segments(ids, L, C)
-            assert out["num_segments"] <= oracle.max_segments(M, L, C)
-
-
-def test_tiles_cover_segments():
-    rng = np.random.default_rng(3)
-    ids = np.concatenate([np.full(200, 4), rng.integers(-1, 9, size=300), np.full(65, 2)])
-    seg = oracle.segments(ids, 9, 0)
-    large, small = oracle.tiles(seg["seg_indptr"], seg["seg_lora_ids"], 64, 16)
-    covered = np.zeros(int(seg["seg_indptr"][-1]), dtype=int)
-    for lst in (large, small):
-        for l, start, rows, s in lst:
-            assert 1 <= rows <= 64
-            assert seg["seg_indptr"][s] <= start and start + rows <= seg["seg_indptr"][s + 1]
-            assert seg["seg_lora_ids"][s] == l
-            covered[start:start + rows] += 1
-    assert np.all(covered == 1)
-    assert np.all(large[:, 2] > 16) and np.all(small[:, 2] <= 16)
-    # pieces follow segment order inside each list
-    assert np.all(np.diff(large[:, 1]) > 0) and np.all(np.diff(small[:, 1]) > 0)
 
 
 # ---------------------------------------------------------------------------------------

@@ -2,7 +2,7 @@
 sequence keeps its adapter, so the grouping changes only when sequences join or leave).
 
 Bar: at every step of a seeded decode trace the cached call leaves the segment arrays bit-equal
-to a fresh build of that step's ids; when the ids (and M, L, chunk size) equal those of the
+to the oracle's segments of that step's ids (and to a fresh build of them); when the ids (and M, L, chunk size) equal those of the
 last build made through the cache, it writes nothing (checked by poisoning the arrays); a
 zeroed cache[0] forces a rebuild. Host path on the CPU; device path (three builder kernels by
 batch size) and the fused delta on cached segments on the GPU.
@@ -13,8 +13,10 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import segmented_gather_gemv_amd as sg
 import workloads
+from test_abi_host import check_records
 
 KEYS = ("sorted_token_ids", "seg_indptr", "seg_lora_ids", "large_tiles", "small_tiles",
         "num_segments", "status")
@@ -27,6 +29,21 @@ def _same(a, b):
             assert torch.equal(ha[k], hb[k]), k
         else:
             assert ha[k] == hb[k], k
+
+
+def _same_as_oracle(seg, ids, L, C):
+    """The arrays in seg equal the oracle's segments of these ids (bad ids read as -1, as the
+    device builder treats them), and the records satisfy their invariants."""
+    got = seg.host()
+    clean = np.asarray(ids.cpu(), dtype=np.int64).copy()
+    clean[(clean < -1) | (clean >= L)] = -1
+    ref = oracle.segments(clean, L, C)
+    M = clean.shape[0]
+    assert np.array_equal(got["sorted_token_ids"].numpy()[:M], ref["sorted_token_ids"])
+    assert np.array_equal(got["seg_indptr"].numpy(), ref["seg_indptr"])
+    assert np.array_equal(got["seg_lora_ids"].numpy(), ref["seg_lora_ids"])
+    assert got["num_segments"] == ref["num_segments"]
+    check_records(got, ref)
 
 
 def _poison(seg):
@@ -49,6 +66,7 @@ def _trace_check(dev, M, L, C, steps, mean_len, admit_every, seed):
     for s in range(steps):
         ids = trace[s].to(dev)
         sg.sgmv_build_segments_cached(ids, seg, cache, on_device=on_device)
+        _same_as_oracle(seg, trace[s], L, C)
         fresh = sg.sgmv_build_segments(ids, L, C, on_device=on_device)
         _same(seg, fresh)
         hits += int(s > 0 and torch.equal(trace[s], trace[s - 1]))
@@ -82,6 +100,7 @@ def test_host_cache_hit_writes_nothing():
     seg = sg.sgmv_segments_alloc(100, 10, 0, "cpu")
     cache = sg.sgmv_segments_cache_alloc(100, "cpu")
     sg.sgmv_build_segments_cached(ids, seg, cache, on_device=False)
+    _same_as_oracle(seg, ids, 10, 0)
     _same(seg, sg.sgmv_build_segments(ids, 10, 0, on_device=False))
     _poison(seg)
     sg.sgmv_build_segments_cached(ids.clone(), seg, cache, on_device=False)
@@ -89,11 +108,13 @@ def test_host_cache_hit_writes_nothing():
     ids2 = ids.clone()
     ids2[17] = (int(ids2[17]) + 1) % 10
     sg.sgmv_build_segments_cached(ids2, seg, cache, on_device=False)
+    _same_as_oracle(seg, ids2, 10, 0)
     _same(seg, sg.sgmv_build_segments(ids2, 10, 0, on_device=False))
     # a zeroed tag forces a rebuild of unchanged ids
     _poison(seg)
     cache[0] = 0
     sg.sgmv_build_segments_cached(ids2, seg, cache, on_device=False)
+    _same_as_oracle(seg, ids2, 10, 0)
     _same(seg, sg.sgmv_build_segments(ids2, 10, 0, on_device=False))
 
 
@@ -162,6 +183,7 @@ def test_device_cache_hit_writes_nothing(gpu, M, L, C):
     seg = sg.sgmv_segments_alloc(M, L, C, DEV)
     cache = sg.sgmv_segments_cache_alloc(M, DEV)
     sg.sgmv_build_segments_cached(ids, seg, cache)
+    _same_as_oracle(seg, ids, L, C)
     _same(seg, sg.sgmv_build_segments(ids, L, C))
     _poison(seg)
     sg.sgmv_build_segments_cached(ids.clone(), seg, cache)
@@ -170,10 +192,12 @@ def test_device_cache_hit_writes_nothing(gpu, M, L, C):
     ids2 = ids.clone()
     ids2[M - 1] = -1 if int(ids2[M - 1]) >= 0 else 0  # the last token changes
     sg.sgmv_build_segments_cached(ids2, seg, cache)
+    _same_as_oracle(seg, ids2, L, C)
     _same(seg, sg.sgmv_build_segments(ids2, L, C))
     _poison(seg)
     cache[0] = 0
     sg.sgmv_build_segments_cached(ids2, seg, cache)
+    _same_as_oracle(seg, ids2, L, C)
     _same(seg, sg.sgmv_build_segments(ids2, L, C))
 
 
@@ -186,6 +210,7 @@ def test_device_cache_bad_ids_cached_with_status(gpu):
     for _ in range(2):
         sg.sgmv_build_segments_cached(ids, seg, cache)
         assert int(seg.info[3]) == sg.SGMV_EBADID
+        _same_as_oracle(seg, ids, 3, 0)
         _same(seg, sg.sgmv_build_segments(ids, 3, 0))
 
 
@@ -193,8 +218,9 @@ def test_device_cache_bad_ids_cached_with_status(gpu):
 def test_fused_delta_on_cached_segments(gpu):
     """Decode steps through the cache, then the fused delta with the K-split exchange: y is
     bit-equal to the delta on freshly built segments at every step (hits leave the exchange
-    control words uncleared; every call still advances them by exactly 64)."""
-    from test_gpu_parity import upload
+    control words uncleared; every call still advances them by exactly 64) and meets the
+    oracle's bar."""
+    from test_gpu_parity import compare, np32, upload
     w = workloads.custom(M=128, K=512, N=512, L=16, R=16, name="cache", seed=9)
     pool, x, y0, _ = upload(w, sg)
     trace = workloads.decode_trace(12, M=128, L=16, mean_len=30, admit_every=4, seed=2)
@@ -211,3 +237,6 @@ def test_fused_delta_on_cached_segments(gpu):
         sg.sgmv_lora_delta(x, pool, fresh, yb, opts=opts)
         torch.cuda.synchronize()
         assert torch.equal(ya, yb), s
+        ref = oracle.lora_delta(np32(w.x), np32(w.y0), trace[s].numpy(), np32(w.a), np32(w.b),
+                                w.rank.numpy(), w.alpha.numpy())
+        compare(np32(ya), ref, w.dtype, what=f"cached step {s}")

@@ -210,17 +210,22 @@ def custom(M: int, K: int, N: int, L: int, R: int, dtype: torch.dtype = torch.bf
            seed: int = SEED, ranks: Optional[Sequence[int]] = None, no_lora_frac: float = 0.0,
            seq_lens: Optional[Sequence[int]] = None, w_std: float = 0.02, chunk: int = 0,
            alphas: Optional[Sequence[float]] = None, y0_zero: bool = False,
-           slices: Optional[Sequence[Tuple[int, int]]] = None, name: str = "custom") -> Workload:
+           slices: Optional[Sequence[Tuple[int, int]]] = None, name: str = "custom",
+           seq_adapters: Optional[Sequence[int]] = None) -> Workload:
     """General generator for parity cases: odd shapes, ragged tails, mixed ranks, id -1.
 
     ``ranks``: per-adapter rank choices (uniform over the list); default all R.
     ``seq_lens``: if given, ids are constant per sequence (prefill-like), else i.i.d.
+    ``seq_adapters``: with seq_lens, the adapter of each sequence (else drawn uniformly).
     """
     g = torch.Generator().manual_seed(seed)
     if seq_lens is not None:
         seq_lens = [int(v) for v in seq_lens]
         assert sum(seq_lens) == M
         seq_ids = torch.randint(0, L, (len(seq_lens),), generator=g, dtype=torch.int32)
+        if seq_adapters is not None:
+            assert len(seq_adapters) == len(seq_lens)
+            seq_ids = torch.tensor(list(seq_adapters), dtype=torch.int32)
         ids = torch.repeat_interleave(seq_ids, torch.tensor(seq_lens, dtype=torch.int64))
         ids = ids.to(torch.int32)
     else:
