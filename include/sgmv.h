@@ -135,8 +135,9 @@ sgmv_status sgmv_pool_pack_ex(const void* a_user, const void* b_user, const int3
  * cross buckets. For the worked example of the Punica page, ids 2,2,2,5,5,1,1 give
  * sorted_token_ids 0..6, seg_indptr [0,3,5,7], seg_lora_ids [2,5,1].
  *
- * Work descriptors ("tiles"): every segment is cut into pieces of at most SGMV_TILE_ROWS
- * rows, in segment order. A piece of at most SGMV_SMALL_ROWS rows is small, otherwise large.
+ * Work descriptors ("tiles"): every segment is cut, from its first sorted row, into pieces
+ * of SGMV_TILE_ROWS rows, the last one shorter; records follow segment order within each
+ * class. A piece of at most SGMV_SMALL_ROWS rows is small, otherwise large.
  * Each descriptor is a record of SGMV_TILE_INTS int32 at tiles + i * SGMV_TILE_INTS:
  *   [0] adapter, [1] first row in sorted order, [2] rows, [3] segment, [4..15] 0,
  *   [16..31] for a small piece its token ids (sorted_token_ids[first .. first + rows)), then
