@@ -342,6 +342,31 @@ sgmv_status sgmv_lora_delta_ids_ex(const int32_t* lora_indices, const void* x, i
                                    const sgmv_launch_opts* opts, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): sgmv_lora_delta_ids with the K-split
+ * exchange workspace in a static device array of SGMV_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends, instead of in seg->exchange (which
+ * is ignored). Same arguments, launches and results, bit for bit, as sgmv_lora_delta_ids on
+ * segments with a workspace. The call allocates nothing: no hipMalloc or hipFree, no
+ * allocating library routine; its first call on a device looks up that device's copy of the
+ * array. The caller still provides the inputs and the outputs (ids, x, the pool, the
+ * segment arrays of seg, y).
+ * Limit: the exchange layout of seg (sgmv_segments_init's exchange_bytes) must fit in
+ * SGMV_NOALLOC_SCRATCH_BYTES, e.g. a 256-token batch over a pool of up to 1024 adapters, or a
+ * 512-token batch over up to 440; larger ones return SGMV_EUNSUPPORTED before anything runs.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents (its
+ * counters stay consistent across completed calls): calls that overlap on one GPU race, so
+ * order them on one stream.
+ * Errors: as sgmv_lora_delta_ids; EUNSUPPORTED beyond the limit; EHIP if the array's device
+ * address cannot be looked up.
+ * ------------------------------------------------------------------------------------ */
+#define SGMV_NOALLOC_SCRATCH_BYTES (16 << 20)
+sgmv_status sgmv_lora_delta_ids_noalloc(const int32_t* lora_indices, const void* x, int64_t ldx,
+                                        int32_t M, const sgmv_pool* pool,
+                                        const sgmv_segments* seg, const sgmv_slice* out,
+                                        int32_t n_slices, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
  * Merged weight of one adapter (Ascend article 1.1 and 4.4: for a batch that holds only one
  * or two long-lived adapters, merging each into a copy of the base weight and running the
  * plain GEMM can beat the unmerged delta; Punica page, SGMV section: merged and unmerged

@@ -35,6 +35,7 @@ MAX_SLICES = 4
 DEVICE_BUILDER_MAX_L = 1024
 CACHE_HEADER = 4
 FOLD_SCALE = 1
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = [
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
@@ -42,7 +43,7 @@ EXPORTED = [
     "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
     "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached", "sgmv_build_segments_cached_ex",
     "sgmv_pool_pack_ex", "sgmv_merge_adapter", "sgmv_merge_adapter_ex", "sgmv_status_string",
-    "sgmv_version", "sgmv_chunk_size_for_batch",
+    "sgmv_version", "sgmv_chunk_size_for_batch", "sgmv_lora_delta_ids_noalloc",
 ]
 
 
@@ -129,12 +130,14 @@ def _load():
     lib.sgmv_lora_delta_ids_ex.argtypes = [vp, vp, i64, i32, P(_Pool), P(_Segments), P(_Slice),
                                            i32, O, vp]
     lib.sgmv_merge_adapter_ex.argtypes = [vp, i64, vp, i64, P(_Pool), i32, O, vp]
+    lib.sgmv_lora_delta_ids_noalloc.argtypes = [vp, vp, i64, i32, P(_Pool), P(_Segments),
+                                                P(_Slice), i32, vp]
     for f in ["sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_init", "sgmv_build_segments",
               "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_build_segments_ex",
               "sgmv_shrink_ex", "sgmv_expand_ex", "sgmv_lora_delta_ex", "sgmv_lora_delta_ids",
               "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached",
               "sgmv_build_segments_cached_ex", "sgmv_pool_pack_ex", "sgmv_merge_adapter",
-              "sgmv_merge_adapter_ex"]:
+              "sgmv_merge_adapter_ex", "sgmv_lora_delta_ids_noalloc"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.sgmv_status_string.argtypes = [ctypes.c_int]
     lib.sgmv_status_string.restype = ctypes.c_char_p
@@ -469,6 +472,24 @@ def sgmv_lora_delta_ids(ids: torch.Tensor, x: torch.Tensor, pool: Pool, seg: Seg
                                        _opts(opts), _stream(x.device)), "sgmv_lora_delta_ids")
 
 
+def sgmv_lora_delta_ids_noalloc(ids: torch.Tensor, x: torch.Tensor, pool: Pool,
+                                seg: Segments,
+                                y: Union[torch.Tensor, Sequence[SliceSpec]]) -> None:
+    """sgmv_lora_delta_ids with the exchange workspace in the library's static device array
+    (seg.exchange is not used): for callers that cannot allocate device memory. Calls that
+    overlap on one GPU share that array; order them on one stream."""
+    _check_x(x, pool)
+    M = x.shape[0]
+    if ids.dtype != torch.int32 or ids.device != x.device or ids.numel() != M:
+        raise TypeError("ids must be an int32 tensor of M entries on x's device")
+    ids = ids.contiguous()
+    arr, n = _slices(y, pool, M)
+    _check(_lib.sgmv_lora_delta_ids_noalloc(_ptr(ids), _ptr(x), x.stride(0), M,
+                                            ctypes.byref(pool.desc), ctypes.byref(seg.desc),
+                                            arr, n, _stream(x.device)),
+           "sgmv_lora_delta_ids_noalloc")
+
+
 def sgmv_merge_adapter(w: torch.Tensor, pool: Pool, adapter: int,
                        out: Optional[torch.Tensor] = None,
                        opts: Optional[LaunchOpts] = None) -> torch.Tensor:
@@ -492,6 +513,6 @@ __all__ = [
     "LIB_PATH", "EXPORTED", "SgmvError", "Pool", "Segments", "LaunchOpts", "library",
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_alloc", "sgmv_build_segments",
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_lora_delta_ids",
-    "sgmv_segments_cache_alloc", "sgmv_build_segments_cached", "sgmv_merge_adapter",
+    "sgmv_lora_delta_ids_noalloc", "sgmv_segments_cache_alloc", "sgmv_build_segments_cached", "sgmv_merge_adapter",
     "sgmv_chunk_size_for_batch",
 ]
