@@ -215,6 +215,74 @@ def calibration_copy(args):
     log(f"elementwise copy of {args.copy_mib} MiB, {reps} times over {args.copy_sets} pairs")
 
 
+def stream_ceiling(read_bytes: int, write_bytes: int, reps: int, ev, stream) -> dict:
+    """The best time of a hand-written HIP streaming kernel (libsgmv_bench.so) that reads
+    read_bytes and writes write_bytes in 16-byte lanes in one launch, over a sweep of launch
+    shapes (threads per workgroup x loads in flight per thread), with the buffers rotating over
+    sets larger than twice the last-level cache so every launch starts in HBM; each shape is
+    timed like the delta kernel (stream events around `reps` back-to-back launches)."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "segmented_gather_gemv_amd", "libsgmv_bench.so"))
+    lib.sgmv_bench_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    rb = (read_bytes + 15) // 16 * 16
+    wb = (write_bytes + 15) // 16 * 16
+    n_sets = max(2, -(-2 * MALL_BYTES // (rb + wb)))
+    g = torch.Generator(device="cuda").manual_seed(5)
+    src = [torch.randint(0, 1 << 30, (rb // 4,), dtype=torch.int32, device="cuda", generator=g)
+           for _ in range(n_sets)]
+    dst = [torch.empty(max(wb // 4, 4), dtype=torch.int32, device="cuda") for _ in range(n_sets)]
+    torch.cuda.synchronize()
+    h = ctypes.c_void_p(stream.cuda_stream)
+    rows = []
+    for block in (256, 512, 1024):
+        for unroll in (1, 2, 4, 8, 16):
+            def launch(i):
+                rc = lib.sgmv_bench_stream(src[i % n_sets].data_ptr(), rb,
+                                           dst[i % n_sets].data_ptr(), wb, block, unroll,
+                                           None, None, h)
+                assert rc == 0, f"sgmv_bench_stream failed ({rc})"
+            with torch.cuda.stream(stream):
+                for i in range(2 * n_sets):
+                    launch(i)
+            torch.cuda.synchronize()
+            us, host = region_us(ev, stream, launch, reps)
+            rows.append({"block": block, "unroll": unroll, "us": round(us, 3),
+                         "host_issue_us": round(host, 2)})
+    best = min(rows, key=lambda r: r["us"])
+    gbps = (rb + wb) / (best["us"] * 1e-6) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"read_bytes": rb, "write_bytes": wb, "buffer_sets": n_sets, "best": best,
+            "gbps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS, "sweep": rows}
+
+
+def flush_last_level_cache(n_bytes: int = 2 * MALL_BYTES):
+    """Writes n_bytes of device memory (untimed), so what setup left in the 256 MB memory-side
+    cache is evicted before a timed region."""
+    import torch
+    buf = torch.empty(n_bytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(1)
+    torch.cuda.synchronize()
+    del buf
+
+
+def device_clocks() -> dict:
+    """Shader and memory clocks as rocm-smi reports them (current level), or an error note."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        d = json.loads(r.stdout)
+        card = d[sorted(d)[0]]
+        keep = {k: v for k, v in card.items() if "clock" in k.lower() and
+                any(c in k.lower() for c in ("sclk", "mclk", "fclk", "socclk"))}
+        return keep or card
+    except Exception as e:  # the tool may be missing or print no JSON
+        return {"error": f"rocm-smi --showclocks: {type(e).__name__}"}
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle as it stands, on the same batch, repeated for about `seconds`."""
     import numpy as np
@@ -478,6 +546,11 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--copy-sets", type=int, default=1,
                     help="buffer pairs the calibration copy rotates over")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only time the streaming reference kernel with the workload's byte "
+                         "mix over its launch-shape sweep")
+    ap.add_argument("--no-stream-ceiling", action="store_true",
+                    help="skip the streaming reference kernel in the benchmark line")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
                     help="delta FETCH, delta WRITE, copy FETCH, copy WRITE counter CSVs")
     args = ap.parse_args()
@@ -488,6 +561,20 @@ def main():
         return
     if args.calibration_copy:
         calibration_copy(args)
+        return
+    if args.stream_ceiling:
+        import torch
+        import workloads
+        w = workloads.get(args.workload)
+        elem = 2 if w.dtype == torch.bfloat16 else 4
+        ids_np = w.ids.numpy()
+        alg = workloads.algorithmic_bytes(ids_np, w.rank.numpy(), w.K, w.N, elem)
+        wr = int((ids_np >= 0).sum()) * w.N * elem
+        stream = torch.cuda.Stream()
+        res = stream_ceiling(alg - wr, wr, max(50, min(args.steps, 400)), HipEvents(), stream)
+        log(json.dumps({k: v for k, v in res.items() if k != "sweep"}))
+        print(json.dumps({"metric": "streaming reference kernel, the workload's byte mix",
+                          "workload": args.workload, **res}), flush=True)
         return
     if args.merge:
         merge_bench(args)
@@ -556,7 +643,11 @@ def main():
 
     # --trace: buffer set j replays its own seeded decode trace, one row per use of the set
     # (rows for the warm-up, the timed region and the sampled region)
-    rows = -(-(args.warmup + 2 * args.steps) // n_sets)
+    # sampled launches (dispatch events) in a region of their own: at least 50 of them
+    every = max(1, args.event_every)
+    n_samp = max(50, len(range(0, args.steps, every)))
+    K_samp = n_samp * every
+    rows = -(-(args.warmup + args.steps + K_samp) // n_sets)
     if args.trace:
         for j, st in enumerate(sets):
             tr = workloads.decode_trace(rows, M=w.M, L=w.L, mean_len=args.trace_mean_len,
@@ -573,8 +664,6 @@ def main():
     K = args.steps
     # launches that record a pair of events in their own dispatch (start, end of the kernel);
     # they run in a region of their own, after the timed one
-    every = max(1, args.event_every)
-    n_samp = len(range(0, K, every))
     evs = [ev.create(4) for _ in range(n_samp)]
     plain = sg.LaunchOpts(n_split_small=args.split_small, n_split_large=args.split_large,
                           exchange=args.exchange)
@@ -627,6 +716,12 @@ def main():
         return t / 1e6, host / 1e6
 
     rc = 0
+    # setup: one call per buffer set, so that every set's first-use costs (address
+    # translation fills for buffers the kernel has not touched yet) are paid before the warm-up;
+    # a serving loop reuses one pool and its activation buffers every step
+    for i in range(n_sets):
+        rc |= step(i)
+    torch.cuda.synchronize()
     for i in range(args.warmup):
         rc |= step(i)
     torch.cuda.synchronize()
@@ -647,6 +742,7 @@ def main():
         torch.cuda.synchronize()
         assert rc == 0, f"library call failed with status {rc}"
     reg = ev.create(2)
+    flush_last_level_cache()  # setup's residue leaves the memory-side cache
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev.record(reg[0], s_handle)
@@ -664,11 +760,12 @@ def main():
     region_s = ev.elapsed_ms(reg[0], reg[1]) / K / 1e3
     ev.destroy(reg)
 
-    # the sampled region: K more steps, every `every`-th with dispatch events (per-launch
-    # durations; each such launch runs longer than a plain one)
+    clocks = device_clocks()  # right after the timed region
+    # the sampled region: n_samp * every more steps, every `every`-th with dispatch events
+    # (per-launch durations; each such launch runs longer than a plain one)
     g_samp = args.warmup + K
     samp_g = []
-    for i in range(K):
+    for i in range(K_samp):
         j = i // every if i % every == 0 else None
         if j is not None:
             samp_g.append(g_samp + i)
@@ -700,7 +797,8 @@ def main():
     else:
         timing = {"delta": "stream events around K launches of the delta kernel alone",
                   "builder": "the timed step less the delta alone (builder launch and gap)"}
-        d_avg, h = region(g_samp + K, K, part="delta")
+        flush_last_level_cache()
+        d_avg, h = region(g_samp + K_samp, K, part="delta")
         host_us["delta_alone"] = h * 1e6
         b_avg = max(region_s - d_avg, 0.0)
     for k, v in host_us.items():
@@ -782,6 +880,7 @@ def main():
             "sampled_launches": n_ev,
             "sampled_delta_kernel_us_p10_p50_p90": [srt[n_ev // 10] * 1e3, srt[n_ev // 2] * 1e3,
                                                     srt[9 * n_ev // 10] * 1e3],
+            "clocks_after_timed_region": clocks,
             "device": (f"{torch.cuda.get_device_name(dev)} "
                        f"({torch.cuda.get_device_properties(dev).gcnArchName})"),
             "hip_runtime": torch.version.hip,
@@ -808,6 +907,19 @@ def main():
                                      else "")
     del sets
     torch.cuda.empty_cache()
+    if not args.no_stream_ceiling and not args.trace:
+        # the same byte mix through the streaming reference kernel: the memory system's
+        # ceiling for one launch that moves these bytes
+        wr = int(round(n_lora)) * w.N * elem
+        sc = stream_ceiling(int(alg_bytes) - wr, wr, max(50, min(K, 400)), ev, stream)
+        sc["delta_kernel_frac_of_ceiling"] = sc["best"]["us"] / (d_avg * 1e6)
+        result["config"]["stream_ceiling"] = {k: v for k, v in sc.items() if k != "sweep"}
+        log("streaming reference sweep (block x loads per thread: us): " +
+            ", ".join(f"{r['block']}x{r['unroll']}: {r['us']:.2f}" for r in sc["sweep"]))
+        log(f"streaming reference, same bytes: {sc['best']['us']:.2f} us "
+            f"({sc['gbps']:.0f} GB/s, {sc['frac_of_peak'] * 100:.1f}% of peak; block "
+            f"{sc['best']['block']} x {sc['best']['unroll']} loads); delta kernel at "
+            f"{sc['delta_kernel_frac_of_ceiling'] * 100:.1f}% of it")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

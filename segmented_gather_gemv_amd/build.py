@@ -2,7 +2,8 @@
 
 HIP sources are compiled by hipcc for gfx950 (packed fp32 instructions disabled), the
 host-only segment builder by g++; the objects are linked by hipcc into
-``segmented_gather_gemv_amd/libsgmv.so``. Always rebuilds. Run as
+``segmented_gather_gemv_amd/libsgmv.so``. The benchmark's streaming reference kernel
+(``csrc/bench/``, not part of the library) goes into ``libsgmv_bench.so``. Always rebuilds. Run as
 ``python -m segmented_gather_gemv_amd.build`` or call ``build()``.
 """
 from __future__ import annotations
@@ -19,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsgmv.so")
+BENCH_LIB = os.path.join(PKG, "libsgmv_bench.so")
+BENCH_SRC = os.path.join(CSRC, "bench")
 ARCH = os.environ.get("SGMV_OFFLOAD_ARCH", "gfx950")
 
 HIP_FLAGS = [
@@ -64,6 +67,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         o = os.path.join(OUT_DIR, f + ".o")
         objs.append(o)
         cmds.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, f), "-o", o])
+    bench_objs = []
+    for f in sorted(f for f in os.listdir(BENCH_SRC) if f.endswith(".hip")):
+        o = os.path.join(OUT_DIR, "bench_" + f + ".o")
+        bench_objs.append(o)
+        cmds.append([hipcc, *HIP_FLAGS, "-c", os.path.join(BENCH_SRC, f), "-o", o])
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
@@ -71,6 +79,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    tmp = BENCH_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *bench_objs])
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 
