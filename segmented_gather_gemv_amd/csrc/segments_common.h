@@ -326,7 +326,7 @@ struct WgBuildDst {  // the builder's outputs, written by the writer workgroup o
 // blocks by blocked_tile once the count is known), returns the descriptor, its adapter, first
 // sorted row and rows, and writes its token ids to s_tok. Ends without a barrier: the
 // caller's next barrier makes s_tok visible, and S may be written again only after it.
-__device__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile, bool writer,
+__device__ __forceinline__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile, bool writer,
                                const WgBuildDst& D, const WgBuildLds& S, int* s_tok) {
   constexpr int NW = FUSED_BUILD_WAVES;
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
