@@ -67,6 +67,11 @@ typedef enum { SGMV_F32 = 0, SGMV_BF16 = 1 } sgmv_dtype;
 #define SGMV_MAX_SLICES 4
 /* Largest batch for which sgmv_lora_delta_ids builds the segments inside the delta launch. */
 #define SGMV_FUSED_BUILD_MAX_M 512
+/* Largest batch on which fused bf16 calls run every large piece as parts of SGMV_SMALL_ROWS
+ * rows (part j: rows 16j .. 16j + 15 of the piece), each with the small pieces' column
+ * split, so that batches of a few adapters spread over as many workgroups as batches of
+ * many. The descriptor records are the same either way. */
+#define SGMV_PART_SPLIT_MAX_M 1024
 
 /* ------------------------------------------------------------------------------------ *
  * Adapter pool (Fused-LoRA page Step 1; Ascend article 2.1 and 4.2).
@@ -160,10 +165,13 @@ sgmv_status sgmv_pool_pack_ex(const void* a_user, const void* b_user, const int3
  * partial sums pass through this buffer). Results do not depend on timing: a workgroup that
  * waits too long for its partners computes their partials itself, bit-identically.
  * Layout: [large_cap + small_cap][16] int32 control words indexed like the descriptor records
- * (word 0: the piece's arrival counter, which every call advances by exactly 64; the rest
- * reserved), padded to 256 bytes; then [small_cap][SGMV_EXCHANGE_MAX_SPLITS][16][64] fp32
+ * (word 0: the piece's arrival counter, which every call advances by exactly 64; when large
+ * pieces run as parts, word j of a large record is part j's counter; the rest reserved),
+ * padded to 256 bytes; then [small_cap][SGMV_EXCHANGE_MAX_SPLITS][16][64] fp32
  * small-piece partials; then [large_cap][SGMV_EXCHANGE_MAX_SPLITS_LARGE][64][64] fp32
- * large-piece partials. Zero-fill it when it is allocated; the device builder clears the
+ * large-piece partials (a part j of a large piece keeps its split q partial, 16 rows of ncol
+ * floats, at q * 64 * ncol + j * 16 * ncol floats into the piece's slots; ncol is 32 for
+ * adapter ranks up to 32, else 64). Zero-fill it when it is allocated; the device builder clears the
  * control words on every build. Fused calls that share one segments object with an exchange
  * workspace must be ordered on one stream.
  * ------------------------------------------------------------------------------------ */
@@ -299,10 +307,11 @@ sgmv_status sgmv_lora_delta_ids(const int32_t* lora_indices, const void* x, int6
  *     hipEventElapsedTime(start, stop) is the kernel's execution time. The caller creates,
  *     owns and destroys them.
  *   n_split_small, n_split_large: workgroups across the output columns for each small /
- *     large work descriptor in expand and fused calls; 0 = the library's choice, else 1..64.
+ *     large work descriptor in expand and fused calls (for each part of a large piece when
+ *     large pieces run as parts); 0 = the library's choice, else 1..64.
  *   exchange: fused calls only; 0 = the library's choice, 1 = split a piece class's shrink
  *     over K whenever seg->exchange is set and its split count is in range (small: 2..8,
- *     large: 2..4), -1 = never.
+ *     large: 2..4; parts of large pieces: 2..8 when R_pad <= 32, else 2..4), -1 = never.
  *   exchange_wait: bound on a small piece's wait for its partners' partial sums, in units of
  *     10 ns (large pieces wait up to 10 times as long); 0 = default (20 us), -1 = no wait
  *     (every partial not yet published is computed locally; same results, for testing that

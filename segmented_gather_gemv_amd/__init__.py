@@ -33,6 +33,8 @@ TILE_INTS = 32
 MAX_RANK = 64
 MAX_SLICES = 4
 DEVICE_BUILDER_MAX_L = 1024
+FUSED_BUILD_MAX_M = 512
+PART_SPLIT_MAX_M = 1024
 CACHE_HEADER = 4
 FOLD_SCALE = 1
 NOALLOC_SCRATCH_BYTES = 16 << 20

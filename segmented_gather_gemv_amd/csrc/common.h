@@ -69,8 +69,10 @@ struct DeltaArgs {
   int32_t n_split_large;  // workgroups across output columns per large piece
   int32_t n_split_small;  // ... per small piece
   int32_t grid_large;     // workgroups [0, grid_large) take large pieces, the rest small ones
+                          // (unless small_first)
   int32_t n_slices;
   int32_t v_total;        // sum of slice widths
+  int32_t rsplit;         // 4: large pieces run as 16-row parts (small batches), else 1
   // K-split exchange (fused calls): control words indexed like the records, partial tiles
   // of small and of large pieces (layout in workspace.h)
   int32_t* xctl;
@@ -87,6 +89,8 @@ struct DeltaArgs {
   // t holds adapter t's small piece (its tokens found by one ballot per wave, no sort), and
   // workgroup grid_writer builds and writes the segment arrays
   int32_t amajor, grid_writer;
+  // nonzero: workgroups [0, small_first) take small pieces, the next grid_large large ones
+  int32_t small_first;
   int32_t spec;  // with amajor: A and B of a small piece loaded before its tokens are known
   int32_t *w_sorted, *w_indptr, *w_seg_lora, *w_tiles, *w_info;
   SliceArg slices[SGMV_MAX_SLICES];
@@ -100,7 +104,8 @@ struct LaunchEvents {
 };
 
 // Piece and column split of this workgroup, from its index alone. Workgroups
-// [0, grid_large) take large pieces, the rest small ones; within a class, piece i runs on
+// [0, grid_large) take large pieces, the rest small ones (with small_first, the small class
+// comes first and has small_first workgroups, a multiple of 8); within a class, piece i runs on
 // XCD i % 8 (workgroup b runs on XCD b % 8) and its P column splits on consecutive slots of
 // that XCD. Returns false for a workgroup past the class capacity. With `blocked_large`, a
 // large piece's `tile` is only its cyclic slot, to be turned into the piece by blocked_tile
@@ -109,8 +114,13 @@ __device__ __forceinline__ bool locate_piece(const DeltaArgs& A, bool split, boo
                                              int& tile, int& p, int& P,
                                              bool blocked_large = false) {
   int b = blockIdx.x;
-  small = b >= A.grid_large;
-  if (small) b -= A.grid_large;
+  if (A.small_first) {
+    small = b < A.small_first;
+    if (!small) b -= A.small_first;
+  } else {
+    small = b >= A.grid_large;
+    if (small) b -= A.grid_large;
+  }
   P = split ? (small ? A.n_split_small : A.n_split_large) : 1;
   const int slot = b >> 3;
   const int q = slot / P;

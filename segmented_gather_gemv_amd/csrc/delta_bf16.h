@@ -51,6 +51,8 @@ struct Piece {
   float scale;
   int v0, v1;         // column range, in the concatenation of the output slices
   int tile, split, nsplit;  // descriptor index in its class, column split and split count
+  int xsub;  // part index when a large piece runs as 16-row parts (its exchange is the
+             // large class's), else -1
 };
 
 // Where concatenated output column v lives: its slice's y, row stride, y column, pool column.
@@ -611,7 +613,8 @@ __device__ __forceinline__ void store_partial(const Piece& pc, const ShrinkGeom&
         v = s_h[row * HS + j];
       else
         v = part_sum<NRK>(s_part, G, row, j, pc.r);
-      __hip_atomic_store(slot + row * 64 + j, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(slot + row * S::NCOL + j, v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -625,12 +628,30 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
   using S = XchShape<NRK, LARGE>;
   const int tid = threadIdx.x, P = pc.nsplit, p = pc.split;
   const int entries = G.nrt * 16 * S::NCOL;
-  const size_t rec = LARGE ? (size_t)pc.tile : (size_t)A.large_cap + pc.tile;
-  uint32_t* counter = reinterpret_cast<uint32_t*>(A.xctl) + rec * XCH_CTL_INTS;
-  float* part = (LARGE ? A.xpart_large : A.xpart_small) + (size_t)pc.tile * S::MAXS * S::TILE;
+  // slots: a small piece's, a large piece's, or those of part j of a large piece, which
+  // counts arrivals in word j of the piece's control block and keeps its split q partial (16
+  // rows of NCOL floats) at q * 64 NCOL + j * 16 NCOL floats into the piece's partial slots
+  // (up to 8 splits at NCOL 32, 4 at NCOL 64)
+  const bool prt = !LARGE && NRK <= 2 && pc.xsub >= 0;  // parts: ranks up to 32 only
+  const size_t rec = (LARGE || prt) ? (size_t)pc.tile : (size_t)A.large_cap + pc.tile;
+  uint32_t* counter =
+      reinterpret_cast<uint32_t*>(A.xctl) + rec * XCH_CTL_INTS + (prt ? pc.xsub : 0);
+  float* part;
+  int xs;
+  if (LARGE || prt) {
+    part = A.xpart_large + (size_t)pc.tile * SGMV_EXCHANGE_MAX_SPLITS_LARGE * XCH_LARGE_TILE;
+    xs = (int)XCH_LARGE_TILE;
+    if (prt) {
+      part += pc.xsub * SGMV_SMALL_ROWS * S::NCOL;
+      xs = SGMV_TILE_ROWS * S::NCOL;
+    }
+  } else {
+    part = A.xpart_small + (size_t)pc.tile * SGMV_EXCHANGE_MAX_SPLITS * XCH_SMALL_TILE;
+    xs = (int)XCH_SMALL_TILE;
+  }
   const int64_t wait = LARGE ? A.xwait_large : A.xwait;
 
-  store_partial<NRK, LARGE>(pc, G, s_part, s_h, part + p * S::TILE);
+  store_partial<NRK, LARGE>(pc, G, s_part, s_h, part + p * xs);
   wait_stores();
   __syncthreads();
   if (tid == 0) {
@@ -662,7 +683,7 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
       else
         shrink_range<NRK, ALIGNED>(A, pc, G, s_tok, q * nch / P, (q + 1) * nch / P, s_part);
       __syncthreads();
-      store_partial<NRK, LARGE>(pc, G, s_part, s_h, part + q * S::TILE);
+      store_partial<NRK, LARGE>(pc, G, s_part, s_h, part + q * xs);
     }
     wait_stores();
     __syncthreads();
@@ -677,7 +698,7 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
       const int idx = tid + e * DT_THREADS;
       const int row = idx / S::NCOL, j = idx - row * S::NCOL;
       pv[q][e] = (q < P && idx < entries)
-                     ? __hip_atomic_load(part + q * S::TILE + row * 64 + j, __ATOMIC_RELAXED,
+                     ? __hip_atomic_load(part + q * xs + row * S::NCOL + j, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT)
                      : 0.f;
     }
@@ -709,7 +730,7 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
   constexpr bool xkernel = XCH && MODE == MODE_FUSED;
-  const bool xch = xkernel && A.xch_small;
+  const bool xch = xkernel && ((NRK <= 2 && pc.xsub >= 0) ? A.xch_large : A.xch_small);
   // K steps whose loads are issued together, and column groups per wave whose B and y are
   // prefetched, sized so that everything in flight fits in registers. With the exchange a
   // workgroup covers a fraction of K, one step per load round suffices, and the smaller
@@ -929,14 +950,17 @@ __attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_ker
       const int id = threadIdx.x < (unsigned)A.M ? A.ids[threadIdx.x] : 0;
       const WgBuildDst dst{A.w_sorted, A.w_indptr, A.w_seg_lora, A.w_tiles, A.w_info,
                            A.seg_cap, A.large_cap, A.small_cap};
-      wg_build(id, A.M, A.L, A.chunk, false, -8 /* a slot with no piece */, true, dst,
+      wg_build(id, A.M, A.L, A.chunk, false, -8 /* a slot with no piece */, false, true, dst,
                wg_build_lds(reinterpret_cast<unsigned char*>(s_part), A.L), s_tok);
       return;
     }
   }
   bool small;
-  int tile, p, P;
+  int tile, p, P, sub = 0;
   if (!locate_piece(A, split, small, tile, p, P, true)) return;
+  // large pieces as 16-row parts: fused calls on small batches at ranks up to 32 (the host
+  // sets rsplit 1 otherwise; kernels for larger ranks leave the code out)
+  const int rsplit = (MODE == MODE_FUSED && NRKM <= 2) ? A.rsplit : 1;
 
   const int tid = threadIdx.x;
   const bool table = A.L <= RANK_TABLE_MAX;
@@ -961,6 +985,7 @@ __attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_ker
         pc.tile = tile;
         pc.split = p;
         pc.nsplit = P;
+        pc.xsub = -1;
         if (pc.v0 >= pc.v1 && !(XCH && A.xch_small)) return;
         small_piece<MODE, 1, ALIGNED, XCH, true>(A, pc, s_tok, s_part, s_h, &s_mask, rank_l,
                                                  scale_l);
@@ -991,10 +1016,23 @@ __attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_ker
     const WgBuildDst dst{A.w_sorted, A.w_indptr, A.w_seg_lora, A.w_tiles, A.w_info,
                          A.seg_cap, A.large_cap, A.small_cap};
     const WgBuildLds S = wg_build_lds(reinterpret_cast<unsigned char*>(s_part), A.L);
-    const WgBuildOut bo =
-        wg_build(id, A.M, A.L, A.chunk, small, tile, !A.amajor && blockIdx.x == 0, dst, S, s_tok);
+    if (!small && rsplit > 1 && A.amajor) {
+      // adapter-indexed launch: the large class has work only if some adapter has more tokens
+      // than a small piece holds; a histogram in LDS decides before the full build
+      int* s_cnt = reinterpret_cast<int*>(s_part);
+      for (int i = tid; i < A.L; i += DT_THREADS) s_cnt[i] = 0;
+      __syncthreads();
+      if (tid < A.M && id >= 0 && id < A.L) atomicAdd(s_cnt + id, 1);
+      __syncthreads();
+      bool big = false;
+      for (int i = tid; i < A.L; i += DT_THREADS) big = big || s_cnt[i] > SGMV_SMALL_ROWS;
+      if (!__syncthreads_or(big)) return;  // uniform: no large piece in this batch
+    }
+    const WgBuildOut bo = wg_build(id, A.M, A.L, A.chunk, small, tile, rsplit > 1,
+                                   !A.amajor && blockIdx.x == 0, dst, S, s_tok);
     if (bo.tile < 0) return;  // uniform across the workgroup
     tile = bo.tile;
+    sub = bo.sub;
     pc.lora = bo.lora;
     pc.start = bo.start;
     pc.rows = bo.rows;
@@ -1004,13 +1042,20 @@ __attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_ker
     // (a large piece's record waits for the count, which places it) ----
     const int count = A.info[small ? 2 : 1];
     if (!small) {
-      tile = blocked_tile(tile, count);
+      tile = blocked_tile(tile, count * rsplit);
       if (tile < 0) return;  // uniform
+      sub = tile % rsplit;
+      tile /= rsplit;
     }
     const int32_t* rec = A.tiles + (size_t)(small ? A.large_cap + tile : tile) * SGMV_TILE_INTS;
     pc.lora = rec[0];
     pc.start = rec[1];
     pc.rows = rec[2];
+    if (!small && rsplit > 1) {  // part `sub` of the large piece: 16 of its rows
+      pc.start += SGMV_SMALL_ROWS * sub;
+      pc.rows = min(SGMV_SMALL_ROWS, pc.rows - SGMV_SMALL_ROWS * sub);
+      if (pc.rows <= 0) return;  // uniform
+    }
     if (small && tid < SGMV_SMALL_ROWS) s_tok[tid] = rec[16 + tid];
     if (table) {
       for (int i = tid; i < A.L; i += DT_THREADS) {
@@ -1022,6 +1067,9 @@ __attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_ker
     if (!small && tid < pc.rows) s_tok[tid] = A.sorted[pc.start + tid];
     __syncthreads();
   }
+  // large pieces run as 16-row parts through the small-piece path
+  const bool part = !small && rsplit > 1;
+  if (part) small = true;
   pc.r = table ? s_rank[pc.lora] : A.rank[pc.lora];
   pc.scale = table ? s_scale[pc.lora] : A.scale[pc.lora];
   const int width = (((A.v_total + P - 1) / P) + 63) & ~63;
@@ -1030,9 +1078,10 @@ __attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_ker
   pc.tile = tile;
   pc.split = p;
   pc.nsplit = P;
+  pc.xsub = part ? sub : -1;
   // a split with no columns still owes its K range to the exchange
   if (split && pc.v0 >= pc.v1 &&
-      !(MODE == MODE_FUSED && XCH && (small ? A.xch_small : A.xch_large)))
+      !(MODE == MODE_FUSED && XCH && (small && !part ? A.xch_small : A.xch_large)))
     return;
 
   const int nrk = (pc.r + 15) >> 4;
@@ -1059,14 +1108,24 @@ __attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_ker
 // Grid and dynamic LDS of a launch; the kernel arguments get the class boundary.
 inline void delta_geometry(int mode, DeltaArgs& A, int& grid, size_t& lds, bool build = false) {
   const bool split = mode != MODE_SHRINK;
-  A.grid_large = class_grid(A.large_cap, split ? A.n_split_large : 1);
+  // large slots: pieces, or their 16-row parts, rsplit slots per piece when the records are
+  // read directly and densely numbered when built in the launch (every large piece has at
+  // least 17 rows, so the parts number at most (M + 15 * large_cap) / 16)
+  int large_slots = A.large_cap * A.rsplit;
+  const int part_bound = (A.M + (SGMV_SMALL_ROWS - 1) * A.large_cap) / SGMV_SMALL_ROWS;
+  if (build && A.rsplit > 1 && part_bound < large_slots) large_slots = part_bound;
+  A.grid_large = class_grid(large_slots, split ? A.n_split_large : 1);
   grid = A.grid_large + class_grid(A.small_cap, split ? A.n_split_small : 1);
   // partial tiles of every wave (8 waves x R_pad/16 rank tiles x 1 KB); large pieces reuse
   // them for their h fragments, which fit for every rank
   lds = (size_t)DT_WAVES * (A.R_pad / 16) * 256 * sizeof(float);
   if (build && wg_build_lds_bytes(A.L) > lds) lds = wg_build_lds_bytes(A.L);  // aliases s_part
-  if (build && A.amajor) {  // small slots per adapter, then the writer
-    grid = A.grid_large + class_grid(A.L, split ? A.n_split_small : 1) + 1;
+  if (build && A.amajor) {
+    // small slots per adapter first, then the large class, then the writer: large work is
+    // rare in adapter-indexed batches, and its workgroups (which first check for it) then do
+    // not put their id loads ahead of the small pieces' in the memory queues
+    A.small_first = class_grid(A.L, split ? A.n_split_small : 1);
+    grid = A.small_first + A.grid_large + 1;
     A.grid_writer = grid - 1;
   }
 }

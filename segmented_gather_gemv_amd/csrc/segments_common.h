@@ -81,6 +81,32 @@ __device__ __forceinline__ void piece_tiles(int len, int& nl, int& ns) {
   ns = (rem > 0 && rem <= SGMV_SMALL_ROWS) ? 1 : 0;
 }
 
+constexpr int PARTS_PER_PIECE = SGMV_TILE_ROWS / SGMV_SMALL_ROWS;
+
+// Parts of SGMV_SMALL_ROWS rows in the large pieces of a segment (chunk) of len rows: four per
+// full piece, and ceil(rem / 16) for a ragged large piece.
+__device__ __forceinline__ int large_parts(int len) {
+  const int rem = len % SGMV_TILE_ROWS;
+  return PARTS_PER_PIECE * (len / SGMV_TILE_ROWS) +
+         (rem > SGMV_SMALL_ROWS ? (rem + SGMV_SMALL_ROWS - 1) / SGMV_SMALL_ROWS : 0);
+}
+
+// Large piece li (within the bucket) and part `sub` of the bucket's lp-th part. A chunk's large
+// pieces come in row order, all but a ragged last one with four parts.
+__device__ __forceinline__ void part_of(int lp, int C, int cnt, int& li, int& sub) {
+  int chunk = 0, r = lp, nlf = 0;
+  if (C > 0) {
+    int nsf;
+    piece_tiles(C, nlf, nsf);
+    const int np = (cnt + C - 1) / C;
+    const int pf = large_parts(C);
+    chunk = (pf > 0 && lp < (np - 1) * pf) ? lp / pf : np - 1;
+    r = lp - chunk * pf;
+  }
+  li = chunk * nlf + r / PARTS_PER_PIECE;
+  sub = r % PARTS_PER_PIECE;
+}
+
 // The segment entries and piece records of one bucket (adapter `lora`, `cnt` rows from sorted
 // row `start`, chunk size C), written by the bucket's own token threads (one token per
 // thread): the first token of each chunk writes that segment's start and adapter, the first
@@ -281,14 +307,15 @@ struct WgBuildLds {
   int* sbase;   // [L + 1] first small descriptor of each bucket
   int* seg0;    // [L + 1] first segment of each bucket
   int* lbase;   // [L + 1] first large descriptor of each bucket
-  int* w;       // [5 * 8] workgroup scan scratch
-  int* rec;     // [4] this workgroup's descriptor: adapter, first row, rows, segment
+  int* w;       // [6 * 8] workgroup scan scratch
+  int* rec;     // [6] this workgroup's piece or part: adapter, first row, rows, segment,
+                // descriptor, part
 };
 
 inline size_t wg_build_lds_bytes(int L) {
   const size_t nk = (size_t)L + 1;
   return align16(nk * FUSED_BUILD_WAVES) + 4 * align16(nk * sizeof(int)) +
-         align16(5 * FUSED_BUILD_WAVES * sizeof(int)) + 16;
+         align16(6 * FUSED_BUILD_WAVES * sizeof(int)) + align16(6 * sizeof(int));
 }
 
 __device__ __forceinline__ WgBuildLds wg_build_lds(unsigned char* p, int L) {
@@ -305,7 +332,7 @@ __device__ __forceinline__ WgBuildLds wg_build_lds(unsigned char* p, int L) {
   s.lbase = reinterpret_cast<int*>(p);
   p += align16(nk * sizeof(int));
   s.w = reinterpret_cast<int*>(p);
-  p += align16(5 * FUSED_BUILD_WAVES * sizeof(int));
+  p += align16(6 * FUSED_BUILD_WAVES * sizeof(int));
   s.rec = reinterpret_cast<int*>(p);
   return s;
 }
@@ -313,7 +340,8 @@ __device__ __forceinline__ WgBuildLds wg_build_lds(unsigned char* p, int L) {
 struct WgBuildOut {
   int n_large, n_small;  // 0 when an array would overflow
   int tile;               // this workgroup's descriptor, -1 if none
-  int lora, start, rows;
+  int sub;                // its 16-row part when large pieces run in parts (else 0)
+  int lora, start, rows;  // of the descriptor, or of the part
 };
 
 struct WgBuildDst {  // the builder's outputs, written by the writer workgroup only
@@ -324,10 +352,14 @@ struct WgBuildDst {  // the builder's outputs, written by the writer workgroup o
 // Call from all 512 threads; thread t passes the id of token t (any value for t >= M). For
 // descriptor `tile` of class `small` (a large piece's `tile` is its cyclic slot, dealt in
 // blocks by blocked_tile once the count is known), returns the descriptor, its adapter, first
-// sorted row and rows, and writes its token ids to s_tok. Ends without a barrier: the
-// caller's next barrier makes s_tok visible, and S may be written again only after it.
-__device__ __forceinline__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile, bool writer,
-                               const WgBuildDst& D, const WgBuildLds& S, int* s_tok) {
+// sorted row and rows, and writes its token ids to s_tok. With `parts`, a large slot stands
+// for one 16-row part of a large piece instead: the parts of the batch are numbered densely
+// (bucket by bucket, piece by piece) and dealt in blocks like pieces, and the part's
+// descriptor, part index, first row, rows and tokens are returned. Ends without a barrier:
+// the caller's next barrier makes s_tok visible, and S may be written again only after it.
+__device__ __forceinline__ WgBuildOut wg_build(int id, int M, int L, int C, bool small, int tile,
+                                               bool parts, bool writer, const WgBuildDst& D,
+                                               const WgBuildLds& S, int* s_tok) {
   constexpr int NW = FUSED_BUILD_WAVES;
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
   const int NK = L + 1;
@@ -357,7 +389,8 @@ __device__ __forceinline__ WgBuildOut wg_build(int id, int M, int L, int C, bool
   const bool first = valid && key < L && rank == 0;
   // per bucket, at its first token: tokens, segments, large and small descriptors; and the
   // bad-id count
-  int v[5] = {0, 0, 0, 0, bad ? 1 : 0};
+  // and the large pieces' 16-row parts
+  int v[6] = {0, 0, 0, 0, bad ? 1 : 0, 0};
   if (first) {
     const int np = C > 0 ? (cnt + C - 1) / C : 1;
     const int last = C > 0 ? cnt - C * (np - 1) : cnt;
@@ -368,27 +401,35 @@ __device__ __forceinline__ WgBuildOut wg_build(int id, int M, int L, int C, bool
     v[1] = np;
     v[2] = (np - 1) * nl + nl1;
     v[3] = (np - 1) * ns + ns1;
+    v[5] = C > 0 ? (np - 1) * large_parts(C) + large_parts(last) : large_parts(cnt);
   }
-  int ex[5], tot[5];
-  block_scan<5, NW, false>(v, ex, tot, S.w);
+  int ex[6], tot[6];
+  block_scan<6, NW, false>(v, ex, tot, S.w);
   const int n_lora = tot[0], n_seg = tot[1], n_large = tot[2], n_small = tot[3];
   const bool overflow = n_seg > D.seg_cap || n_large > D.large_cap || n_small > D.small_cap;
-  if (!small) tile = blocked_tile(tile, overflow ? 0 : n_large);
+  const bool by_part = parts && !small;
+  const int n_slots = overflow ? 0 : (small ? n_small : (by_part ? tot[5] : n_large));
+  if (!small) tile = blocked_tile(tile, n_slots);
   if (first) {
     S.base[key] = ex[0];
     S.sbase[key] = ex[3];
     S.seg0[key] = ex[1];
     S.lbase[key] = ex[2];
     if (!overflow) {
-      // this workgroup's descriptor, if it belongs to this bucket
-      const int first_d = small ? ex[3] : ex[2], nd = small ? v[3] : v[2];
+      // this workgroup's descriptor (or part), if it belongs to this bucket
+      const int first_d = small ? ex[3] : (by_part ? ex[5] : ex[2]);
+      const int nd = small ? v[3] : (by_part ? v[5] : v[2]);
       if (tile >= first_d && tile < first_d + nd) {
-        const PieceDesc pd = small ? small_piece_desc(tile - first_d, C, cnt, ex[0], ex[1])
-                                   : large_piece_desc(tile - first_d, C, cnt, ex[0], ex[1]);
+        int li = tile - first_d, sub = 0;
+        if (by_part) part_of(li, C, cnt, li, sub);
+        const PieceDesc pd = small ? small_piece_desc(li, C, cnt, ex[0], ex[1])
+                                   : large_piece_desc(li, C, cnt, ex[0], ex[1]);
         S.rec[0] = key;
-        S.rec[1] = pd.start;
-        S.rec[2] = pd.rows;
+        S.rec[1] = pd.start + SGMV_SMALL_ROWS * sub;
+        S.rec[2] = by_part ? min(SGMV_SMALL_ROWS, pd.rows - SGMV_SMALL_ROWS * sub) : pd.rows;
         S.rec[3] = pd.seg;
+        S.rec[4] = (small ? ex[3] : ex[2]) + li;
+        S.rec[5] = sub;
       }
     }
   }
@@ -406,8 +447,9 @@ __device__ __forceinline__ WgBuildOut wg_build(int id, int M, int L, int C, bool
   WgBuildOut out;
   out.n_large = overflow ? 0 : n_large;
   out.n_small = overflow ? 0 : n_small;
-  const bool mine = tile >= 0 && tile < (small ? out.n_small : out.n_large);
-  out.tile = mine ? tile : -1;
+  const bool mine = tile >= 0 && tile < n_slots;
+  out.tile = mine ? S.rec[4] : -1;
+  out.sub = mine ? S.rec[5] : 0;
   out.lora = mine ? S.rec[0] : 0;
   out.start = mine ? S.rec[1] : 0;
   out.rows = mine ? S.rec[2] : 0;

@@ -128,6 +128,12 @@ bool opts_ok(const sgmv_launch_opts* o) {
                 o->exchange_wait >= -1);
 }
 
+// Most column splits of a 16-row part that a large piece's partial slots hold: 8 when every
+// partial row is 32 floats (ranks up to 32), else 4.
+int part_splits_max(int R_pad) {
+  return R_pad <= 32 ? SGMV_EXCHANGE_MAX_SPLITS : SGMV_EXCHANGE_MAX_SPLITS_LARGE;
+}
+
 // K-split exchange of a fused call, per piece class: needs the workspace and a split count
 // in range (small pieces 2..8, large 2..4); by default also at least two 128-wide K steps per
 // split, so that every workgroup has work of its own.
@@ -139,7 +145,10 @@ void choose_exchange(const sgmv_segments* seg, const sgmv_launch_opts* o, DeltaA
     return v;
   };
   A.xch_small = on(A.n_split_small, SGMV_EXCHANGE_MAX_SPLITS) ? 1 : 0;
-  A.xch_large = on(A.n_split_large, SGMV_EXCHANGE_MAX_SPLITS_LARGE) ? 1 : 0;
+  A.xch_large =
+      on(A.n_split_large, A.rsplit > 1 ? part_splits_max(A.R_pad) : SGMV_EXCHANGE_MAX_SPLITS_LARGE)
+          ? 1
+          : 0;
   if (!A.xch_small && !A.xch_large) return;
   const ExchangeLayout x = exchange_layout(seg->large_cap, seg->small_cap);
   char* base = static_cast<char*>(seg->exchange);
@@ -203,12 +212,28 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
     A.v_total = 0;
   }
   fill_common(pool, seg, A);
+  A.rsplit = 1;
   if (mode == MODE_SHRINK) {
     A.n_split_large = A.n_split_small = 1;
   } else {
     const bool xch = mode == MODE_FUSED && pool->dtype == SGMV_BF16 && seg->exchange &&
                      !(opts && opts->exchange < 0);
     choose_splits(A.v_total, M, pool->L, xch, opts, A);
+    // small batches: large pieces run as 16-row parts with the small pieces' column split
+    // (few-adapter batches then spread over as many workgroups as 16-row chunks would give);
+    // with the exchange, at most the splits a large piece's partial slots hold for parts
+    if (mode == MODE_FUSED && pool->dtype == SGMV_BF16 && M <= SGMV_PART_SPLIT_MAX_M &&
+        pool->R_pad <= 32) {
+      A.rsplit = SGMV_TILE_ROWS / SGMV_SMALL_ROWS;
+      // the small pieces' split; with the exchange (where more splits cost no extra reads of
+      // x and A) up to about 128 part workgroups for a batch of one adapter (M / 16 parts)
+      int pp = A.n_split_small;
+      if (xch) {
+        if (2048 / M > pp) pp = 2048 / M;
+        if (pp > part_splits_max(pool->R_pad)) pp = part_splits_max(pool->R_pad);
+      }
+      if (!(opts && opts->n_split_large > 0)) A.n_split_large = pp;
+    }
   }
   if (mode == MODE_FUSED && pool->dtype == SGMV_BF16) choose_exchange(seg, opts, A);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -45,6 +45,15 @@ def test_library_exports_every_declared_symbol():
     assert set(sg.EXPORTED) <= exported
 
 
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define SGMV_([A-Z_0-9]+) (\d+)", text))
+    for name in ["TILE_ROWS", "SMALL_ROWS", "TILE_INTS", "MAX_RANK", "MAX_SLICES",
+                 "DEVICE_BUILDER_MAX_L", "FUSED_BUILD_MAX_M", "PART_SPLIT_MAX_M"]:
+        assert int(defs[name]) == getattr(sg, name), name
+    assert int(defs["TILE_ROWS"]) % int(defs["SMALL_ROWS"]) == 0
+
+
 def test_version_and_status_strings():
     lib = sg.library()
     assert lib.sgmv_version() >= 100

@@ -12,7 +12,7 @@ import torch
 
 import workloads
 from test_gpu_parity import (DEV, _check_control, _xch_control, check_no_adapter_rows, compare,
-                             np32, oracle_y, upload)
+                             large_counters, large_splits, np32, oracle_y, runs_parts, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +27,14 @@ def sg():
 
 def _ids_perm(M, L, seed):
     return torch.from_numpy(np.random.default_rng(seed).permutation(M) % L).to(torch.int32)
+
+
+def _ids_few(M, adapters, no_lora_frac, seed):
+    """Ids drawn from a few adapters, a fraction of the tokens without one (-1)."""
+    rng = np.random.default_rng(seed)
+    ids = rng.choice(np.asarray(adapters), size=M)
+    ids[rng.random(M) < no_lora_frac] = -1
+    return torch.from_numpy(ids.astype(np.int32))
 
 
 # name: (custom workload arguments, ids override or None)
@@ -52,6 +60,20 @@ CASES = {
     "unaligned_r16": (dict(M=90, K=1000, N=300, L=20, R=16, ranks=[7, 16]), None),
     "prefill_like_r16": (dict(M=400, K=2048, N=768, L=6, R=16, ranks=[5, 16],
                               seq_lens=[200, 17, 64, 119]), None),
+    # few adapters: large pieces as 16-row parts (one adapter; two adapters of different
+    # ranks with ragged pieces and tokens without an adapter), at and past the largest batch
+    # that runs parts
+    "one_adapter_256": (dict(M=256, K=2048, N=1024, L=64, R=16),
+                        lambda: torch.full((256,), 5, dtype=torch.int32)),
+    "two_adapters_ragged": (dict(M=250, K=1152, N=640, L=8, R=32, ranks=[8, 32]),
+                            lambda: _ids_few(250, [3, 6], 0.05, 2)),
+    "parts_1024": (dict(M=1024, K=1024, N=512, L=4, R=16), None),
+    # parts of chunked segments: a 40-row chunk is one large piece of three parts; a 100-row
+    # chunk a full piece (four parts) and a 36-row piece (three)
+    "chunked40_parts": (dict(M=400, K=1024, N=512, L=3, R=16, chunk=40), None),
+    "chunked100_parts": (dict(M=500, K=1024, N=384, L=2, R=32, chunk=100,
+                              no_lora_frac=0.05), None),
+    "whole_1025": (dict(M=1025, K=1024, N=512, L=4, R=16), None),
     # two launches: beyond the single-launch batch size, and fp32
     "two_launch_513": (dict(M=513, K=512, N=256, L=40, R=16, no_lora_frac=0.05), None),
     "two_launch_f32": (dict(M=64, K=256, N=128, L=5, R=16, dtype=torch.float32), None),
@@ -93,17 +115,18 @@ def _same_segments(a, b):
     return ha
 
 
-def _check_control_any_slot(sg, seg, calls):
+def _check_control_any_slot(sg, seg, calls, pool):
     """The single launch may index small pieces' control words by adapter instead of by
     descriptor: the large counters and, among the small ones, exactly num_small_tiles of them
     advance by 64 per call; every other word stays zero."""
     ctl = _xch_control(sg, seg)
-    nl, ns = int(seg.info[1].item()), int(seg.info[2].item())
+    ns = int(seg.info[2].item())
     lc = seg.desc.large_cap
-    assert torch.all(ctl[:nl, 0] == 64 * calls) and torch.all(ctl[nl:lc, 0] == 0)
+    want = large_counters(sg, seg, calls, runs_parts(sg, pool, seg.desc.M))
+    assert torch.equal(ctl[:lc], want), ctl[:lc, :4]
     small = ctl[lc:, 0]
     assert int((small == 64 * calls).sum()) == ns and int((small == 0).sum()) == small.numel() - ns
-    assert torch.all(ctl[:, 1:] == 0)
+    assert torch.all(ctl[lc:, 1:] == 0)
 
 
 def _both(sg, w, pool, x, y0, ids, opts):
@@ -129,27 +152,30 @@ def test_build_and_delta_match_two_calls(sg, name):
 
 @pytest.mark.parametrize("name", ["max_one_adapter", "mixed_rank", "prefill_like", "chunked",
                                   "unaligned", "mixed_rank_r16", "prefill_like_r16",
-                                  "chunked_r16", "unaligned_r16"])
+                                  "chunked_r16", "unaligned_r16", "one_adapter_256",
+                                  "two_adapters_ragged", "parts_1024", "whole_1025",
+                                  "chunked40_parts", "chunked100_parts"])
 @pytest.mark.parametrize("P", [2, 4, 8])
 def test_build_and_delta_with_exchange(sg, name, P):
     """Every piece splits its shrink over K with its partners; the single launch advances
     each piece's arrival counter by 64, as the two-call path does."""
     w = _workload(name, seed=P)
     pool, x, y0, ids = upload(w, sg)
-    opts = sg.LaunchOpts(n_split_small=P, n_split_large=min(P, 4), exchange=1)
+    PL = large_splits(sg, pool, w.M, P)
+    opts = sg.LaunchOpts(n_split_small=P, n_split_large=PL, exchange=1)
     sep, ya, one, yb = _both(sg, w, pool, x, y0, ids, opts)
     _same_segments(sep, one)
     assert torch.equal(ya, yb)
-    _check_control(sg, sep, 1)
-    _check_control_any_slot(sg, one, 1)
+    _check_control(sg, sep, 1, pool)
+    _check_control_any_slot(sg, one, 1, pool)
     # partials of late partners recomputed locally: the same bits
-    local = sg.LaunchOpts(n_split_small=P, n_split_large=min(P, 4), exchange=1, exchange_wait=-1)
+    local = sg.LaunchOpts(n_split_small=P, n_split_large=PL, exchange=1, exchange_wait=-1)
     yc = _delta(sg, w, x, y0, lambda y, o: sg.sgmv_lora_delta_ids(ids, x, pool, one, y, opts=o),
                 local)
     assert torch.equal(ya, yc)
     # the single launch leaves the counters running; two launches rebuild, which clears them
     single = pool.desc.R_pad == 16 and 1 <= w.M <= 512 and w.dtype == torch.bfloat16
-    _check_control_any_slot(sg, one, 2 if single else 1)
+    _check_control_any_slot(sg, one, 2 if single else 1, pool)
     compare(np32(yb), oracle_y(w, np32(w.y0)), w.dtype, what=f"{name} P={P}")
 
 
@@ -172,15 +198,16 @@ def test_single_launch_rank16_exchange(sg, name, P):
     """Bit-exact against two launches, also with every partner's partial computed locally."""
     w = workloads.custom(name=name, seed=20 + P, **ROLE_CASES[name])
     pool, x, y0, ids = upload(w, sg)
-    opts = sg.LaunchOpts(n_split_small=P, n_split_large=min(P, 4), exchange=1)
+    PL = large_splits(sg, pool, w.M, P)
+    opts = sg.LaunchOpts(n_split_small=P, n_split_large=PL, exchange=1)
     sep, ya, one, yb = _both(sg, w, pool, x, y0, ids, opts)
     _same_segments(sep, one)
     assert torch.equal(ya, yb)
-    local = sg.LaunchOpts(n_split_small=P, n_split_large=min(P, 4), exchange=1, exchange_wait=-1)
+    local = sg.LaunchOpts(n_split_small=P, n_split_large=PL, exchange=1, exchange_wait=-1)
     yc = _delta(sg, w, x, y0, lambda y, o: sg.sgmv_lora_delta_ids(ids, x, pool, one, y, opts=o),
                 local)
     assert torch.equal(ya, yc)
-    _check_control_any_slot(sg, one, 2)
+    _check_control_any_slot(sg, one, 2, pool)
     compare(np32(yb), oracle_y(w, np32(w.y0)), w.dtype, what=f"{name} P={P}")
     check_no_adapter_rows(w, yb, w.y0)
 

@@ -446,6 +446,9 @@ XCH_CASES = {
                         seq_lens=[200, 17, 64, 119]),
     "xch_prefill_r16": dict(M=300, K=1024, N=512, L=3, R=16, seq_lens=[100, 150, 50]),
     "xch_prefill_odd": dict(M=150, K=700, N=200, L=4, R=48, seq_lens=[33, 90, 27]),
+    # past the part-split batch size: large pieces run whole
+    "xch_prefill_whole": dict(M=1100, K=1024, N=384, L=5, R=32, ranks=[8, 32],
+                              seq_lens=[500, 17, 300, 83, 200]),
 }
 
 
@@ -456,15 +459,40 @@ def _xch_control(sg, seg):
     return seg.exchange[:n * 4].view(torch.int32).view(-1, 16).cpu()
 
 
-def _check_control(sg, seg, calls):
-    """Every exchange call advances the counter of every piece by exactly 64."""
-    ctl = _xch_control(sg, seg)
-    nl, ns = int(seg.info[1].item()), int(seg.info[2].item())
+def runs_parts(sg, pool, M):
+    """Fused bf16 calls run large pieces as 16-row parts on batches up to PART_SPLIT_MAX_M
+    tokens at pool ranks up to 32."""
+    return M <= sg.PART_SPLIT_MAX_M and pool.desc.R_pad <= 32
+
+
+def large_counters(sg, seg, calls, parts):
+    """Expected control words of the large records after `calls` exchange calls: word 0 of
+    each large piece, or, when large pieces run as 16-row parts, word j of part j (parts
+    0 .. ceil(rows / 16) - 1); every other word zero."""
     lc = seg.desc.large_cap
-    assert torch.all(ctl[:nl, 0] == 64 * calls), ctl[:nl, 0]
-    assert torch.all(ctl[nl:lc, 0] == 0)
+    want = torch.zeros(lc, 16, dtype=torch.int32)
+    nl = int(seg.info[1].item())
+    rows = seg.tiles.view(-1, sg.TILE_INTS)[:nl, 2].cpu()
+    for i in range(nl):
+        want[i, :-(-int(rows[i]) // sg.SMALL_ROWS) if parts else 1] = 64 * calls
+    return want
+
+
+def large_splits(sg, pool, M, P):
+    """The most column splits up to P that large pieces take with the exchange: 16-row parts
+    hold 8 at ranks up to 32; whole pieces, and parts at larger ranks, 4."""
+    return min(P, 8 if runs_parts(sg, pool, M) else 4)
+
+
+def _check_control(sg, seg, calls, pool):
+    """Every exchange call advances the counter of every piece (or part) by exactly 64."""
+    ctl = _xch_control(sg, seg)
+    ns = int(seg.info[2].item())
+    lc = seg.desc.large_cap
+    want = large_counters(sg, seg, calls, runs_parts(sg, pool, seg.desc.M))
+    assert torch.equal(ctl[:lc], want), ctl[:lc, :4]
     assert torch.all(ctl[lc:lc + ns, 0] == 64 * calls), ctl[lc:lc + ns, 0]
-    assert torch.all(ctl[lc + ns:, 0] == 0) and torch.all(ctl[:, 1:] == 0)
+    assert torch.all(ctl[lc + ns:, 0] == 0) and torch.all(ctl[lc:, 1:] == 0)
 
 
 def _fused_opts(sg, w, seg, pool, x, y0, **kw):
@@ -482,16 +510,16 @@ def test_exchange_parity_and_determinism(sg, name, P):
     seg = sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True)
     assert seg.exchange is not None
     torch.cuda.synchronize()
-    _check_control(sg, seg, 0)
+    _check_control(sg, seg, 0, pool)
     ref = oracle_y(w, np32(w.y0))
-    PL = min(P, 4)
+    PL = large_splits(sg, pool, w.M, P)
     off = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, n_split_large=PL, exchange=-1)
-    _check_control(sg, seg, 0)
+    _check_control(sg, seg, 0, pool)
     on = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, n_split_large=PL, exchange=1)
     compare(np32(off), ref, w.dtype, what=f"{name} P={P} no exchange")
     compare(np32(on), ref, w.dtype, what=f"{name} P={P} exchange")
     check_no_adapter_rows(w, on, w.y0)
-    _check_control(sg, seg, 1)
+    _check_control(sg, seg, 1, pool)
     # the sum is taken in split order: the same bits on every call, and when the partials
     # of late partners are recomputed locally (no wait at all)
     again = _fused_opts(sg, w, seg, pool, x, y0, n_split_small=P, n_split_large=PL, exchange=1)
@@ -499,11 +527,11 @@ def test_exchange_parity_and_determinism(sg, name, P):
                         exchange_wait=-1)
     assert torch.equal(on, again)
     assert torch.equal(on, local)
-    _check_control(sg, seg, 3)
+    _check_control(sg, seg, 3, pool)
     # a rebuild clears the control words
     sg.sgmv_build_segments(ids, w.L, w.chunk_size, on_device=True, out=seg)
     torch.cuda.synchronize()
-    _check_control(sg, seg, 0)
+    _check_control(sg, seg, 0, pool)
 
 
 def test_exchange_workspace_optional(sg):
