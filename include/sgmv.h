@@ -242,6 +242,20 @@ sgmv_status sgmv_build_segments_cached(const int32_t* lora_indices, int32_t M, i
  * Never fails. */
 int32_t sgmv_chunk_size_for_batch(int32_t M, int32_t n_adapters);
 
+/* ------------------------------------------------------------------------------------
+ * sgmv_exchange_placement: checks, on the current device, the workgroup placement that the
+ * K-split exchange of the fused call relies on (the exchange workspace described at
+ * sgmv_segments): the workgroups that share a piece have equal launch indices modulo 8 and
+ * must run on one XCD, whose L2 is where their partial sums meet. It launches a grid of
+ * 2048 workgroups that read their XCD id (hardware register XCC_ID) on `stream`, waits for
+ * it, and returns SGMV_OK when every workgroup index b ran on the XCD of index b mod 8 (true
+ * when the dispatcher deals workgroups round-robin over 1, 2, 4 or 8 XCDs), with the number
+ * of XCDs seen in *n_xcd (may be NULL). SGMV_EUNSUPPORTED: the placement does not hold;
+ * callers must then pass segments without an exchange workspace. Allocates a small device
+ * buffer; not for use under graph capture. Errors: EHIP.
+ * ------------------------------------------------------------------------------------ */
+sgmv_status sgmv_exchange_placement(int32_t* n_xcd, void* stream);
+
 /* One output slice: pool columns [n_begin, n_begin + n_len) land in columns [0, n_len) of
  * y, a device array [M][ldy] of the pool dtype (e.g. q, k and v of a fused projection). */
 typedef struct {

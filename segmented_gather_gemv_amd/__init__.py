@@ -46,6 +46,7 @@ EXPORTED = [
     "sgmv_lora_delta_ids_ex", "sgmv_build_segments_cached", "sgmv_build_segments_cached_ex",
     "sgmv_pool_pack_ex", "sgmv_merge_adapter", "sgmv_merge_adapter_ex", "sgmv_status_string",
     "sgmv_version", "sgmv_chunk_size_for_batch", "sgmv_lora_delta_ids_noalloc",
+    "sgmv_exchange_placement",
 ]
 
 
@@ -146,6 +147,8 @@ def _load():
     lib.sgmv_version.restype = ctypes.c_int32
     lib.sgmv_chunk_size_for_batch.argtypes = [i32, i32]
     lib.sgmv_chunk_size_for_batch.restype = ctypes.c_int32
+    lib.sgmv_exchange_placement.argtypes = [P(i32), vp]
+    lib.sgmv_exchange_placement.restype = ctypes.c_int
     return lib
 
 
@@ -307,9 +310,30 @@ class Segments:
         }
 
 
+_PLACEMENT = {}
+
+
+def sgmv_exchange_placement(device: Union[str, torch.device] = "cuda") -> Tuple[bool, int]:
+    """Whether the fused call's K-split exchange may be used on `device` (the workgroups of
+    a piece run on one XCD), and the number of XCDs seen; checked once per device."""
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    if key not in _PLACEMENT:
+        n = ctypes.c_int32(0)
+        with torch.cuda.device(key):
+            st = _lib.sgmv_exchange_placement(ctypes.byref(n),
+                                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st not in (SGMV_OK, SGMV_EUNSUPPORTED):
+            _check(st, "sgmv_exchange_placement")
+        _PLACEMENT[key] = (st == SGMV_OK, int(n.value))
+    return _PLACEMENT[key]
+
+
 def _exchange_buffer(desc: _Segments, dev: torch.device) -> Optional[torch.Tensor]:
     if dev.type != "cuda" or desc.exchange_bytes <= 0:
         return None
+    if not sgmv_exchange_placement(dev)[0]:
+        return None  # partners of a piece would not share an L2: fused calls run without it
     buf = torch.zeros(int(desc.exchange_bytes) + 256, dtype=torch.uint8, device=dev)
     off = (-buf.data_ptr()) % 256  # the library wants 256-byte alignment
     return buf[off:off + int(desc.exchange_bytes)]
@@ -516,5 +540,5 @@ __all__ = [
     "sgmv_pool_init", "sgmv_pool_pack", "sgmv_segments_alloc", "sgmv_build_segments",
     "sgmv_shrink", "sgmv_expand", "sgmv_lora_delta", "sgmv_lora_delta_ids",
     "sgmv_lora_delta_ids_noalloc", "sgmv_segments_cache_alloc", "sgmv_build_segments_cached", "sgmv_merge_adapter",
-    "sgmv_chunk_size_for_batch",
+    "sgmv_chunk_size_for_batch", "sgmv_exchange_placement",
 ]

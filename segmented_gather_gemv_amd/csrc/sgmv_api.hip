@@ -295,6 +295,12 @@ sgmv_status build_segments(const int32_t* lora_indices, int32_t M, int32_t L, in
                                           static_cast<hipStream_t>(stream)));
 }
 
+// The XCD (hardware register XCC_ID) of every workgroup of the grid, from its first lane.
+__global__ void xcd_probe_kernel(int32_t* out) {
+  const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // HW_REG_XCC_ID, bits 0..3
+  if (threadIdx.x == 0) out[blockIdx.x] = xcc;
+}
+
 }  // namespace
 }  // namespace sgmv
 
@@ -315,6 +321,28 @@ const char* sgmv_status_string(sgmv_status s) {
 }
 
 int32_t sgmv_version(void) { return 100; }
+
+sgmv_status sgmv_exchange_placement(int32_t* n_xcd, void* stream) {
+  constexpr int G = 2048;
+  int32_t* d = nullptr;
+  if (hipMalloc(&d, G * sizeof(int32_t)) != hipSuccess) return SGMV_EHIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  xcd_probe_kernel<<<G, WAVE, 0, s>>>(d);
+  int32_t h[G];
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(h, d, sizeof(h), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (hipFree(d) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
+  if (e != hipSuccess) return SGMV_EHIP;
+  int32_t most = 0;
+  bool ok = true;
+  for (int b = 0; b < G; ++b) {
+    most = h[b] > most ? h[b] : most;
+    ok = ok && h[b] == h[b % 8];
+  }
+  if (n_xcd) *n_xcd = most + 1;
+  return ok ? SGMV_OK : SGMV_EUNSUPPORTED;
+}
 
 int32_t sgmv_chunk_size_for_batch(int32_t M, int32_t n_adapters) {
   if (M <= 0) return 0;

@@ -76,3 +76,13 @@ def test_exchange_soak_prefill(sg):
     n = _soak(lambda y: sg.sgmv_lora_delta(x, pool, seg, y), y0, ref, 200, batch=8,
               what="prefill")
     assert n == 200
+
+
+def test_exchange_placement(sg):
+    """The exchange's partners (equal launch index modulo 8) run on one XCD: every workgroup
+    b of a 2048-workgroup grid reads XCD id equal to that of workgroup b mod 8."""
+    ok, n_xcd = sg.sgmv_exchange_placement("cuda")
+    assert ok, f"workgroups b and b mod 8 ran on different XCDs ({n_xcd} XCDs seen)"
+    assert n_xcd in (1, 2, 4, 8)
+    seg = sg.sgmv_segments_alloc(256, 64, 0, "cuda")
+    assert seg.exchange is not None
