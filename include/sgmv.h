@@ -246,7 +246,7 @@ int32_t sgmv_chunk_size_for_batch(int32_t M, int32_t n_adapters);
  * sgmv_exchange_placement: checks, on the current device, the workgroup placement that the
  * K-split exchange of the fused call relies on (the exchange workspace described at
  * sgmv_segments): the workgroups that share a piece have equal launch indices modulo 8 and
- * must run on one XCD, whose L2 is where their partial sums meet. It launches a grid of
+ * must run on one XCD, whose L2 performs their arrival counter's atomics. It launches a grid of
  * 2048 workgroups that read their XCD id (hardware register XCC_ID) on `stream`, waits for
  * it, and returns SGMV_OK when every workgroup index b ran on the XCD of index b mod 8 (true
  * when the dispatcher deals workgroups round-robin over 1, 2, 4 or 8 XCDs), with the number

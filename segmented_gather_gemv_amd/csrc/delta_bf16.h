@@ -1127,6 +1127,10 @@ inline void delta_geometry(int mode, DeltaArgs& A, int& grid, size_t& lds, bool 
     A.small_first = class_grid(A.L, split ? A.n_split_small : 1);
     grid = A.small_first + A.grid_large + 1;
     A.grid_writer = grid - 1;
+  } else if (A.rsplit > 1) {
+    // parts of large pieces (four slots per piece, most of them empty in decode-like batches)
+    // after the small pieces, for the same reason
+    A.small_first = class_grid(A.small_cap, split ? A.n_split_small : 1);
   }
 }
 
