@@ -44,7 +44,11 @@ constexpr int DT_THREADS = 512;
 constexpr int DT_WAVES = DT_THREADS / WAVE;
 constexpr int KSTEP = 128;
 constexpr int HS = 68;                // LDS row stride of the h tile (64 ranks + 4 pad floats)
-constexpr int RANK_TABLE_MAX = 2048;  // pools up to this size get rank/scale staged in LDS
+constexpr int RANK_TABLE_MAX = 1024;  // pools up to this size get rank/scale staged in LDS
+// LDS-staged large shrink: K chunks of 64, each a 64-row x tile and a 64-rank A tile (8 KB
+// each) brought in by direct global-to-LDS loads, STAGES of them in flight
+constexpr int STAGE_BYTES = 16384;
+constexpr int STAGES = 3;
 
 struct Piece {
   int lora, start, rows, r;
@@ -533,15 +537,127 @@ __device__ void shrink_range(const DeltaArgs& A, const Piece& pc, const ShrinkGe
   store_wave_partial<NRK>(s_part, w, c, g, acc);
 }
 
+// Shrink of a large piece over K steps [k0, k1) of KSTEP, staged through LDS: the range is
+// cut into 64-wide chunks; for each, 16 direct global-to-LDS loads of 1 KB (2 per wave:
+// waves 0-3 the 64 x rows, waves 4-7 the 64 A rank rows, 128 bytes of each row) fill one of
+// STAGES buffers, STAGES - 1 chunks ahead of the one being multiplied, so loads stay in flight
+// without registers. Wave w owns row tile w % 4 and rank tiles 2 (w / 4) .. + 1 over the
+// whole range (8 accumulator registers), reading its MFMA operands from LDS; the partial
+// goes straight to s_h (times mult). Within a row of 128 bytes the eight 16-byte chunks are
+// stored in the order q ^ ((row / 2) % 8), which makes the operand reads of 16 lanes (16
+// rows) fall in distinct LDS banks. Rows past the piece read its first token's row, ranks
+// past the adapter's rank its first rank row, k past K the row's first bytes; all of these
+// are zeroed when read. The same steps in the same order serve a piece's own partial and the
+// local recomputation of a partner's. Needs STAGES * STAGE_BYTES of s_part.
+// This wave's two 1 KB loads of one chunk (k0: the chunk's first K index) into buf.
+__device__ __forceinline__ void stage_chunk(const uint16_t* const (&src)[2], const int (&kq)[2],
+                                            int k0, int K, unsigned char* buf, int w) {
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int k = k0 + kq[i];
+    __builtin_amdgcn_global_load_lds(src[i] + (k < K ? k : 0),
+                                     (lds_void*)(buf + (2 * w + i) * 1024), 16, 0, 0);
+  }
+}
+
+template <int NRK>
+__device__ __forceinline__ void large_shrink_staged(const DeltaArgs& A, const Piece& pc, int nrt,
+                                    const int* s_tok, int k0, int k1, float mult,
+                                    float* s_part, float* s_h) {
+  const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
+  const int c = lane & 15, g = lane >> 4;
+  unsigned char* stage0 = reinterpret_cast<unsigned char*>(s_part);
+  // this lane's two loads per chunk: slot 2w + i covers tile rows 8 (2w + i) .. + 7 (x for
+  // slots 0..7, A for 8..15), lane l takes row 8 slot + l / 8 and 16-byte chunk
+  // (l % 8) ^ ((row / 2) % 8) of the row's 128 bytes
+  const uint16_t* src[2];
+  int kq[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int slot = 2 * w + i;
+    const int row = 8 * (slot & 7) + (lane >> 3);
+    kq[i] = 8 * ((lane & 7) ^ ((row >> 1) & 7));
+    if (slot < 8) {
+      const int tok = s_tok[row < pc.rows ? row : 0];
+      src[i] = static_cast<const uint16_t*>(A.x) + (size_t)tok * (size_t)A.ldx;
+    } else {
+      const int rk = row < pc.r ? row : 0;  // past the adapter's rank: a row already read
+      src[i] = static_cast<const uint16_t*>(A.a) + ((size_t)pc.lora * A.R_pad + rk) * A.K_pad;
+    }
+  }
+  const int nck = 2 * (k1 - k0);  // 64-wide chunks
+  const int kbase = k0 * KSTEP, K = A.K;
+  const int rt = w & 3, rp = w >> 2;
+  const bool active = rt < nrt;
+  const int row = rt * 16 + c;
+  const bool vrow = row < pc.rows;
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ck = 0; ck < STAGES - 1; ++ck)
+    if (ck < nck) stage_chunk(src, kq, kbase + 64 * ck, K, stage0 + (ck % STAGES) * STAGE_BYTES, w);
+  for (int ck = 0; ck < nck; ++ck) {
+    // this wave's loads of chunk ck are in once at most the later chunk's two are outstanding
+    static_assert(STAGES == 3, "the wait counts below assume one chunk in flight behind");
+    if (ck + 1 < nck) __builtin_amdgcn_s_waitcnt(0x0f70 | 2);  // vmcnt(2)
+    else __builtin_amdgcn_s_waitcnt(0x0f70);                  // vmcnt(0)
+    __syncthreads();  // every wave's loads of chunk ck are in; chunk ck - 1 is consumed
+    if (ck + STAGES - 1 < nck) {
+      const int cn = ck + STAGES - 1;
+      stage_chunk(src, kq, kbase + 64 * cn, K, stage0 + (cn % STAGES) * STAGE_BYTES, w);
+    }
+    if (active) {
+      const unsigned char* buf = stage0 + (ck % STAGES) * STAGE_BYTES;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int q = 4 * st + g;
+        const int k = kbase + 64 * ck + 8 * q;
+        const int xo = row * 128 + ((q ^ ((row >> 1) & 7)) << 4);
+        u32x4_t xv = *reinterpret_cast<const u32x4_t*>(buf + xo);
+        if (!vrow || k >= K) xv = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int j = (2 * rp + t) * 16 + c;  // rank row
+          if (2 * rp + t < NRK) {  // compile-time bound per wave pair
+            const int ao = 8192 + j * 128 + ((q ^ ((j >> 1) & 7)) << 4);
+            u32x4_t av = *reinterpret_cast<const u32x4_t*>(buf + ao);
+            if (j >= pc.r || k >= K) av = u32x4_t{0u, 0u, 0u, 0u};
+            acc[t] = mfma_16x16x32_bf16(as_bf16x8(xv), as_bf16x8(av), acc[t]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();  // the last chunk is consumed: s_part is free again
+  // D layout: lane (c, g) holds rows 4g..4g+3 of rank column c
+  constexpr int NCOL = (NRK + 1) / 2 * 32;
+  if (active) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int col = (2 * rp + t) * 16 + c;
+      if (col < NCOL) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_h[(rt * 16 + 4 * g + e) * HS + col] = acc[t][e] * mult;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // Shrink of a large piece over K steps [k0, k1) of KSTEP: the 8 waves split the range into
 // 8 slices of 32-wide substeps, and each wave accumulates every row tile x rank tile of the
 // piece over its slice, so x and A are each read once per workgroup. The wave partials are
 // then summed in wave order, one row tile at a time, into s_h rows (times mult; zero at ranks
 // >= r). The same steps in the same order serve a piece's own partial and the local
 // recomputation of a partner's, so both are bit-identical.
-template <int NRK, bool ALIGNED>
-__device__ void large_shrink(const DeltaArgs& A, const Piece& pc, int nrt, const int* s_tok,
+template <int NRK, bool ALIGNED, bool STAGED = false>
+__device__ __forceinline__ void large_shrink(const DeltaArgs& A, const Piece& pc, int nrt, const int* s_tok,
                              int k0, int k1, float mult, float* s_part, float* s_h) {
+  if constexpr (ALIGNED && STAGED) {  // fused launches give s_part STAGES * STAGE_BYTES when
+                                      // whole large pieces can occur
+    large_shrink_staged<NRK>(A, pc, nrt, s_tok, k0, k1, mult, s_part, s_h);
+    return;
+  }
   constexpr int NCOL = (NRK + 1) / 2 * 32;  // whole 32-rank expand tiles
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
   const int c = lane & 15, g = lane >> 4;
@@ -678,7 +794,7 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
       if (q == p) continue;
       __syncthreads();  // the previous round's readers of s_part / s_h are done
       if constexpr (LARGE)
-        large_shrink<NRK, ALIGNED>(A, pc, G.nrt, s_tok, q * nch / P, (q + 1) * nch / P, 1.f,
+        large_shrink<NRK, ALIGNED, true>(A, pc, G.nrt, s_tok, q * nch / P, (q + 1) * nch / P, 1.f,
                                    s_part, s_h);
       else
         shrink_range<NRK, ALIGNED>(A, pc, G, s_tok, q * nch / P, (q + 1) * nch / P, s_part);
@@ -856,7 +972,7 @@ __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc,
     // K steps of this workgroup: all of K, or its split's range
     const int k0 = xch ? pc.split * nch / pc.nsplit : 0;
     const int k1 = xch ? (pc.split + 1) * nch / pc.nsplit : nch;
-    large_shrink<NRK, ALIGNED>(A, pc, nrt, s_tok, k0, k1,
+    large_shrink<NRK, ALIGNED, MODE == MODE_FUSED>(A, pc, nrt, s_tok, k0, k1,
                                (MODE == MODE_FUSED && !xch) ? pc.scale : 1.f, s_part, s_h);
     if (xch) exchange_h<NRK, ALIGNED, true>(A, pc, G, s_tok, nch, s_part, s_h, s_mask);
   }
@@ -1120,6 +1236,11 @@ inline void delta_geometry(int mode, DeltaArgs& A, int& grid, size_t& lds, bool 
   // them for their h fragments, which fit for every rank
   lds = (size_t)DT_WAVES * (A.R_pad / 16) * 256 * sizeof(float);
   if (build && wg_build_lds_bytes(A.L) > lds) lds = wg_build_lds_bytes(A.L);  // aliases s_part
+  // whole large pieces (no parts) of fused calls stage their shrink through s_part in the
+  // aligned kernels
+  if (mode == MODE_FUSED && A.rsplit == 1 && A.large_cap > 0 &&
+      lds < (size_t)STAGES * STAGE_BYTES)
+    lds = (size_t)STAGES * STAGE_BYTES;
   if (build && A.amajor) {
     // small slots per adapter first, then the large class, then the writer: large work is
     // rare in adapter-indexed batches, and its workgroups (which first check for it) then do

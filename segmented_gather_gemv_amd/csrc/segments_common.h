@@ -267,7 +267,7 @@ __device__ __forceinline__ uint64_t wave_adapter_mask(const int32_t* ids, int M,
 // Returns the piece's rows (0: no small piece; uniform) and writes its tokens to s_tok,
 // visible after the caller's next barrier.
 template <int NW>
-__device__ int adapter_small_piece(uint64_t m, int* s_wc, int* s_tok) {
+__device__ __forceinline__ int adapter_small_piece(uint64_t m, int* s_wc, int* s_tok) {
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
   const bool mine = (m >> lane) & 1u;
   if (lane == 0) s_wc[w] = __popcll(m);

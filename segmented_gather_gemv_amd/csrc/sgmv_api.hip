@@ -252,6 +252,8 @@ sgmv_status run_delta(int mode, const void* x, int64_t ldx, const float* h_in, f
     // every adapter at the full rank of one tile: a small piece's A and B loads need
     // neither its rank nor its tokens and are issued first
     A.spec = (A.amajor && pool->R_pad == 16 && pool->rank_min == pool->R_pad) ? 1 : 0;
+    // the in-launch build's kernels run large pieces only as 16-row parts
+    if (A.rsplit != SGMV_TILE_ROWS / SGMV_SMALL_ROWS) return SGMV_EUNSUPPORTED;
     return hip_status(launch_delta_bf16_build(aligned, A, ev, s));
   }
   if (pool->dtype == SGMV_BF16) return hip_status(launch_delta_bf16(mode, aligned, A, ev, s));
