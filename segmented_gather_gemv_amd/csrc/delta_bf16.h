@@ -455,6 +455,16 @@ __device__ __forceinline__ void wait_stores() {
   __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes are complete
+// before it arrives, while its global loads (direct-to-LDS ones included) stay in flight.
+// __syncthreads' workgroup fence would also wait for all of those, which takes away the
+// overlap of the staged shrink below, which orders its direct-to-LDS loads with explicit
+// vmcnt waits instead. The memory clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // How the 8 waves of a workgroup share a piece's shrink: wave w takes row tile w % ntp and
 // K slice w / ntp (ks slices). Small pieces: one row tile, 8 K slices; large pieces: 2 row
 // tiles x 4 slices or 4 row tiles (3 or 4 used) x 2 slices.
@@ -601,7 +611,7 @@ __device__ __forceinline__ void large_shrink_staged(const DeltaArgs& A, const Pi
     static_assert(STAGES == 3, "the wait counts below assume one chunk in flight behind");
     if (ck + 1 < nck) __builtin_amdgcn_s_waitcnt(0x0f70 | 2);  // vmcnt(2)
     else __builtin_amdgcn_s_waitcnt(0x0f70);                  // vmcnt(0)
-    __syncthreads();  // every wave's loads of chunk ck are in; chunk ck - 1 is consumed
+    lds_barrier();  // every wave's loads of chunk ck are in; chunk ck - 1 is consumed
     if (ck + STAGES - 1 < nck) {
       const int cn = ck + STAGES - 1;
       stage_chunk(src, kq, kbase + 64 * cn, K, stage0 + (cn % STAGES) * STAGE_BYTES, w);
