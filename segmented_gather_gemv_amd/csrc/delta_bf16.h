@@ -551,13 +551,14 @@ __device__ void shrink_range(const DeltaArgs& A, const Piece& pc, const ShrinkGe
 // cut into 64-wide chunks; for each, 16 direct global-to-LDS loads of 1 KB (2 per wave:
 // waves 0-3 the 64 x rows, waves 4-7 the 64 A rank rows, 128 bytes of each row) fill one of
 // STAGES buffers, STAGES - 1 chunks ahead of the one being multiplied, so loads stay in flight
-// without registers. Wave w owns row tile w % 4 and rank tiles 2 (w / 4) .. + 1 over the
-// whole range (8 accumulator registers), reading its MFMA operands from LDS; the partial
-// goes straight to s_h (times mult). Within a row of 128 bytes the eight 16-byte chunks are
-// stored in the order q ^ ((row / 2) % 8), which makes the operand reads of 16 lanes (16
-// rows) fall in distinct LDS banks. Rows past the piece read its first token's row, ranks
-// past the adapter's rank its first rank row, k past K the row's first bytes; all of these
-// are zeroed when read. The same steps in the same order serve a piece's own partial and the
+// without registers. Wave w owns row tiles 2 (w % 2) .. + 1 and rank tiles 2 ((w / 2) % 2)
+// .. + 1 over the 32-wide half w / 4 of every chunk (16 accumulator registers), reading its
+// MFMA operands from LDS (each wave reads 4 KB of a 16 KB chunk); the two halves' partials
+// are added once at the end (half 0 + half 1) and go to s_h (times mult). Within a row of
+// 128 bytes the eight 16-byte chunks are stored in the order q ^ ((row / 2) % 8), which makes
+// the operand reads of 16 lanes (16 rows) fall in distinct LDS banks. Rows past the piece
+// read its first token's row, ranks past the adapter's rank its first rank row, k past K the
+// row's first bytes; all of these are zeroed when read. The same steps in the same order serve a piece's own partial and the
 // local recomputation of a partner's. Needs STAGES * STAGE_BYTES of s_part.
 // This wave's two 1 KB loads of one chunk (k0: the chunk's first K index) into buf.
 __device__ __forceinline__ void stage_chunk(const uint16_t* const (&src)[2], const int (&kq)[2],
@@ -598,11 +599,22 @@ __device__ __forceinline__ void large_shrink_staged(const DeltaArgs& A, const Pi
   }
   const int nck = 2 * (k1 - k0);  // 64-wide chunks
   const int kbase = k0 * KSTEP, K = A.K;
-  const int rt = w & 3, rp = w >> 2;
-  const bool active = rt < nrt;
-  const int row = rt * 16 + c;
-  const bool vrow = row < pc.rows;
-  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  // this wave's MFMA work: row tiles 2 tp, 2 tp + 1, rank tiles 2 kp, 2 kp + 1, the 32-wide
+  // half ks of every chunk (wave-uniform, from the first lane)
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int tp = wu & 1, kp = (wu >> 1) & 1, ks = wu >> 2;
+  const int q = 4 * ks + g;  // this lane's 16-byte chunk of a 128-byte row
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t mrow[2], mrank[2];  // operand masks: rows past the piece, ranks past the adapter's
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    mrow[i] = (2 * tp + i) * 16 + c < pc.rows ? 0xffffffffu : 0u;
+    mrank[i] = (2 * kp + i) * 16 + c < pc.r ? 0xffffffffu : 0u;
+  }
 #pragma unroll
   for (int ck = 0; ck < STAGES - 1; ++ck)
     if (ck < nck) stage_chunk(src, kq, kbase + 64 * ck, K, stage0 + (ck % STAGES) * STAGE_BYTES, w);
@@ -616,38 +628,59 @@ __device__ __forceinline__ void large_shrink_staged(const DeltaArgs& A, const Pi
       const int cn = ck + STAGES - 1;
       stage_chunk(src, kq, kbase + 64 * cn, K, stage0 + (cn % STAGES) * STAGE_BYTES, w);
     }
-    if (active) {
-      const unsigned char* buf = stage0 + (ck % STAGES) * STAGE_BYTES;
+    // every operand read first, masked by AND (no branches between the reads and the MFMAs)
+    const unsigned char* buf = stage0 + (ck % STAGES) * STAGE_BYTES;
+    const uint32_t kin = kbase + 64 * ck + 8 * q < K ? 0xffffffffu : 0u;
+    u32x4_t xv[2], av[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int q = 4 * st + g;
-        const int k = kbase + 64 * ck + 8 * q;
-        const int xo = row * 128 + ((q ^ ((row >> 1) & 7)) << 4);
-        u32x4_t xv = *reinterpret_cast<const u32x4_t*>(buf + xo);
-        if (!vrow || k >= K) xv = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int j = (2 * rp + t) * 16 + c;  // rank row
-          if (2 * rp + t < NRK) {  // compile-time bound per wave pair
-            const int ao = 8192 + j * 128 + ((q ^ ((j >> 1) & 7)) << 4);
-            u32x4_t av = *reinterpret_cast<const u32x4_t*>(buf + ao);
-            if (j >= pc.r || k >= K) av = u32x4_t{0u, 0u, 0u, 0u};
-            acc[t] = mfma_16x16x32_bf16(as_bf16x8(xv), as_bf16x8(av), acc[t]);
-          }
-        }
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int row = (2 * tp + i) * 16 + c;
+      const int j = (2 * kp + i) * 16 + c;  // rank row
+      xv[i] = *reinterpret_cast<const u32x4_t*>(buf + row * 128 + ((q ^ ((row >> 1) & 7)) << 4));
+      av[i] = *reinterpret_cast<const u32x4_t*>(buf + 8192 + j * 128 +
+                                                ((q ^ ((j >> 1) & 7)) << 4));
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[i][e] &= mrow[i] & kin;
+        av[i][e] &= mrank[i] & kin;
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        if (2 * tp + i < nrt && (NRK == 4 || 2 * kp + t < NRK))  // tiles with work
+          acc[i][t] = mfma_16x16x32_bf16(as_bf16x8(xv[i]), as_bf16x8(av[t]), acc[i][t]);
   }
   __syncthreads();  // the last chunk is consumed: s_part is free again
-  // D layout: lane (c, g) holds rows 4g..4g+3 of rank column c
+  // the two halves' partials summed (half 0 + half 1) into s_h, times mult; D layout: lane
+  // (c, g) holds rows 4g..4g+3 of rank column c
   constexpr int NCOL = (NRK + 1) / 2 * 32;
-  if (active) {
+  float* red = s_part + (size_t)(wu & 3) * 1024;  // [tile i, t][e][lane] of wave w % 4
+  if (ks == 1) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int col = (2 * rp + t) * 16 + c;
-      if (col < NCOL) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_h[(rt * 16 + 4 * g + e) * HS + col] = acc[t][e] * mult;
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[((2 * i + t) * 4 + e) * WAVE + lane] = acc[i][t][e];
+  }
+  __syncthreads();
+  if (ks == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (2 * tp + i >= nrt) continue;  // wave-uniform
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int col = (2 * kp + t) * 16 + c;
+        if (col < NCOL) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s_h[((2 * tp + i) * 16 + 4 * g + e) * HS + col] =
+                (acc[i][t][e] + red[((2 * i + t) * 4 + e) * WAVE + lane]) * mult;
+        }
       }
     }
   }
