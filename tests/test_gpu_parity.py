@@ -446,6 +446,11 @@ XCH_CASES = {
                         seq_lens=[200, 17, 64, 119]),
     "xch_prefill_r16": dict(M=300, K=1024, N=512, L=3, R=16, seq_lens=[100, 150, 50]),
     "xch_prefill_odd": dict(M=150, K=700, N=200, L=4, R=48, seq_lens=[33, 90, 27]),
+    # the LDS-staged shrink of whole large pieces at its edges: a last K chunk of 8 columns
+    # (K % 64 = 8, aligned), pieces of 17..64 rows (2, 3 and 4 row tiles), ranks that end
+    # inside a 16-rank tile
+    "xch_prefill_kedge": dict(M=400, K=2120, N=384, L=6, R=64, ranks=[17, 33, 47, 64],
+                              seq_lens=[113, 17, 48, 97, 125]),
     # past the part-split batch size: large pieces run whole
     "xch_prefill_whole": dict(M=1100, K=1024, N=384, L=5, R=32, ranks=[8, 32],
                               seq_lens=[500, 17, 300, 83, 200]),
