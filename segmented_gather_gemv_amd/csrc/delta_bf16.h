@@ -149,8 +149,9 @@ __device__ __forceinline__ void expand_mfma(const bf16x8_t (&P)[NE][2],
     }
 }
 
-// Old y of rows 4g..4g+3 of row tile rt at this lane's four columns (aligned path).
-template <bool ALIGNED>
+// Old y of rows 4g..4g+3 of row tile rt at this lane's four columns (aligned path). NT: the
+// loads are marked non-temporal (y is read once and rewritten; the caches keep A and B).
+template <bool ALIGNED, bool NT = false>
 __device__ __forceinline__ void load_y(const int* s_tok, int rows, int rt, int g, int vl, int v1,
                                        const ColMap (&cm)[4], uint2 (&yv)[4]) {
   // the four rows' tokens in one 16-byte LDS read (s_tok is 16-byte aligned)
@@ -160,14 +161,22 @@ __device__ __forceinline__ void load_y(const int* s_tok, int rows, int rt, int g
   for (int e = 0; e < 4; ++e) {
     const int row = rt * 16 + 4 * g + e;
     yv[e] = make_uint2(0u, 0u);
-    if (ALIGNED && row < rows && vl < v1)
-      yv[e] = *reinterpret_cast<const uint2*>(cm[0].y + (size_t)toks[e] * (size_t)cm[0].ldy +
-                                              cm[0].col);
+    if (ALIGNED && row < rows && vl < v1) {
+      const uint2* p =
+          reinterpret_cast<const uint2*>(cm[0].y + (size_t)toks[e] * (size_t)cm[0].ldy + cm[0].col);
+      if constexpr (NT) {
+        const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+        yv[e] = make_uint2(t.x, t.y);
+      } else {
+        yv[e] = *p;
+      }
+    }
   }
 }
 
-// y update of one row tile: yv holds the old values (aligned path), yacc the delta.
-template <bool ALIGNED>
+// y update of one row tile: yv holds the old values (aligned path), yacc the delta. NT: the
+// aligned path's stores are marked non-temporal.
+template <bool ALIGNED, bool NT = false>
 __device__ __forceinline__ void store_y(const int* s_tok, int rows, int rt, int g, int vl, int v1,
                                         const ColMap (&cm)[4], const uint2 (&yv)[4],
                                         const f32x4_t (&yacc)[4]) {
@@ -188,7 +197,14 @@ __device__ __forceinline__ void store_y(const int* s_tok, int rows, int rt, int 
       const float d3 = bf16_bits_to_f32(v.y >> 16) + yacc[3][e];
       v.x = pack_bf16x2(d0, d1);
       v.y = pack_bf16x2(d2, d3);
-      *reinterpret_cast<uint2*>(yp) = v;
+      if constexpr (NT) {
+        u32x2_t t;
+        t.x = v.x;
+        t.y = v.y;
+        __builtin_nontemporal_store(t, reinterpret_cast<u32x2_t*>(yp));
+      } else {
+        *reinterpret_cast<uint2*>(yp) = v;
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -378,8 +394,8 @@ __device__ __forceinline__ void shrink_step_halves(const uint16_t* xr, bool vx,
 }
 
 // B fragments and old y of the first PF column groups of a wave (small pieces), loaded
-// before the shrink's MFMAs so their latency overlaps the shrink.
-template <int NE, int PF, bool ALIGNED>
+// before the shrink's MFMAs so their latency overlaps the shrink; NT: y loads non-temporal.
+template <int NE, int PF, bool ALIGNED, bool NT = false>
 struct ExpandPrefetch {
   static constexpr int N = PF > 0 ? PF : 1;  // PF = 0: no prefetch (never loaded)
   ColMap cm[N][4];
@@ -392,7 +408,7 @@ struct ExpandPrefetch {
       const int vl = pc.v0 + 64 * (w + DT_WAVES * f) + 4 * c;
       map_group<ALIGNED>(A, vl, cm[f]);
       load_b_group<NE>(bb, A.N_pad, pc.r, vl, pc.v1, g, cm[f], bq[f]);
-      sgmv::load_y<ALIGNED>(s_tok, pc.rows, 0, g, vl, pc.v1, cm[f], yv[f]);
+      sgmv::load_y<ALIGNED, NT>(s_tok, pc.rows, 0, g, vl, pc.v1, cm[f], yv[f]);
     }
   }
   // The same loads in two parts: B of the adapter at rank r (the pool's full rank, before
@@ -423,7 +439,7 @@ struct ExpandPrefetch {
 #pragma unroll
     for (int f = 0; f < PF; ++f) {
       const int vl = pc.v0 + 64 * (w + DT_WAVES * f) + 4 * c;
-      sgmv::load_y<ALIGNED>(s_tok, pc.rows, 0, g, vl, pc.v1, cm[f], yv[f]);
+      sgmv::load_y<ALIGNED, NT>(s_tok, pc.rows, 0, g, vl, pc.v1, cm[f], yv[f]);
     }
   }
 };
@@ -560,15 +576,21 @@ __device__ void shrink_range(const DeltaArgs& A, const Piece& pc, const ShrinkGe
 // read its first token's row, ranks past the adapter's rank its first rank row, k past K the
 // row's first bytes; all of these are zeroed when read. The same steps in the same order serve a piece's own partial and the
 // local recomputation of a partner's. Needs STAGES * STAGE_BYTES of s_part.
-// This wave's two 1 KB loads of one chunk (k0: the chunk's first K index) into buf.
+// This wave's two 1 KB loads of one chunk (k0: the chunk's first K index) into buf. NT: waves
+// 0-3's x loads are marked non-temporal (x is read once; A stays cached).
+template <bool NT = false>
 __device__ __forceinline__ void stage_chunk(const uint16_t* const (&src)[2], const int (&kq)[2],
                                             int k0, int K, unsigned char* buf, int w) {
   typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int k = k0 + kq[i];
-    __builtin_amdgcn_global_load_lds(src[i] + (k < K ? k : 0),
-                                     (lds_void*)(buf + (2 * w + i) * 1024), 16, 0, 0);
+    if (NT && w < 4)
+      __builtin_amdgcn_global_load_lds(src[i] + (k < K ? k : 0),
+                                       (lds_void*)(buf + (2 * w + i) * 1024), 16, 0, 2 /* nt */);
+    else
+      __builtin_amdgcn_global_load_lds(src[i] + (k < K ? k : 0),
+                                       (lds_void*)(buf + (2 * w + i) * 1024), 16, 0, 0);
   }
 }
 
@@ -617,7 +639,8 @@ __device__ __forceinline__ void large_shrink_staged(const DeltaArgs& A, const Pi
   }
 #pragma unroll
   for (int ck = 0; ck < STAGES - 1; ++ck)
-    if (ck < nck) stage_chunk(src, kq, kbase + 64 * ck, K, stage0 + (ck % STAGES) * STAGE_BYTES, w);
+    if (ck < nck)
+      stage_chunk<(NRK >= 2)>(src, kq, kbase + 64 * ck, K, stage0 + (ck % STAGES) * STAGE_BYTES, w);
   for (int ck = 0; ck < nck; ++ck) {
     // this wave's loads of chunk ck are in once at most the later chunk's two are outstanding
     static_assert(STAGES == 3, "the wait counts below assume one chunk in flight behind");
@@ -626,7 +649,8 @@ __device__ __forceinline__ void large_shrink_staged(const DeltaArgs& A, const Pi
     lds_barrier();  // every wave's loads of chunk ck are in; chunk ck - 1 is consumed
     if (ck + STAGES - 1 < nck) {
       const int cn = ck + STAGES - 1;
-      stage_chunk(src, kq, kbase + 64 * cn, K, stage0 + (cn % STAGES) * STAGE_BYTES, w);
+      stage_chunk<(NRK >= 2)>(src, kq, kbase + 64 * cn, K, stage0 + (cn % STAGES) * STAGE_BYTES,
+                              w);
     }
     // every operand read first, masked by AND (no branches between the reads and the MFMAs)
     const unsigned char* buf = stage0 + (ck % STAGES) * STAGE_BYTES;
@@ -882,7 +906,7 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
 // adapter and the columns only; the first K step's A tile is loaded before the adapter's
 // tokens are looked up in the batch's ids, the tokens' x after, B and y once x is in; the
 // adapter's rank and scale (rank_l, scale_l) mask A and B where they are first used.
-template <int MODE, int NRK, bool ALIGNED, bool XCH, bool SPEC = false>
+template <int MODE, int NRK, bool ALIGNED, bool XCH, bool SPEC = false, bool YNT = false>
 __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* s_tok,
                                             float* s_part, float* s_h, int* s_mask,
                                             int rank_l = 0, float scale_l = 0.f) {
@@ -900,7 +924,7 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
   const uint16_t* bb =
       static_cast<const uint16_t*>(A.b) + (size_t)pc.lora * (A.R_pad / 8) * A.N_pad * 8;
 
-  ExpandPrefetch<NE, PF, ALIGNED> pf;
+  ExpandPrefetch<NE, PF, ALIGNED, YNT> pf;
   bool fetched = false;
   const int nch = (A.K + KSTEP - 1) / KSTEP;
 
@@ -979,7 +1003,7 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
 #pragma unroll
     for (int q = 0; q < 4; ++q) yacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     expand_mfma<NE>(P, pf.bq[f], yacc);
-    store_y<ALIGNED>(s_tok, pc.rows, 0, g, vg + 4 * c, pc.v1, pf.cm[f], pf.yv[f], yacc);
+    store_y<ALIGNED, YNT>(s_tok, pc.rows, 0, g, vg + 4 * c, pc.v1, pf.cm[f], pf.yv[f], yacc);
   }
   // remaining groups
   for (int vg = pc.v0 + 64 * (w + DT_WAVES * PF); vg < pc.v1; vg += 64 * DT_WAVES) {
@@ -989,19 +1013,19 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
     u32x4_t b2[NE][4];
     uint2 y2[4];
     load_b_group<NE>(bb, A.N_pad, pc.r, vl, pc.v1, g, cg, b2);
-    load_y<ALIGNED>(s_tok, pc.rows, 0, g, vl, pc.v1, cg, y2);
+    load_y<ALIGNED, YNT>(s_tok, pc.rows, 0, g, vl, pc.v1, cg, y2);
     f32x4_t yacc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) yacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     expand_mfma<NE>(P, b2, yacc);
-    store_y<ALIGNED>(s_tok, pc.rows, 0, g, vl, pc.v1, cg, y2, yacc);
+    store_y<ALIGNED, YNT>(s_tok, pc.rows, 0, g, vl, pc.v1, cg, y2, yacc);
   }
 }
 
 // ---------------------------------------------------------------------------------------
 // large pieces (17..64 rows): waves cover (row tile, K slice) pairs and stream K
 // ---------------------------------------------------------------------------------------
-template <int MODE, int NRK, bool ALIGNED, bool XCH>
+template <int MODE, int NRK, bool ALIGNED, bool XCH, bool YNT = false>
 __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc, const int* s_tok,
                                             float* s_part, float* s_h, int* s_mask) {
   const int tid = threadIdx.x, w = tid / WAVE, lane = tid & (WAVE - 1);
@@ -1038,7 +1062,7 @@ __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc,
     uint2 yv[4][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      if (rt < nrt) load_y<ALIGNED>(s_tok, pc.rows, rt, g, vl, pc.v1, cm, yv[rt]);
+      if (rt < nrt) load_y<ALIGNED, YNT>(s_tok, pc.rows, rt, g, vl, pc.v1, cm, yv[rt]);
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -1049,38 +1073,43 @@ __device__ __forceinline__ void large_piece(const DeltaArgs& A, const Piece& pc,
 #pragma unroll
       for (int q = 0; q < 4; ++q) yacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       expand_mfma<NE>(P, bq, yacc);
-      store_y<ALIGNED>(s_tok, pc.rows, rt, g, vl, pc.v1, cm, yv[rt], yacc);
+      store_y<ALIGNED, YNT>(s_tok, pc.rows, rt, g, vl, pc.v1, cm, yv[rt], yacc);
     }
   }
 }
 
 // Dispatch on the piece's rank tiles (1..NRKM) and class.
-template <int MODE, bool ALIGNED, int NRK, bool XCH>
+// YNT: y is read and written non-temporally (it streams through once; A and B stay cached).
+// The kernels for ranks above 16 take it (prefill-like batches: 10% faster at rank 64); the
+// rank-16 kernel, which decode batches run, keeps plain accesses.
+template <int MODE, bool ALIGNED, int NRK, bool XCH, bool YNT>
 __device__ __forceinline__ void piece_of(const DeltaArgs& A, const Piece& pc, bool small,
                                          const int* s_tok, float* s_part, float* s_h,
                                          int* s_mask) {
   if (small) {
     Piece q = pc;
-    small_piece<MODE, NRK, ALIGNED, XCH>(A, q, const_cast<int*>(s_tok), s_part, s_h, s_mask);
+    small_piece<MODE, NRK, ALIGNED, XCH, false, YNT>(A, q, const_cast<int*>(s_tok), s_part, s_h,
+                                                     s_mask);
   } else
-    large_piece<MODE, NRK, ALIGNED, XCH>(A, pc, s_tok, s_part, s_h, s_mask);
+    large_piece<MODE, NRK, ALIGNED, XCH, YNT>(A, pc, s_tok, s_part, s_h, s_mask);
 }
 
 template <int MODE, bool ALIGNED, int NRKM, bool XCH>
 __device__ __forceinline__ void run_piece(const DeltaArgs& A, const Piece& pc, bool small,
                                           int nrk, const int* s_tok, float* s_part, float* s_h,
                                           int* s_mask) {
+  constexpr bool YNT = NRKM >= 2;
   if constexpr (NRKM == 1) {
-    piece_of<MODE, ALIGNED, 1, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask);
+    piece_of<MODE, ALIGNED, 1, XCH, YNT>(A, pc, small, s_tok, s_part, s_h, s_mask);
   } else if constexpr (NRKM == 2) {
-    if (nrk <= 1) piece_of<MODE, ALIGNED, 1, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask);
-    else piece_of<MODE, ALIGNED, 2, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask);
+    if (nrk <= 1) piece_of<MODE, ALIGNED, 1, XCH, YNT>(A, pc, small, s_tok, s_part, s_h, s_mask);
+    else piece_of<MODE, ALIGNED, 2, XCH, YNT>(A, pc, small, s_tok, s_part, s_h, s_mask);
   } else {
     switch (nrk) {
-      case 1: piece_of<MODE, ALIGNED, 1, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
-      case 2: piece_of<MODE, ALIGNED, 2, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
-      case 3: piece_of<MODE, ALIGNED, 3, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
-      default: piece_of<MODE, ALIGNED, 4, XCH>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
+      case 1: piece_of<MODE, ALIGNED, 1, XCH, YNT>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
+      case 2: piece_of<MODE, ALIGNED, 2, XCH, YNT>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
+      case 3: piece_of<MODE, ALIGNED, 3, XCH, YNT>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
+      default: piece_of<MODE, ALIGNED, 4, XCH, YNT>(A, pc, small, s_tok, s_part, s_h, s_mask); break;
     }
   }
 }
