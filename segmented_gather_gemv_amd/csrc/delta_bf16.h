@@ -46,9 +46,16 @@ constexpr int KSTEP = 128;
 constexpr int HS = 68;                // LDS row stride of the h tile (64 ranks + 4 pad floats)
 constexpr int RANK_TABLE_MAX = 1024;  // pools up to this size get rank/scale staged in LDS
 // LDS-staged large shrink: K chunks of 64, each a 64-row x tile and a 64-rank A tile (8 KB
-// each) brought in by direct global-to-LDS loads, STAGES of them in flight
+// each) brought in by direct global-to-LDS loads into a ring of STAGES buffers at the start
+// of the dynamic LDS, STAGES - 1 chunks in flight
 constexpr int STAGE_BYTES = 16384;
-constexpr int STAGES = 3;
+constexpr int STAGES = 4;
+// The h tile (64 rows of HS floats) lives in the dynamic LDS too, over the ring's last buffer
+// (a staged shrink writes it only once its last chunk is consumed): the dynamic part holds
+// the ring and the tile in 65 KB, and with the static part two workgroups still fit a CU.
+constexpr int SH_OFFSET = (STAGES - 1) * STAGE_BYTES;
+constexpr int SH_BYTES = SGMV_TILE_ROWS * HS * 4;
+static_assert(SH_BYTES >= STAGE_BYTES, "the h tile covers the ring's last buffer");
 
 struct Piece {
   int lora, start, rows, r;
@@ -643,9 +650,12 @@ __device__ __forceinline__ void large_shrink_staged(const DeltaArgs& A, const Pi
       stage_chunk<(NRK >= 2)>(src, kq, kbase + 64 * ck, K, stage0 + (ck % STAGES) * STAGE_BYTES, w);
   for (int ck = 0; ck < nck; ++ck) {
     // this wave's loads of chunk ck are in once at most the later chunk's two are outstanding
-    static_assert(STAGES == 3, "the wait counts below assume one chunk in flight behind");
-    if (ck + 1 < nck) __builtin_amdgcn_s_waitcnt(0x0f70 | 2);  // vmcnt(2)
-    else __builtin_amdgcn_s_waitcnt(0x0f70);                  // vmcnt(0)
+    // (only the two loads of each later chunk already issued, up to STAGES - 2 of them, may
+    // still be outstanding)
+    static_assert(STAGES == 4, "the wait counts below assume two chunks in flight behind");
+    if (ck + 2 < nck) __builtin_amdgcn_s_waitcnt(0x0f70 | 4);       // vmcnt(4)
+    else if (ck + 1 < nck) __builtin_amdgcn_s_waitcnt(0x0f70 | 2);  // vmcnt(2)
+    else __builtin_amdgcn_s_waitcnt(0x0f70);                        // vmcnt(0)
     lds_barrier();  // every wave's loads of chunk ck are in; chunk ck - 1 is consumed
     if (ck + STAGES - 1 < nck) {
       const int cn = ck + STAGES - 1;
@@ -720,8 +730,7 @@ __device__ __forceinline__ void large_shrink_staged(const DeltaArgs& A, const Pi
 template <int NRK, bool ALIGNED, bool STAGED = false>
 __device__ __forceinline__ void large_shrink(const DeltaArgs& A, const Piece& pc, int nrt, const int* s_tok,
                              int k0, int k1, float mult, float* s_part, float* s_h) {
-  if constexpr (ALIGNED && STAGED) {  // fused launches give s_part STAGES * STAGE_BYTES when
-                                      // whole large pieces can occur
+  if constexpr (ALIGNED && STAGED) {  // every launch gives s_part STAGES * STAGE_BYTES
     large_shrink_staged<NRK>(A, pc, nrt, s_tok, k0, k1, mult, s_part, s_h);
     return;
   }
@@ -1123,13 +1132,13 @@ template <int MODE, bool ALIGNED, int NRKM, bool XCH, bool BUILD>
 __global__ __launch_bounds__(DT_THREADS)
 __attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_kernel(DeltaArgs A) {
   __shared__ __align__(16) int s_tok[SGMV_TILE_ROWS];
-  __shared__ __align__(16) float s_h[SGMV_TILE_ROWS * HS];
   __shared__ int s_rank[RANK_TABLE_MAX];
   __shared__ float s_scale[RANK_TABLE_MAX];
   __shared__ int s_mask;  // K-split exchange: 1 when every partner's partial is in
   // partial shrink tiles, [wave][rank tile][16][16] fp32 (R_pad/16 rank tiles); reused for
-  // the expand's h fragments afterwards
+  // the expand's h fragments afterwards; the staged shrink's ring; the h tile at SH_OFFSET
   extern __shared__ __align__(16) float s_part[];
+  float* const s_h = s_part + SH_OFFSET / sizeof(float);
 
   // ---- which piece and column split (from the workgroup index alone) ----
   const bool split = MODE != MODE_SHRINK;
@@ -1308,11 +1317,8 @@ inline void delta_geometry(int mode, DeltaArgs& A, int& grid, size_t& lds, bool 
   // them for their h fragments, which fit for every rank
   lds = (size_t)DT_WAVES * (A.R_pad / 16) * 256 * sizeof(float);
   if (build && wg_build_lds_bytes(A.L) > lds) lds = wg_build_lds_bytes(A.L);  // aliases s_part
-  // whole large pieces (no parts) of fused calls stage their shrink through s_part in the
-  // aligned kernels
-  if (mode == MODE_FUSED && A.rsplit == 1 && A.large_cap > 0 &&
-      lds < (size_t)STAGES * STAGE_BYTES)
-    lds = (size_t)STAGES * STAGE_BYTES;
+  // the h tile at SH_OFFSET, which also covers the staged shrink's ring
+  if (lds < (size_t)(SH_OFFSET + SH_BYTES)) lds = (size_t)(SH_OFFSET + SH_BYTES);
   if (build && A.amajor) {
     // small slots per adapter first, then the large class, then the writer: large work is
     // rare in adapter-indexed batches, and its workgroups (which first check for it) then do
