@@ -418,15 +418,20 @@ struct ExpandPrefetch {
       sgmv::load_y<ALIGNED, NT>(s_tok, pc.rows, 0, g, vl, pc.v1, cm[f], yv[f]);
     }
   }
-  // The same loads in two parts: B of the adapter at rank r (the pool's full rank, before
-  // the adapter's own is known; mask_rank trims it), then the tokens' y rows.
-  __device__ __forceinline__ void load_b(const DeltaArgs& A, const uint16_t* bb, const Piece& pc,
-                                         int r, int w, int c, int g) {
+  // The same loads in three steps: the column groups' maps, the tokens' y rows (load_y,
+  // which needs the maps), then B of the adapter at rank r (the pool's full rank, before the
+  // adapter's own is known; mask_rank trims it).
+  __device__ __forceinline__ void map(const DeltaArgs& A, const Piece& pc, int w, int c) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f)
+      map_group<ALIGNED>(A, pc.v0 + 64 * (w + DT_WAVES * f) + 4 * c, cm[f]);
+  }
+  __device__ __forceinline__ void load_b(const uint16_t* bb, int N_pad, const Piece& pc, int r,
+                                         int w, int c, int g) {
 #pragma unroll
     for (int f = 0; f < PF; ++f) {
       const int vl = pc.v0 + 64 * (w + DT_WAVES * f) + 4 * c;
-      map_group<ALIGNED>(A, vl, cm[f]);
-      load_b_group<NE>(bb, A.N_pad, r, vl, pc.v1, g, cm[f], bq[f]);
+      load_b_group<NE>(bb, N_pad, r, vl, pc.v1, g, cm[f], bq[f]);
     }
   }
   __device__ __forceinline__ void mask_rank(int r, int g) {
@@ -913,7 +918,7 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
 // ---------------------------------------------------------------------------------------
 // SPEC (fused build + delta, adapter-major, every adapter at full rank 16): pc holds the
 // adapter and the columns only; the first K step's A tile is loaded before the adapter's
-// tokens are looked up in the batch's ids, the tokens' x after, B and y once x is in; the
+// tokens are looked up in the batch's ids, the tokens' x and y after, B once x is in; the
 // adapter's rank and scale (rank_l, scale_l) mask A and B where they are first used.
 template <int MODE, int NRK, bool ALIGNED, bool XCH, bool SPEC = false, bool YNT = false>
 __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* s_tok,
@@ -963,11 +968,13 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
       const bool vx = c < pc.rows;
       S.load_x(static_cast<const uint16_t*>(A.x) + (size_t)(vx ? s_tok[c] : 0) * (size_t)A.ldx,
                vx, A.K, ch, c1, g);
+      // y right behind x (loads complete in order, so the MFMAs wait for x alone), B once x is
+      // in: y's round trip overlaps the shrink, and x does not queue behind B
+      pf.map(A, pc, w, c);
+      pf.load_y(pc, s_tok, w, c, g);
       S.mask_rank(pc.r, c);
       S.mfma(acc);
-      // B and y once x is in: they have the exchange to arrive, and x does not queue behind
-      pf.load_b(A, bb, pc, A.R_pad, w, c, g);
-      pf.load_y(pc, s_tok, w, c, g);
+      pf.load_b(bb, A.N_pad, pc, A.R_pad, w, c, g);
       fetched = true;
       ch += NSTEP;
     }
@@ -980,11 +987,18 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
       } else {
         ShrinkSteps<NRK, NSTEP, ALIGNED> S;
         S.load(xr, vx, ab, A.K_pad, A.K, pc.r, ch, c1, c, g);
-        if (MODE == MODE_FUSED && PF > 0 && !fetched) {  // rides along the first loads
-          pf.load(A, bb, pc, s_tok, w, c, g);
-          fetched = true;
+        // y rides along the first loads (the MFMAs wait for x and A alone: loads complete in
+        // order), B follows once they are in, so x and A do not queue behind it
+        const bool first = MODE == MODE_FUSED && PF > 0 && !fetched;
+        if (first) {
+          pf.map(A, pc, w, c);
+          pf.load_y(pc, s_tok, w, c, g);
         }
         S.mfma(acc);
+        if (first) {
+          pf.load_b(bb, A.N_pad, pc, pc.r, w, c, g);
+          fetched = true;
+        }
       }
     }
     store_wave_partial<NRK>(s_part, w, c, g, acc);
