@@ -495,6 +495,92 @@ def chunk_sweep(args):
                       "best": [best[k] for k in sorted(best)]}), flush=True)
 
 
+def phase_stamps(args):
+    """Per-phase times of the decode single launch from libsgmv_stamps.so, the profiling copy
+    of the library whose single-launch kernel records the 100 MHz real-time counter at its
+    phase points (thread 0 of every workgroup; the last point waits for the workgroup's stores).
+    The stamp stores and that wait make the copy slightly slower than the library; the phases
+    are what it is for. Prints one JSON line: p10/p50/p90 of every phase in ns over the
+    workgroups that carry a piece, over `reps` rounds of rotating-buffer launches."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    import segmented_gather_gemv_amd as sg
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    path = os.path.join(ROOT, "segmented_gather_gemv_amd", "libsgmv_stamps.so")
+    if not os.path.exists(path):
+        print("libsgmv_stamps.so is not built (segmented_gather_gemv_amd/build.py builds it)",
+              file=sys.stderr)
+        sys.exit(1)
+    lib = ctypes.CDLL(path)
+    base = sg.library()
+    f = lib.sgmv_lora_delta_ids_ex
+    f.argtypes, f.restype = base.sgmv_lora_delta_ids_ex.argtypes, ctypes.c_int
+    lib.sgmv_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.sgmv_phase_stamps.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)  # default priority
+    w = workloads.get("decode")
+    n_sets = 24
+    sets = []
+    with torch.cuda.stream(stream):
+        a_dev, b_dev = w.a.to(dev), w.b.to(dev)
+        for _ in range(n_sets):
+            pool = sg.sgmv_pool_pack(a_dev, b_dev, w.rank.tolist(), w.alpha.tolist())
+            x, y, ids = w.x.to(dev), w.y0.to(dev), w.ids.to(dev)
+            seg = sg.sgmv_segments_alloc(w.M, w.L, 0, dev)
+            sl, n_sl = sg._slices([(y, 0)], pool, w.M)
+            sets.append(dict(pool=pool, x=x, y=y, ids=ids, seg=seg, sl=sl, n_sl=n_sl))
+    torch.cuda.synchronize()
+    names = ["launch to ids in", "ids to tokens known", "x in, first K step multiplied",
+             "partial published (B, y in)", "counter complete", "partials summed, h in LDS",
+             "expand, y stores issued", "y stores complete"]
+    phases = {k: [] for k in names}
+    ends, spreads, n_full = [], [], []
+    reps = 8
+    rows_max, slots = 8192, 16
+    for rep in range(reps):
+        with torch.cuda.stream(stream):
+            for i in range(n_sets + 1):  # every launch overwrites the rows; the last one stays
+                st = sets[(i + rep) % n_sets]
+                rc = f(vp(st["ids"].data_ptr()), vp(st["x"].data_ptr()), st["x"].stride(0), w.M,
+                       ctypes.byref(st["pool"].desc), ctypes.byref(st["seg"].desc), st["sl"],
+                       st["n_sl"], None, vp(stream.cuda_stream))
+                if rc != 0:
+                    raise SystemExit(f"sgmv_lora_delta_ids_ex returned {rc}")
+        torch.cuda.synchronize()
+        buf = np.zeros(rows_max * slots, dtype=np.uint64)
+        if lib.sgmv_phase_stamps(buf.ctypes.data_as(vp), buf.nbytes) != 0:
+            raise SystemExit("sgmv_phase_stamps failed")
+        st_ = buf.reshape(rows_max, slots).astype(np.int64)
+        live = st_[:, 0] > 0
+        full = live & (st_[:, 8] > st_[:, 0])  # workgroups that ran a piece to its end
+        t0 = st_[live, 0].min()
+        rows = st_[full]
+        for k, nm in enumerate(names):
+            phases[nm].extend(((rows[:, k + 1] - rows[:, k]) * 10.0).tolist())
+        ends.append(float((rows[:, 8].max() - t0) * 10.0))
+        spreads.append(float((st_[live, 0].max() - t0) * 10.0))
+        n_full.append(int(full.sum()))
+    out = {"metric": "decode single-launch phase times (ns, p10/p50/p90 over workgroups)",
+           "workload": w.note, "rounds": reps, "workgroups_with_piece": int(np.median(n_full)),
+           "start_spread_ns": round(float(np.median(spreads))),
+           "first_start_to_last_end_ns": round(float(np.median(ends)))}
+    for nm in names:
+        v = np.asarray(phases[nm])
+        out[nm] = [round(float(np.percentile(v, q))) for q in (10, 50, 90)]
+    for nm in names:
+        log(f"{nm:34s} p50 {out[nm][1] / 1000:.2f} us (p10 {out[nm][0] / 1000:.2f}, "
+            f"p90 {out[nm][2] / 1000:.2f})")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -551,6 +637,8 @@ def main():
                          "mix over its launch-shape sweep")
     ap.add_argument("--no-stream-ceiling", action="store_true",
                     help="skip the streaming reference kernel in the benchmark line")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="per-phase times of the decode single launch from libsgmv_stamps.so")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
                     help="delta FETCH, delta WRITE, copy FETCH, copy WRITE counter CSVs")
     args = ap.parse_args()
@@ -578,6 +666,9 @@ def main():
         return
     if args.merge:
         merge_bench(args)
+        return
+    if args.phase_stamps:
+        phase_stamps(args)
         return
     if args.chunk_sweep:
         chunk_sweep(args)

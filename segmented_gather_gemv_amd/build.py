@@ -3,7 +3,9 @@
 HIP sources are compiled by hipcc for gfx950 (packed fp32 instructions disabled), the
 host-only segment builder by g++; the objects are linked by hipcc into
 ``segmented_gather_gemv_amd/libsgmv.so``. The benchmark's streaming reference kernel
-(``csrc/bench/``, not part of the library) goes into ``libsgmv_bench.so``. Always rebuilds. Run as
+(``csrc/bench/``, not part of the library) goes into ``libsgmv_bench.so``, and a profiling copy
+of the library whose single-launch kernel records phase stamps (``-DSGMV_PHASE_STAMPS``) into
+``libsgmv_stamps.so``. Always rebuilds. Run as
 ``python -m segmented_gather_gemv_amd.build`` or call ``build()``.
 """
 from __future__ import annotations
@@ -21,6 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsgmv.so")
 BENCH_LIB = os.path.join(PKG, "libsgmv_bench.so")
+STAMPS_LIB = os.path.join(PKG, "libsgmv_stamps.so")
+STAMPED = "delta_bf16_build.hip"  # the source compiled again with the stamps
 BENCH_SRC = os.path.join(CSRC, "bench")
 ARCH = os.environ.get("SGMV_OFFLOAD_ARCH", "gfx950")
 
@@ -67,6 +71,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         o = os.path.join(OUT_DIR, f + ".o")
         objs.append(o)
         cmds.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, f), "-o", o])
+    stamp_obj = os.path.join(OUT_DIR, "stamps_" + STAMPED + ".o")
+    cmds.append([hipcc, *HIP_FLAGS, "-DSGMV_PHASE_STAMPS", "-c", os.path.join(CSRC, STAMPED),
+                 "-o", stamp_obj])
     bench_objs = []
     for f in sorted(f for f in os.listdir(BENCH_SRC) if f.endswith(".hip")):
         o = os.path.join(OUT_DIR, "bench_" + f + ".o")
@@ -79,6 +86,10 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    tmp = STAMPS_LIB + ".tmp"
+    stamp_objs = [o for o in objs if os.path.basename(o) != STAMPED + ".o"] + [stamp_obj]
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *stamp_objs])
+    os.replace(tmp, STAMPS_LIB)
     tmp = BENCH_LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *bench_objs])
     os.replace(tmp, BENCH_LIB)

@@ -40,6 +40,43 @@
 
 namespace sgmv {
 
+// Phase stamps, for profiling builds only (libsgmv_stamps.so). With SGMV_PHASE_STAMPS defined,
+// thread 0 of each of the first STAMP_WGS workgroups records the 100 MHz real-time counter at
+// the phase points of a small piece into slot k of its row; sgmv_phase_stamps reads the array
+// back. Without it (the library itself) the macros are empty and no stamp code is compiled.
+#ifdef SGMV_PHASE_STAMPS
+constexpr int STAMP_WGS = 8192, STAMP_SLOTS = 16;
+static __device__ uint64_t g_phase_stamps[STAMP_WGS * STAMP_SLOTS];
+#define SGMV_STAMP(k)                                                                   \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && blockIdx.x < STAMP_WGS)                                     \
+      g_phase_stamps[blockIdx.x * STAMP_SLOTS + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+// stamp k once the wave-uniform value v is in its scalar registers
+#define SGMV_STAMP_AFTER(k, v)                                      \
+  do {                                                              \
+    if (threadIdx.x == 0) asm volatile("" ::"s"(v));                \
+    SGMV_STAMP(k);                                                  \
+  } while (0)
+// stamp k after every store of the workgroup has completed
+#define SGMV_STAMP_DRAINED(k)        \
+  do {                               \
+    __builtin_amdgcn_s_waitcnt(0);   \
+    __syncthreads();                 \
+    SGMV_STAMP(k);                   \
+  } while (0)
+#else
+#define SGMV_STAMP(k) \
+  do {                \
+  } while (0)
+#define SGMV_STAMP_AFTER(k, v) \
+  do {                         \
+  } while (0)
+#define SGMV_STAMP_DRAINED(k) \
+  do {                        \
+  } while (0)
+#endif
+
 constexpr int DT_THREADS = 512;
 constexpr int DT_WAVES = DT_THREADS / WAVE;
 constexpr int KSTEP = 128;
@@ -851,6 +888,7 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
   store_partial<NRK, LARGE>(pc, G, s_part, s_h, part + p * xs);
   wait_stores();
   __syncthreads();
+  if (!LARGE) SGMV_STAMP(4);  // the partial is published (and B and y are in)
   if (tid == 0) {
     const uint32_t inc = p == P - 1 ? 64u - (uint32_t)(P - 1) : 1u;
     const uint32_t old =
@@ -867,6 +905,7 @@ __device__ void exchange_h(const DeltaArgs& A, const Piece& pc, const ShrinkGeom
     *s_flag = cur - base >= 64u ? 1 : 0;
   }
   __syncthreads();
+  if (!LARGE) SGMV_STAMP(5);  // the counter is complete (or the wait is over)
 
   if (!*s_flag) {  // uniform: a partner is late. Every other partial is computed here, by the
                    // same steps as its owner's, and written to its slot (the owner, if it is
@@ -956,13 +995,15 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
       static_assert(MODE == MODE_FUSED && NRK == 1 && PF > 0, "adapter-major rank-16 pieces");
       ShrinkSteps<NRK, NSTEP, ALIGNED> S;
       S.load_a(ab, A.K_pad, A.K, ch, c1, c, g);
-      pc.rows = adapter_small_piece<DT_WAVES>(wave_adapter_mask(A.ids, A.M, pc.lora),
-                                              reinterpret_cast<int*>(s_part), s_tok);
+      const uint64_t idmask = wave_adapter_mask(A.ids, A.M, pc.lora);
+      SGMV_STAMP_AFTER(1, idmask);  // the ids are in
+      pc.rows = adapter_small_piece<DT_WAVES>(idmask, reinterpret_cast<int*>(s_part), s_tok);
       if (pc.rows == 0) {  // uniform: no small piece; let the loads land before leaving
         __builtin_amdgcn_s_waitcnt(0);
         return;
       }
       __syncthreads();  // s_tok; s_part is free again
+      SGMV_STAMP(2);  // the piece's tokens are known
       pc.r = rank_l;
       pc.scale = scale_l;
       const bool vx = c < pc.rows;
@@ -974,6 +1015,7 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
       pf.load_y(pc, s_tok, w, c, g);
       S.mask_rank(pc.r, c);
       S.mfma(acc);
+      SGMV_STAMP(3);  // x is in, the first K step multiplied
       pf.load_b(bb, A.N_pad, pc, A.R_pad, w, c, g);
       fetched = true;
       ch += NSTEP;
@@ -1016,6 +1058,7 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
   bf16x8_t P[NE][2];
   h_fragments<NE>(s_h, 0, lane, P);
   if constexpr (SPEC) pf.mask_rank(pc.r, g);
+  if constexpr (SPEC) SGMV_STAMP(6);  // h is in LDS
 
   // prefetched groups
 #pragma unroll
@@ -1042,6 +1085,10 @@ __device__ __forceinline__ void small_piece(const DeltaArgs& A, Piece& pc, int* 
     for (int q = 0; q < 4; ++q) yacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     expand_mfma<NE>(P, b2, yacc);
     store_y<ALIGNED, YNT>(s_tok, pc.rows, 0, g, vl, pc.v1, cg, y2, yacc);
+  }
+  if constexpr (SPEC) {
+    SGMV_STAMP(7);          // the y stores are issued
+    SGMV_STAMP_DRAINED(8);  // and complete
   }
 }
 
@@ -1152,6 +1199,7 @@ __attribute__((amdgpu_waves_per_eu(XCH && ALIGNED ? 4 : 1))) void delta_bf16_ker
   // partial shrink tiles, [wave][rank tile][16][16] fp32 (R_pad/16 rank tiles); reused for
   // the expand's h fragments afterwards; the staged shrink's ring; the h tile at SH_OFFSET
   extern __shared__ __align__(16) float s_part[];
+  SGMV_STAMP(0);
   float* const s_h = s_part + SH_OFFSET / sizeof(float);
 
   // ---- which piece and column split (from the workgroup index alone) ----

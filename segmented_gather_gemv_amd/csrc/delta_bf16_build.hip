@@ -28,3 +28,12 @@ hipError_t launch_delta_bf16_build(bool aligned, DeltaArgs A, LaunchEvents ev,
 }
 
 }  // namespace sgmv
+
+#ifdef SGMV_PHASE_STAMPS
+// Profiling builds only: copies the phase stamps of the last single launches (STAMP_WGS rows
+// of STAMP_SLOTS uint64 counter values, row = workgroup) to host memory. Returns 0 on success.
+extern "C" int sgmv_phase_stamps(void* host, size_t bytes) {
+  if (!host || bytes > sizeof(sgmv::g_phase_stamps)) return 1;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(sgmv::g_phase_stamps), bytes) == hipSuccess ? 0 : 1;
+}
+#endif

@@ -43,6 +43,19 @@ def test_library_exports_every_declared_symbol():
     exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
     assert set(names) <= exported
     assert set(sg.EXPORTED) <= exported
+    assert "sgmv_phase_stamps" not in exported  # profiling builds only
+
+
+def test_stamps_library_exports_the_same_calls_and_the_stamp_reader():
+    """libsgmv_stamps.so (the profiling copy behind bench.py --phase-stamps) is the library
+    with phase stamps compiled into the single-launch kernel: the same C-ABI plus the reader."""
+    path = os.path.join(os.path.dirname(sg.LIB_PATH), "libsgmv_stamps.so")
+    assert os.path.exists(path), "build.py builds libsgmv_stamps.so beside libsgmv.so"
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    assert set(declared_functions()) <= exported
+    assert "sgmv_phase_stamps" in exported
 
 
 def test_binding_constants_match_the_header():
