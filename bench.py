@@ -42,6 +42,9 @@ unchanged and with changed ids.
 The CPU baseline is the fp64 oracle (plain per-token NumPy loop) on the same batch, repeated
 for about 10 s on this host.
 
+--phase-stamps instead prints the per-phase times of the decode single launch, read from
+libsgmv_stamps.so (the library built with phase stamps in that kernel).
+
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
