@@ -545,7 +545,7 @@ def phase_stamps(args):
              "partial published (B, y in)", "counter complete", "partials summed, h in LDS",
              "expand, y stores issued", "y stores complete"]
     phases = {k: [] for k in names}
-    ends, spreads, n_full = [], [], []
+    ends, spreads, n_full, starts = [], [], [], []
     reps = 8
     rows_max, slots = 8192, 16
     for rep in range(reps):
@@ -570,11 +570,14 @@ def phase_stamps(args):
             phases[nm].extend(((rows[:, k + 1] - rows[:, k]) * 10.0).tolist())
         ends.append(float((rows[:, 8].max() - t0) * 10.0))
         spreads.append(float((st_[live, 0].max() - t0) * 10.0))
+        starts.extend(((rows[:, 0] - t0) * 10.0).tolist())
         n_full.append(int(full.sum()))
     out = {"metric": "decode single-launch phase times (ns, p10/p50/p90 over workgroups)",
            "workload": w.note, "rounds": reps, "workgroups_with_piece": int(np.median(n_full)),
            "start_spread_ns": round(float(np.median(spreads))),
-           "first_start_to_last_end_ns": round(float(np.median(ends)))}
+           "first_start_to_last_end_ns": round(float(np.median(ends))),
+           "piece_workgroup_start_ns_p10_p50_p90_max": [
+               round(float(np.percentile(starts, q))) for q in (10, 50, 90, 100)]}
     for nm in names:
         v = np.asarray(phases[nm])
         out[nm] = [round(float(np.percentile(v, q))) for q in (10, 50, 90)]
